@@ -1,0 +1,202 @@
+/*
+ * la.h — C ABI of the MI355X (gfx950) lookahead decoding library.
+ *
+ * One call of la_step runs one lookahead decoding step as described in
+ * "Break the Sequential Dependency of LLM Inference Using Lookahead
+ * Decoding" (Fu, Bailis, Stoica, Zhang 2024), summary page:
+ *   - Summary: decoding is a non-linear system solved by Jacobi iteration; a
+ *     lookahead branch keeps a 2D window over recent iterations and produces
+ *     many disjoint n-grams per step; the n-grams are cached in a pool; a
+ *     verification branch checks pool candidates in the same forward pass,
+ *     so the output is exactly that of ordinary (here: greedy) decoding;
+ *   - Key points, "Tuning knobs": W = lookahead window, N = n-gram size,
+ *     G = verification size; the step forwards 1 + (W + G)(N - 1) rows.
+ * The model is a LLaMA-style decoder (pre-norm RMSNorm, rotary embedding on
+ * adjacent dimension pairs, grouped KV heads, SwiGLU, untied LM head).
+ *
+ * Conventions
+ *   - Every pointer documented as "device" is HIP device memory; "host" is
+ *     ordinary host memory.  The library never allocates or frees device
+ *     memory: the caller passes one workspace of la_workspace_bytes() bytes
+ *     and owns the weights, the workspace and the stream; all must outlive
+ *     the context.  The library allocates one small pinned host buffer per
+ *     context for the step result.
+ *   - Every call returns la_status; nothing aborts and no exception crosses
+ *     the ABI.  Arguments are validated before any HIP call.  After a HIP
+ *     failure the context is poisoned: every later call except la_destroy
+ *     returns LA_ERR_STATE.  la_last_error() describes the last failure.
+ *   - A context is not thread-safe; use one context per stream.
+ */
+#ifndef LA_H
+#define LA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct la_ctx la_ctx;
+
+typedef enum {
+  LA_OK = 0,
+  LA_ERR_INVALID_ARG = -1,     /* bad argument or configuration */
+  LA_ERR_STATE = -2,           /* call out of order, or context poisoned */
+  LA_ERR_OUT_OF_CAPACITY = -3, /* KV cache (max_ctx) or workspace too small */
+  LA_ERR_HIP = -4,             /* a HIP runtime call failed */
+  LA_ERR_UNSUPPORTED = -5      /* valid but not supported by the kernels */
+} la_status;
+
+typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+
+typedef struct {
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ffn, vocab;
+  float rope_theta; /* rotary base, e.g. 10000 */
+  float rms_eps;    /* RMSNorm epsilon, e.g. 1e-5 */
+  int32_t W;        /* lookahead window (columns), >= 0 */
+  int32_t N;        /* n-gram size, 2..32 */
+  int32_t G;        /* verification size = candidates per step = pool cap per key */
+  int32_t max_ctx;  /* KV capacity in tokens (prompt + generated + one step's rows) */
+  int32_t dtype;    /* la_dtype of weights, activations and KV cache */
+} la_config;
+/* Supported shapes.  LA_BF16: head_dim 128, d_model % 32 == 0,
+ * d_ffn % 32 == 0, vocab % 32 == 0.  LA_F32 (small models): head_dim even and
+ * <= 256, d_model, d_ffn and vocab even, max_ctx <= 16384.  Both:
+ * n_heads % n_kv_heads == 0 and 1 + (W + G)(N - 1) <= 256.  W = G = 0 gives
+ * the plain one-token greedy decode step. */
+
+/* Result of one step (host struct). */
+typedef struct {
+  int32_t n_emitted;  /* tokens emitted this step, k + 1, in [1, N] */
+  int32_t tokens[32]; /* emitted tokens; tokens[n_emitted-1] is the new current token */
+  int32_t accepted;   /* k: candidate tokens accepted by verification */
+  int32_t winner;     /* g*: index of the accepted candidate, -1 if the pool had none */
+  int32_t n_candidates; /* candidates verified this step (<= G) */
+  int32_t kv_len;     /* committed KV length after the step */
+} la_step_result;
+
+/* Weights: an array of 3 + 9 * n_layers DEVICE pointers, each a row-major
+ * tensor of the config's dtype ([out_features][in_features] for matrices):
+ *   [0] tok_emb [vocab][d_model]   [1] final_norm [d_model]
+ *   [2] lm_head [vocab][d_model]
+ *   then for layer l at 3 + 9 l:  +0 attn_norm [d_model],
+ *   +1 wq [n_heads*head_dim][d_model], +2 wk [n_kv_heads*head_dim][d_model],
+ *   +3 wv [n_kv_heads*head_dim][d_model], +4 wo [d_model][n_heads*head_dim],
+ *   +5 ffn_norm [d_model], +6 w_gate [d_ffn][d_model],
+ *   +7 w_up [d_ffn][d_model], +8 w_down [d_model][d_ffn]. */
+
+/* Bytes of DEVICE workspace a context needs (0 for an invalid config).
+ * Holds the repacked weights (bf16), the KV cache, the n-gram pool, the
+ * activations and scratch. */
+size_t la_workspace_bytes(const la_config *cfg);
+
+/* Create a context.  Validates cfg, carves the workspace, repacks the
+ * weights into the workspace (bf16: MFMA operand tiles, fused QKV and
+ * interleaved gate/up; f32: fused QKV), clears the cache and captures the
+ * step as a HIP graph.  hip_stream: the hipStream_t all work is queued on
+ * (NULL = the null stream).  Blocks until set-up is done.
+ * Errors: LA_ERR_INVALID_ARG (cfg, NULL pointers), LA_ERR_UNSUPPORTED
+ * (shape), LA_ERR_OUT_OF_CAPACITY (workspace_bytes too small), LA_ERR_HIP. */
+la_status la_create(const la_config *cfg, const void *const *weights,
+                    void *workspace, size_t workspace_bytes, void *hip_stream,
+                    la_ctx **out);
+
+/* Prefill: empty the cache and the pool, run the prompt (host int32
+ * [n_prompt], ids < vocab) causally in chunks, install the initial window
+ * (host int32 [(N-1)*W], level 1 first, then level 2, ...; required when
+ * W > 0, ignored otherwise) and return the first generated token (the
+ * prompt's greedy next token) in *first_token (host).  The first token
+ * becomes the current token of the next step.
+ * Errors: LA_ERR_INVALID_ARG, LA_ERR_OUT_OF_CAPACITY (n_prompt + step rows >
+ * max_ctx), LA_ERR_STATE (poisoned), LA_ERR_HIP. */
+la_status la_prefill(la_ctx *c, const int32_t *prompt, int32_t n_prompt,
+                     const int32_t *init_window, int32_t *first_token);
+
+/* One lookahead step (blocks until the result is on the host, *out).
+ * Errors: LA_ERR_STATE (before prefill or poisoned), LA_ERR_OUT_OF_CAPACITY
+ * (kv_len + step rows > max_ctx), LA_ERR_INVALID_ARG (out NULL), LA_ERR_HIP. */
+la_status la_step(la_ctx *c, la_step_result *out);
+
+/* Destroy a context (NULL is fine).  Waits for the context's queued work. */
+la_status la_destroy(la_ctx *c);
+
+const char *la_status_string(la_status s);
+const char *la_last_error(const la_ctx *c);
+
+/* Rows forwarded per step: 1 + (W + G)(N - 1). */
+int32_t la_step_rows(const la_ctx *c);
+
+/* ---- profiling ----------------------------------------------------------
+ * Run one step like la_step (same kernels, same state change) but launched
+ * directly rather than from the captured graph, with a HIP event recorded
+ * on the context's stream before and after every kernel launch.  ms[k]
+ * (host float [LA_PROF_CLASSES]) receives the summed event time of kernel
+ * class k and launches[k] (host int32) the number of launches.  The event
+ * pairs add small gaps, so the step itself runs slower than la_step. */
+enum {
+  LA_PROF_QKV = 0,    /* fused RMSNorm'd QKV projection + RoPE + KV write */
+  LA_PROF_ATTN = 1,   /* masked attention (+ split merge) */
+  LA_PROF_O = 2,      /* output projection + residual */
+  LA_PROF_GATEUP = 3, /* fused gate/up projection + SwiGLU */
+  LA_PROF_DOWN = 4,   /* down projection + residual */
+  LA_PROF_LMHEAD = 5, /* LM head (logits) */
+  LA_PROF_NORM = 6,   /* RMSNorm kernels */
+  LA_PROF_OTHER = 7,  /* assembly, argmax, verification, KV compaction */
+  LA_PROF_CLASSES = 8
+};
+la_status la_profile_step(la_ctx *c, float *ms, int32_t *launches,
+                          la_step_result *out);
+
+/* ---- inspection (tests, debugging); each synchronizes the stream ------- */
+
+/* Logits of the last step's rows, host float [rows][vocab]; n = element
+ * count of the buffer (must be >= rows * vocab). */
+la_status la_debug_logits(la_ctx *c, float *host, size_t n);
+/* Tokens and per-row argmax of the last step, host int32 [rows] each (either
+ * may be NULL). */
+la_status la_debug_block(la_ctx *c, int32_t *tokens, int32_t *amax);
+/* Current window, host int32 [(N-1)*W] (level 1 first). */
+la_status la_debug_window(la_ctx *c, int32_t *win);
+/* Pool: host int32 len [vocab] and tails [vocab][G][N-1] (oldest first). */
+la_status la_debug_pool(la_ctx *c, int32_t *len, int32_t *tails);
+/* Insert one n-gram tail (host int32 [N-1]) under key, with the pool's
+ * policy (tests plant candidates with it). */
+la_status la_debug_pool_insert(la_ctx *c, int32_t key, const int32_t *tail);
+/* Cached K and V of positions pos0..pos0+n-1 of one layer as host float
+ * [n_kv_heads][n][head_dim] each. */
+la_status la_debug_kv(la_ctx *c, int32_t layer, int32_t pos0, int32_t n,
+                      float *k, float *v);
+/* Committed length and current token. */
+la_status la_debug_state(la_ctx *c, int32_t *kv_len, int32_t *current);
+
+/* ---- one layer's masked attention on its own ---------------------------
+ * The attention of a lookahead step ("Summary": both branches in one pass)
+ * for the bf16 kernel: query rows in the step's row order (current token,
+ * window rows level by level, candidate rows candidate by candidate); each
+ * row sees cache positions 0..prefix_len-1 and the block rows the
+ * lookahead/verification mask allows; block row r's key/value sit at cache
+ * position prefix_len + r.
+ *   q        DEVICE bf16 [rows][n_heads][128], rows = 1 + (W+G)(N-1)
+ *   k_cache  DEVICE bf16 [n_kv_heads][ctx_stride][128]
+ *   vt_cache DEVICE bf16 [n_kv_heads][128][ctx_stride] (V transposed)
+ *   out      DEVICE bf16 [rows][n_heads][128]
+ *   ctx_stride % 64 == 0 and prefix_len + rows <= ctx_stride.
+ *   workspace: DEVICE, la_attention_workspace_bytes() bytes (split-KV
+ *   partial results); stream: hipStream_t or NULL.  Asynchronous.
+ * Errors: LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED (head_dim != 128),
+ * LA_ERR_OUT_OF_CAPACITY (workspace too small), LA_ERR_HIP. */
+size_t la_attention_workspace_bytes(int32_t n_heads, int32_t head_dim,
+                                    int32_t ctx_stride, int32_t W, int32_t N,
+                                    int32_t G);
+la_status la_attention(const void *q, const void *k_cache,
+                       const void *vt_cache, void *out, int32_t n_heads,
+                       int32_t n_kv_heads, int32_t head_dim,
+                       int32_t prefix_len, int32_t ctx_stride, int32_t W,
+                       int32_t N, int32_t G, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LA_H */

@@ -1,0 +1,743 @@
+// Host side of the lookahead library: configuration checks, workspace
+// carve-up, weight repacking, prefill, the captured step graph and the
+// inspection calls.  See include/la.h for the contract of every entry point.
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "la.h"
+#include "la_internal.h"
+
+using namespace la;
+
+namespace {
+
+constexpr int MAX_ROWS = 256;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Bump allocator over the caller's workspace; with base == nullptr it only
+// measures.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  template <typename T>
+  T* take(size_t count) {
+    off = align_up(off, 256);
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+struct Layer {
+  const void *anorm, *fnorm;
+  const void* wqkv;  // bf16: packed tiles; f32: fused row-major copy
+  const void* wo;
+  const void* wgu;   // bf16: packed, gate/up tiles interleaved
+  const void *wg, *wu;  // f32 originals
+  const void* wd;
+};
+
+// Optional per-launch timing: HIP events recorded around each launch on the
+// launch stream, summed per kernel class.
+struct Prof {
+  std::vector<hipEvent_t>* pool;
+  std::vector<int> cat;
+  size_t used = 0;
+  hipStream_t s;
+  void begin(int c) {
+    ensure();
+    cat.push_back(c);
+    (void)hipEventRecord((*pool)[used++], s);
+  }
+  void end() {
+    ensure();
+    (void)hipEventRecord((*pool)[used++], s);
+  }
+  void ensure() {
+    if (used == pool->size()) {
+      hipEvent_t e;
+      (void)hipEventCreate(&e);
+      pool->push_back(e);
+    }
+  }
+};
+
+}  // namespace
+
+struct la_ctx {
+  la_config cfg;
+  int T = 0, MR = 0, bf16 = 0, elem = 4, ctx_stride = 0;
+  int qdim = 0, kvdim = 0, qkv_rows = 0;
+  hipStream_t stream = nullptr;
+  bool poisoned = false, prefilled = false, use_graph = true;
+  std::string err;
+  int kv_len_host = 0;
+  // device carve-up
+  DevState* st = nullptr;
+  DevResult* res_dev = nullptr;
+  float *x = nullptr, *logits = nullptr, *rope_cos = nullptr, *rope_sin = nullptr;
+  float *gpart = nullptr, *attn_po = nullptr, *attn_pml = nullptr;
+  void *xn = nullptr, *ffa = nullptr, *qb = nullptr;
+  int32_t *tokens = nullptr, *relpos = nullptr, *amax = nullptr, *prompt_buf = nullptr;
+  int32_t *win = nullptr, *pool_len = nullptr, *pool = nullptr, *counters = nullptr;
+  int32_t* tail_buf = nullptr;
+  void *kcache = nullptr, *vtcache = nullptr;
+  size_t kv_layer_elems = 0;  // elements of one layer's K (or V^T) cache
+  // weights
+  const void *emb = nullptr, *final_norm = nullptr, *lm = nullptr;
+  std::vector<Layer> layers;
+  int ks_qkv = 1, ks_o = 1, ks_gu = 1, ks_d = 1, ks_lm = 1, attn_splits = 1;
+  // host
+  DevResult* res_host = nullptr;  // pinned
+  int32_t* pin = nullptr;         // pinned staging
+  size_t pin_count = 0;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t gexec = nullptr;
+  std::vector<hipEvent_t> events;  // profiling only
+};
+
+namespace {
+
+la_status fail(la_ctx* c, la_status s, const std::string& msg) {
+  if (c) {
+    c->err = msg;
+    if (s == LA_ERR_HIP) c->poisoned = true;
+  }
+  return s;
+}
+
+#define LA_HIP(c, call)                                                          \
+  do {                                                                           \
+    hipError_t e_ = (call);                                                      \
+    if (e_ != hipSuccess)                                                        \
+      return fail((c), LA_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+la_status check_config(const la_config* cfg, std::string* why) {
+  auto bad = [&](const char* m) { if (why) *why = m; return LA_ERR_INVALID_ARG; };
+  auto uns = [&](const char* m) { if (why) *why = m; return LA_ERR_UNSUPPORTED; };
+  if (!cfg) return bad("config is NULL");
+  const la_config& c = *cfg;
+  if (c.n_layers < 1 || c.d_model < 1 || c.n_heads < 1 || c.n_kv_heads < 1 || c.head_dim < 2 ||
+      c.d_ffn < 1 || c.vocab < 2 || c.max_ctx < 1)
+    return bad("dimensions must be positive");
+  if (c.n_heads % c.n_kv_heads) return bad("n_heads must be a multiple of n_kv_heads");
+  if (c.N < 2 || c.N > 32) return bad("N must be in 2..32");
+  if (c.W < 0 || c.G < 0) return bad("W and G must be >= 0");
+  if (!(c.rms_eps > 0.f) || !(c.rope_theta > 0.f)) return bad("rms_eps and rope_theta must be > 0");
+  if (c.dtype != LA_F32 && c.dtype != LA_BF16) return bad("dtype must be LA_F32 or LA_BF16");
+  long T = 1 + (long)(c.W + c.G) * (c.N - 1);
+  if (T > MAX_ROWS) return uns("1 + (W+G)(N-1) must be <= 256");
+  if (c.max_ctx < T + 1) return bad("max_ctx must exceed the step's rows");
+  if (c.head_dim % 2) return bad("head_dim must be even");
+  if (c.dtype == LA_BF16) {
+    if (c.head_dim != 128) return uns("bf16 kernels need head_dim 128");
+    if (c.d_model % 32 || c.d_ffn % 32 || c.vocab % 32)
+      return uns("bf16 kernels need d_model, d_ffn and vocab multiples of 32");
+  } else {
+    if (c.head_dim > 256) return uns("f32 kernels need head_dim <= 256");
+    if (c.d_model % 2 || c.d_ffn % 2 || c.vocab % 2) return uns("f32 kernels need even sizes");
+    if (c.max_ctx > 16384) return uns("f32 kernels need max_ctx <= 16384");
+  }
+  return LA_OK;
+}
+
+// Lay out (or measure) the workspace.  Returns the byte count.
+size_t carve(la_ctx* c, void* base) {
+  const la_config& g = c->cfg;
+  Carver cv(base);
+  const int d = g.d_model, V = g.vocab, F = g.d_ffn, dh = g.head_dim;
+  c->st = cv.take<DevState>(1);
+  c->res_dev = cv.take<DevResult>(1);
+  c->tail_buf = cv.take<int32_t>(32);
+  c->tokens = cv.take<int32_t>(c->MR);
+  c->relpos = cv.take<int32_t>(c->MR);
+  c->amax = cv.take<int32_t>(c->MR);
+  c->prompt_buf = cv.take<int32_t>(c->MR);
+  c->win = cv.take<int32_t>((size_t)std::max(1, (g.N - 1) * g.W));
+  c->pool_len = cv.take<int32_t>(V);
+  c->pool = cv.take<int32_t>((size_t)V * std::max(1, g.G) * (g.N - 1));
+  c->x = cv.take<float>((size_t)c->MR * d);
+  c->logits = cv.take<float>((size_t)c->MR * V);
+  c->xn = cv.take<char>((size_t)c->MR * std::max(d, c->qdim) * c->elem);
+  c->ffa = cv.take<char>((size_t)c->MR * F * c->elem);
+  c->qb = cv.take<char>((size_t)c->MR * c->qdim * c->elem);
+  c->rope_cos = cv.take<float>((size_t)c->ctx_stride * (dh / 2));
+  c->rope_sin = cv.take<float>((size_t)c->ctx_stride * (dh / 2));
+  c->kv_layer_elems = (size_t)g.n_kv_heads * c->ctx_stride * dh;
+  c->kcache = cv.take<char>(c->kv_layer_elems * g.n_layers * c->elem);
+  c->vtcache = cv.take<char>(c->kv_layer_elems * g.n_layers * c->elem);
+  if (c->bf16) {
+    c->ks_qkv = gemm_bf16_ksplit(c->qkv_rows, d);
+    c->ks_o = gemm_bf16_ksplit(d, c->qdim);
+    c->ks_gu = gemm_bf16_ksplit(2 * F, d);
+    c->ks_d = gemm_bf16_ksplit(d, F);
+    c->ks_lm = gemm_bf16_ksplit(V, d);
+    size_t gp = 0;
+    gp = std::max(gp, gemm_bf16_partial_floats(c->qkv_rows, c->MR, c->ks_qkv));
+    gp = std::max(gp, gemm_bf16_partial_floats(d, c->MR, c->ks_o));
+    gp = std::max(gp, gemm_bf16_partial_floats(2 * F, c->MR, c->ks_gu));
+    gp = std::max(gp, gemm_bf16_partial_floats(d, c->MR, c->ks_d));
+    gp = std::max(gp, gemm_bf16_partial_floats(V, c->MR, c->ks_lm));
+    c->gpart = cv.take<float>(std::max<size_t>(gp, 1));
+    int tiles = std::max(std::max(gemm_bf16_tiles(c->qkv_rows), gemm_bf16_tiles(2 * F)),
+                         std::max(gemm_bf16_tiles(d), gemm_bf16_tiles(V)));
+    c->counters = cv.take<int32_t>(tiles);
+    c->attn_splits = attn_bf16_splits(g.n_heads, c->T, c->ctx_stride);
+    size_t ap = attn_bf16_partial_floats(g.n_heads, c->MR, c->attn_splits, dh);
+    size_t rows16 = (size_t)g.n_heads * c->attn_splits * c->MR;
+    c->attn_po = cv.take<float>(rows16 * dh);
+    c->attn_pml = cv.take<float>(rows16 * 2);
+    (void)ap;
+  }
+  // weights owned by the workspace
+  c->layers.assign(g.n_layers, Layer{});
+  for (int l = 0; l < g.n_layers; l++) {
+    Layer& L = c->layers[l];
+    L.wqkv = cv.take<char>((size_t)c->qkv_rows * d * c->elem);
+    if (c->bf16) {
+      L.wo = cv.take<char>((size_t)d * c->qdim * 2);
+      L.wgu = cv.take<char>((size_t)2 * F * d * 2);
+      L.wd = cv.take<char>((size_t)d * F * 2);
+    }
+  }
+  if (c->bf16) c->lm = cv.take<char>((size_t)V * d * 2);
+  return align_up(cv.off, 256);
+}
+
+void init_dims(la_ctx* c, const la_config* cfg) {
+  c->cfg = *cfg;
+  c->T = 1 + (cfg->W + cfg->G) * (cfg->N - 1);
+  c->MR = std::max((int)align_up(c->T, 64), 128);
+  c->bf16 = cfg->dtype == LA_BF16;
+  c->elem = c->bf16 ? 2 : 4;
+  c->ctx_stride = (int)align_up(cfg->max_ctx, 64);
+  c->qdim = cfg->n_heads * cfg->head_dim;
+  c->kvdim = cfg->n_kv_heads * cfg->head_dim;
+  c->qkv_rows = c->qdim + 2 * c->kvdim;
+}
+
+void* layer_k(la_ctx* c, int l) { return (char*)c->kcache + (size_t)l * c->kv_layer_elems * c->elem; }
+void* layer_v(la_ctx* c, int l) { return (char*)c->vtcache + (size_t)l * c->kv_layer_elems * c->elem; }
+
+EpiArgs base_epi(la_ctx* c, int M) {
+  EpiArgs ea;
+  memset(&ea, 0, sizeof(ea));
+  ea.M = M;
+  ea.st = c->st;
+  ea.relpos = c->relpos;
+  ea.rope_cos = c->rope_cos;
+  ea.rope_sin = c->rope_sin;
+  ea.qdim = c->qdim;
+  ea.kvdim = c->kvdim;
+  ea.dh = c->cfg.head_dim;
+  ea.max_ctx = c->ctx_stride;
+  return ea;
+}
+
+void gemm(la_ctx* c, int epi, const void* X, const void* W, const void* W2, int K, int N,
+          int M, int ks, const EpiArgs& ea, hipStream_t s) {
+  if (c->bf16)
+    launch_gemm_bf16(epi, (const uint16_t*)X, (const uint16_t*)W, K, N, M, ks, c->gpart,
+                     c->counters, ea, s);
+  else
+    launch_gemm_f32(epi, (const float*)X, (const float*)W, (const float*)W2, K, N, M, ea, s);
+}
+
+// The decoder over the assembled rows (x holds their embeddings).
+void enqueue_layers(la_ctx* c, int M, int mode, hipStream_t s, Prof* pf = nullptr) {
+#define P_BEGIN(k) if (pf) pf->begin(k)
+#define P_END() if (pf) pf->end()
+  const la_config& g = c->cfg;
+  const int d = g.d_model, F = g.d_ffn;
+  for (int l = 0; l < g.n_layers; l++) {
+    const Layer& L = c->layers[l];
+    P_BEGIN(LA_PROF_NORM);
+    launch_rmsnorm(c->x, L.anorm, M, d, g.rms_eps, c->bf16, c->xn, s);
+    P_END();
+    EpiArgs ea = base_epi(c, M);
+    ea.out_act = c->qb;
+    ea.k_cache = layer_k(c, l);
+    ea.vt_cache = layer_v(c, l);
+    P_BEGIN(LA_PROF_QKV);
+    gemm(c, EPI_QKV, c->xn, L.wqkv, nullptr, d, c->qkv_rows, M, c->ks_qkv, ea, s);
+    P_END();
+    AttnArgs aa;
+    memset(&aa, 0, sizeof(aa));
+    aa.q = c->qb;
+    aa.k_cache = layer_k(c, l);
+    aa.vt_cache = layer_v(c, l);
+    aa.out = c->xn;
+    aa.st = c->st;
+    aa.M = M;
+    aa.mode = mode;
+    aa.H = g.n_heads;
+    aa.Hkv = g.n_kv_heads;
+    aa.dh = g.head_dim;
+    aa.ctx_stride = c->ctx_stride;
+    aa.W = g.W;
+    aa.N = g.N;
+    aa.part_o = c->attn_po;
+    aa.part_ml = c->attn_pml;
+    aa.splits = c->attn_splits;
+    P_BEGIN(LA_PROF_ATTN);
+    if (c->bf16) launch_attn_bf16(aa, s);
+    else launch_attn_f32(aa, s);
+    P_END();
+    ea = base_epi(c, M);
+    ea.out_f32 = c->x;
+    ea.ld_out = d;
+    P_BEGIN(LA_PROF_O);
+    gemm(c, EPI_RESID, c->xn, L.wo, nullptr, c->qdim, d, M, c->ks_o, ea, s);
+    P_END();
+    P_BEGIN(LA_PROF_NORM);
+    launch_rmsnorm(c->x, L.fnorm, M, d, g.rms_eps, c->bf16, c->xn, s);
+    P_END();
+    ea = base_epi(c, M);
+    ea.out_act = c->ffa;
+    ea.ld_out = F;
+    P_BEGIN(LA_PROF_GATEUP);
+    if (c->bf16) gemm(c, EPI_SWIGLU, c->xn, L.wgu, nullptr, d, 2 * F, M, c->ks_gu, ea, s);
+    else gemm(c, EPI_SWIGLU, c->xn, L.wg, L.wu, d, F, M, 1, ea, s);
+    P_END();
+    ea = base_epi(c, M);
+    ea.out_f32 = c->x;
+    ea.ld_out = d;
+    P_BEGIN(LA_PROF_DOWN);
+    gemm(c, EPI_RESID, c->ffa, L.wd, nullptr, F, d, M, c->ks_d, ea, s);
+    P_END();
+  }
+}
+
+void enqueue_head(la_ctx* c, int M, hipStream_t s, Prof* pf = nullptr) {
+  const la_config& g = c->cfg;
+  P_BEGIN(LA_PROF_NORM);
+  launch_rmsnorm(c->x, c->final_norm, M, g.d_model, g.rms_eps, c->bf16, c->xn, s);
+  P_END();
+  EpiArgs ea = base_epi(c, M);
+  ea.out_f32 = c->logits;
+  ea.ld_out = g.vocab;
+  P_BEGIN(LA_PROF_LMHEAD);
+  gemm(c, EPI_LOGITS, c->xn, c->lm, nullptr, g.d_model, g.vocab, M, c->ks_lm, ea, s);
+  P_END();
+  P_BEGIN(LA_PROF_OTHER);
+  launch_argmax(c->logits, M, g.vocab, c->amax, s);
+  P_END();
+}
+
+void enqueue_step(la_ctx* c, hipStream_t s, Prof* pf = nullptr) {
+  const la_config& g = c->cfg;
+  P_BEGIN(LA_PROF_OTHER);
+  launch_assemble(MODE_STEP, c->st, c->win, c->pool_len, c->pool, nullptr, c->T, g.W, g.N, g.G,
+                  c->tokens, c->relpos, c->st, c->emb, g.d_model, c->bf16, c->x, s);
+  P_END();
+  enqueue_layers(c, c->T, MODE_STEP, s, pf);
+  enqueue_head(c, c->T, s, pf);
+  P_BEGIN(LA_PROF_OTHER);
+  launch_verify(c->st, c->tokens, c->amax, c->win, c->pool_len, c->pool, g.W, g.N, g.G,
+                c->res_dev, s);
+  P_END();
+  P_BEGIN(LA_PROF_OTHER);
+  launch_kv_compact(c->st, g.n_layers, g.n_kv_heads, g.head_dim, c->ctx_stride, g.W, g.N,
+                    c->elem, c->kcache, c->vtcache, s);
+  P_END();
+  (void)hipMemcpyAsync(c->res_host, c->res_dev, sizeof(DevResult), hipMemcpyDeviceToHost, s);
+}
+#undef P_BEGIN
+#undef P_END
+
+la_status check_usable(la_ctx* c) {
+  if (!c) return LA_ERR_INVALID_ARG;
+  if (c->poisoned) return fail(c, LA_ERR_STATE, "context poisoned by an earlier HIP failure: " + c->err);
+  return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* la_status_string(la_status s) {
+  switch (s) {
+    case LA_OK: return "ok";
+    case LA_ERR_INVALID_ARG: return "invalid argument";
+    case LA_ERR_STATE: return "invalid state";
+    case LA_ERR_OUT_OF_CAPACITY: return "out of capacity";
+    case LA_ERR_HIP: return "HIP error";
+    case LA_ERR_UNSUPPORTED: return "unsupported";
+  }
+  return "unknown status";
+}
+
+const char* la_last_error(const la_ctx* c) { return c ? c->err.c_str() : "no context"; }
+
+int32_t la_step_rows(const la_ctx* c) { return c ? c->T : 0; }
+
+size_t la_workspace_bytes(const la_config* cfg) {
+  if (check_config(cfg, nullptr) != LA_OK) return 0;
+  la_ctx tmp;
+  init_dims(&tmp, cfg);
+  return carve(&tmp, nullptr);
+}
+
+la_status la_create(const la_config* cfg, const void* const* weights, void* workspace,
+                    size_t workspace_bytes, void* hip_stream, la_ctx** out) {
+  if (!out) return LA_ERR_INVALID_ARG;
+  *out = nullptr;
+  std::string why;
+  la_status vs = check_config(cfg, &why);
+  if (vs != LA_OK) return vs;
+  if (!weights || !workspace) return LA_ERR_INVALID_ARG;
+  const int nw = 3 + 9 * cfg->n_layers;
+  for (int i = 0; i < nw; i++)
+    if (!weights[i]) return LA_ERR_INVALID_ARG;
+  la_ctx* c = new la_ctx();
+  init_dims(c, cfg);
+  size_t need = carve(c, nullptr);
+  if (workspace_bytes < need) {
+    delete c;
+    return LA_ERR_OUT_OF_CAPACITY;
+  }
+  carve(c, workspace);
+  c->stream = (hipStream_t)hip_stream;
+  const char* ng = getenv("LA_NO_GRAPH");
+  c->use_graph = !(ng && ng[0] == '1');
+  *out = c;
+  hipStream_t s = c->stream;
+  const la_config& g = c->cfg;
+  const int d = g.d_model, F = g.d_ffn, V = g.vocab, dh = g.head_dim;
+
+  // pinned host buffers
+  c->pin_count = std::max<size_t>(c->MR, (size_t)std::max(1, (g.N - 1) * g.W)) + 64;
+  LA_HIP(c, hipHostMalloc((void**)&c->res_host, sizeof(DevResult), hipHostMallocDefault));
+  LA_HIP(c, hipHostMalloc((void**)&c->pin, c->pin_count * sizeof(int32_t), hipHostMallocDefault));
+  memset(c->res_host, 0, sizeof(DevResult));
+
+  // clear state, caches and activations (fill kernels: finite padding rows)
+  launch_fill_u32(workspace, 0, need / 4, s);
+
+  // rotary tables: angle = pos * theta^(-2i/dh), computed in double
+  {
+    std::vector<float> cs((size_t)c->ctx_stride * (dh / 2)), sn(cs.size());
+    for (int p = 0; p < c->ctx_stride; p++)
+      for (int i = 0; i < dh / 2; i++) {
+        double ang = (double)p * pow((double)g.rope_theta, -2.0 * i / dh);
+        cs[(size_t)p * (dh / 2) + i] = (float)cos(ang);
+        sn[(size_t)p * (dh / 2) + i] = (float)sin(ang);
+      }
+    LA_HIP(c, hipMemcpyAsync(c->rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, s));
+    LA_HIP(c, hipMemcpyAsync(c->rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, s));
+    LA_HIP(c, hipStreamSynchronize(s));
+  }
+
+  // weights
+  c->emb = weights[0];
+  c->final_norm = weights[1];
+  for (int l = 0; l < g.n_layers; l++) {
+    const void* const* lw = weights + 3 + 9 * l;
+    Layer& L = c->layers[l];
+    L.anorm = lw[0];
+    L.fnorm = lw[5];
+    L.wg = lw[6];
+    L.wu = lw[7];
+    if (c->bf16) {
+      uint16_t* q = (uint16_t*)L.wqkv;
+      launch_repack_bf16((const uint16_t*)lw[1], c->qdim, d, q, 0, 1, s);
+      launch_repack_bf16((const uint16_t*)lw[2], c->kvdim, d, q, c->qdim / 16, 1, s);
+      launch_repack_bf16((const uint16_t*)lw[3], c->kvdim, d, q, (c->qdim + c->kvdim) / 16, 1, s);
+      launch_repack_bf16((const uint16_t*)lw[4], d, c->qdim, (uint16_t*)L.wo, 0, 1, s);
+      launch_repack_bf16((const uint16_t*)lw[6], F, d, (uint16_t*)L.wgu, 0, 2, s);
+      launch_repack_bf16((const uint16_t*)lw[7], F, d, (uint16_t*)L.wgu, 1, 2, s);
+      launch_repack_bf16((const uint16_t*)lw[8], d, F, (uint16_t*)L.wd, 0, 1, s);
+    } else {
+      char* q = (char*)L.wqkv;
+      LA_HIP(c, hipMemcpyAsync(q, lw[1], (size_t)c->qdim * d * 4, hipMemcpyDeviceToDevice, s));
+      LA_HIP(c, hipMemcpyAsync(q + (size_t)c->qdim * d * 4, lw[2], (size_t)c->kvdim * d * 4,
+                               hipMemcpyDeviceToDevice, s));
+      LA_HIP(c, hipMemcpyAsync(q + (size_t)(c->qdim + c->kvdim) * d * 4, lw[3],
+                               (size_t)c->kvdim * d * 4, hipMemcpyDeviceToDevice, s));
+      L.wo = lw[4];
+      L.wd = lw[8];
+    }
+  }
+  if (c->bf16) launch_repack_bf16((const uint16_t*)weights[2], V, d, (uint16_t*)c->lm, 0, 1, s);
+  else c->lm = weights[2];
+  LA_HIP(c, hipGetLastError());
+  LA_HIP(c, hipStreamSynchronize(s));
+
+  // capture the step
+  if (c->use_graph) {
+    hipStream_t cs;
+    LA_HIP(c, hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+    hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (e == hipSuccess) {
+      enqueue_step(c, cs);
+      e = hipStreamEndCapture(cs, &c->graph);
+    }
+    if (e == hipSuccess) e = hipGraphInstantiate(&c->gexec, c->graph, nullptr, nullptr, 0);
+    (void)hipStreamDestroy(cs);
+    if (e != hipSuccess) return fail(c, LA_ERR_HIP, std::string("step graph capture: ") + hipGetErrorString(e));
+  }
+  return LA_OK;
+}
+
+la_status la_prefill(la_ctx* c, const int32_t* prompt, int32_t n_prompt, const int32_t* init_window,
+                     int32_t* first_token) {
+  la_status us = check_usable(c);
+  if (us != LA_OK) return us;
+  const la_config& g = c->cfg;
+  if (!prompt || n_prompt < 1 || !first_token) return fail(c, LA_ERR_INVALID_ARG, "prompt/first_token");
+  if (g.W > 0 && !init_window) return fail(c, LA_ERR_INVALID_ARG, "init_window required when W > 0");
+  for (int i = 0; i < n_prompt; i++)
+    if (prompt[i] < 0 || prompt[i] >= g.vocab) return fail(c, LA_ERR_INVALID_ARG, "prompt token out of range");
+  const int nwin = (g.N - 1) * g.W;
+  for (int i = 0; i < nwin; i++)
+    if (init_window[i] < 0 || init_window[i] >= g.vocab) return fail(c, LA_ERR_INVALID_ARG, "window token out of range");
+  if ((long)n_prompt + c->T > g.max_ctx) return fail(c, LA_ERR_OUT_OF_CAPACITY, "prompt + step rows exceed max_ctx");
+  hipStream_t s = c->stream;
+  c->prefilled = false;
+  launch_fill_u32(c->st, 0, sizeof(DevState) / 4, s);
+  launch_fill_u32(c->pool_len, 0, (size_t)g.vocab, s);
+  if (nwin > 0) {
+    memcpy(c->pin, init_window, sizeof(int32_t) * nwin);
+    LA_HIP(c, hipMemcpyAsync(c->win, c->pin, sizeof(int32_t) * nwin, hipMemcpyHostToDevice, s));
+    LA_HIP(c, hipStreamSynchronize(s));
+  }
+  for (int p0 = 0; p0 < n_prompt; p0 += c->MR) {
+    const int m = std::min(c->MR, n_prompt - p0);
+    const bool last = p0 + m == n_prompt;
+    memcpy(c->pin, prompt + p0, sizeof(int32_t) * m);
+    LA_HIP(c, hipMemcpyAsync(c->prompt_buf, c->pin, sizeof(int32_t) * m, hipMemcpyHostToDevice, s));
+    launch_assemble(MODE_CAUSAL, c->st, c->win, c->pool_len, c->pool, c->prompt_buf, m, g.W, g.N,
+                    g.G, c->tokens, c->relpos, c->st, c->emb, g.d_model, c->bf16, c->x, s);
+    enqueue_layers(c, m, MODE_CAUSAL, s);
+    if (last) enqueue_head(c, m, s);
+    launch_advance(c->st, m, c->amax, last ? 1 : 0, s);
+    LA_HIP(c, hipGetLastError());
+    LA_HIP(c, hipStreamSynchronize(s));
+  }
+  DevState hs;
+  LA_HIP(c, hipMemcpy(&hs, c->st, sizeof(hs), hipMemcpyDeviceToHost));
+  c->kv_len_host = hs.L;
+  *first_token = hs.cur;
+  c->prefilled = true;
+  return LA_OK;
+}
+
+la_status la_step(la_ctx* c, la_step_result* out) {
+  la_status us = check_usable(c);
+  if (us != LA_OK) return us;
+  if (!out) return fail(c, LA_ERR_INVALID_ARG, "out is NULL");
+  if (!c->prefilled) return fail(c, LA_ERR_STATE, "la_step before la_prefill");
+  if ((long)c->kv_len_host + c->T > c->cfg.max_ctx)
+    return fail(c, LA_ERR_OUT_OF_CAPACITY, "kv_len + step rows exceed max_ctx");
+  if (c->use_graph) {
+    LA_HIP(c, hipGraphLaunch(c->gexec, c->stream));
+  } else {
+    enqueue_step(c, c->stream);
+    LA_HIP(c, hipGetLastError());
+  }
+  LA_HIP(c, hipStreamSynchronize(c->stream));
+  static_assert(sizeof(DevResult) == sizeof(la_step_result), "result layout");
+  memcpy(out, c->res_host, sizeof(*out));
+  c->kv_len_host = out->kv_len;
+  return LA_OK;
+}
+
+la_status la_profile_step(la_ctx* c, float* ms, int32_t* launches, la_step_result* out) {
+  la_status us = check_usable(c);
+  if (us != LA_OK) return us;
+  if (!out || !ms || !launches) return fail(c, LA_ERR_INVALID_ARG, "NULL output");
+  if (!c->prefilled) return fail(c, LA_ERR_STATE, "la_profile_step before la_prefill");
+  if ((long)c->kv_len_host + c->T > c->cfg.max_ctx)
+    return fail(c, LA_ERR_OUT_OF_CAPACITY, "kv_len + step rows exceed max_ctx");
+  LA_HIP(c, hipStreamSynchronize(c->stream));
+  Prof pf;
+  pf.pool = &c->events;
+  pf.s = c->stream;
+  enqueue_step(c, c->stream, &pf);
+  LA_HIP(c, hipGetLastError());
+  LA_HIP(c, hipStreamSynchronize(c->stream));
+  for (int k = 0; k < LA_PROF_CLASSES; k++) {
+    ms[k] = 0.f;
+    launches[k] = 0;
+  }
+  for (size_t i = 0; i < pf.cat.size(); i++) {
+    float t = 0.f;
+    LA_HIP(c, hipEventElapsedTime(&t, c->events[2 * i], c->events[2 * i + 1]));
+    ms[pf.cat[i]] += t;
+    launches[pf.cat[i]] += 1;
+  }
+  memcpy(out, c->res_host, sizeof(*out));
+  c->kv_len_host = out->kv_len;
+  return LA_OK;
+}
+
+la_status la_destroy(la_ctx* c) {
+  if (!c) return LA_OK;
+  (void)hipStreamSynchronize(c->stream);
+  if (c->gexec) (void)hipGraphExecDestroy(c->gexec);
+  if (c->graph) (void)hipGraphDestroy(c->graph);
+  for (hipEvent_t e : c->events) (void)hipEventDestroy(e);
+  if (c->res_host) (void)hipHostFree(c->res_host);
+  if (c->pin) (void)hipHostFree(c->pin);
+  delete c;
+  return LA_OK;
+}
+
+la_status la_debug_logits(la_ctx* c, float* host, size_t n) {
+  la_status us = check_usable(c);
+  if (us != LA_OK) return us;
+  size_t need = (size_t)c->T * c->cfg.vocab;
+  if (!host || n < need) return fail(c, LA_ERR_INVALID_ARG, "logits buffer too small");
+  LA_HIP(c, hipStreamSynchronize(c->stream));
+  LA_HIP(c, hipMemcpy(host, c->logits, need * sizeof(float), hipMemcpyDeviceToHost));
+  return LA_OK;
+}
+
+la_status la_debug_block(la_ctx* c, int32_t* tokens, int32_t* amax) {
+  la_status us = check_usable(c);
+  if (us != LA_OK) return us;
+  LA_HIP(c, hipStreamSynchronize(c->stream));
+  if (tokens) LA_HIP(c, hipMemcpy(tokens, c->tokens, sizeof(int32_t) * c->T, hipMemcpyDeviceToHost));
+  if (amax) LA_HIP(c, hipMemcpy(amax, c->amax, sizeof(int32_t) * c->T, hipMemcpyDeviceToHost));
+  return LA_OK;
+}
+
+la_status la_debug_window(la_ctx* c, int32_t* win) {
+  la_status us = check_usable(c);
+  if (us != LA_OK) return us;
+  const int n = (c->cfg.N - 1) * c->cfg.W;
+  if (n == 0) return LA_OK;
+  if (!win) return fail(c, LA_ERR_INVALID_ARG, "win is NULL");
+  LA_HIP(c, hipStreamSynchronize(c->stream));
+  LA_HIP(c, hipMemcpy(win, c->win, sizeof(int32_t) * n, hipMemcpyDeviceToHost));
+  return LA_OK;
+}
+
+la_status la_debug_pool(la_ctx* c, int32_t* len, int32_t* tails) {
+  la_status us = check_usable(c);
+  if (us != LA_OK) return us;
+  const la_config& g = c->cfg;
+  LA_HIP(c, hipStreamSynchronize(c->stream));
+  if (len) LA_HIP(c, hipMemcpy(len, c->pool_len, sizeof(int32_t) * g.vocab, hipMemcpyDeviceToHost));
+  if (tails && g.G > 0)
+    LA_HIP(c, hipMemcpy(tails, c->pool, sizeof(int32_t) * (size_t)g.vocab * g.G * (g.N - 1),
+                        hipMemcpyDeviceToHost));
+  return LA_OK;
+}
+
+la_status la_debug_pool_insert(la_ctx* c, int32_t key, const int32_t* tail) {
+  la_status us = check_usable(c);
+  if (us != LA_OK) return us;
+  const la_config& g = c->cfg;
+  if (!tail || key < 0 || key >= g.vocab) return fail(c, LA_ERR_INVALID_ARG, "key/tail");
+  for (int i = 0; i < g.N - 1; i++)
+    if (tail[i] < 0 || tail[i] >= g.vocab) return fail(c, LA_ERR_INVALID_ARG, "tail token out of range");
+  LA_HIP(c, hipStreamSynchronize(c->stream));
+  memcpy(c->pin, tail, sizeof(int32_t) * (g.N - 1));
+  LA_HIP(c, hipMemcpyAsync(c->tail_buf, c->pin, sizeof(int32_t) * (g.N - 1), hipMemcpyHostToDevice,
+                           c->stream));
+  launch_pool_insert(c->st, key, c->tail_buf, c->pool_len, c->pool, g.N, g.G, c->stream);
+  LA_HIP(c, hipGetLastError());
+  LA_HIP(c, hipStreamSynchronize(c->stream));
+  return LA_OK;
+}
+
+la_status la_debug_kv(la_ctx* c, int32_t layer, int32_t pos0, int32_t n, float* k, float* v) {
+  la_status us = check_usable(c);
+  if (us != LA_OK) return us;
+  const la_config& g = c->cfg;
+  if (layer < 0 || layer >= g.n_layers || pos0 < 0 || n < 0 || pos0 + n > g.max_ctx || !k || !v)
+    return fail(c, LA_ERR_INVALID_ARG, "kv range");
+  LA_HIP(c, hipStreamSynchronize(c->stream));
+  const int dh = g.head_dim, Hkv = g.n_kv_heads, es = c->elem;
+  std::vector<char> kb((size_t)n * dh * es), vb((size_t)dh * n * es);
+  for (int h = 0; h < Hkv; h++) {
+    const char* ks = (const char*)layer_k(c, layer) + (((size_t)h * c->ctx_stride + pos0) * dh) * es;
+    LA_HIP(c, hipMemcpy(kb.data(), ks, kb.size(), hipMemcpyDeviceToHost));
+    const char* vs = (const char*)layer_v(c, layer) + ((size_t)h * dh * c->ctx_stride + pos0) * es;
+    LA_HIP(c, hipMemcpy2D(vb.data(), (size_t)n * es, vs, (size_t)c->ctx_stride * es, (size_t)n * es, dh,
+                          hipMemcpyDeviceToHost));
+    for (int p = 0; p < n; p++)
+      for (int i = 0; i < dh; i++) {
+        size_t o = ((size_t)h * n + p) * dh + i;
+        size_t ki = (size_t)p * dh + i, vi = (size_t)i * n + p;
+        if (es == 2) {
+          k[o] = bf2f(((const uint16_t*)kb.data())[ki]);
+          v[o] = bf2f(((const uint16_t*)vb.data())[vi]);
+        } else {
+          k[o] = ((const float*)kb.data())[ki];
+          v[o] = ((const float*)vb.data())[vi];
+        }
+      }
+  }
+  return LA_OK;
+}
+
+la_status la_debug_state(la_ctx* c, int32_t* kv_len, int32_t* current) {
+  la_status us = check_usable(c);
+  if (us != LA_OK) return us;
+  DevState hs;
+  LA_HIP(c, hipStreamSynchronize(c->stream));
+  LA_HIP(c, hipMemcpy(&hs, c->st, sizeof(hs), hipMemcpyDeviceToHost));
+  if (kv_len) *kv_len = hs.L;
+  if (current) *current = hs.cur;
+  return LA_OK;
+}
+
+size_t la_attention_workspace_bytes(int32_t n_heads, int32_t head_dim, int32_t ctx_stride, int32_t W,
+                                    int32_t N, int32_t G) {
+  if (n_heads < 1 || head_dim != 128 || ctx_stride < 1 || N < 2 || W < 0 || G < 0) return 0;
+  const int T = 1 + (W + G) * (N - 1);
+  if (T > MAX_ROWS) return 0;
+  const int splits = attn_bf16_splits(n_heads, T, ctx_stride);
+  const size_t rows = (size_t)n_heads * splits * ((T + 15) & ~15);
+  return align_up(rows * head_dim * 4, 256) + align_up(rows * 2 * 4, 256);
+}
+
+la_status la_attention(const void* q, const void* k_cache, const void* vt_cache, void* out,
+                       int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t prefix_len,
+                       int32_t ctx_stride, int32_t W, int32_t N, int32_t G, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !vt_cache || !out) return LA_ERR_INVALID_ARG;
+  if (n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads || N < 2 || N > 32 || W < 0 || G < 0 ||
+      prefix_len < 0 || ctx_stride < 1)
+    return LA_ERR_INVALID_ARG;
+  if (head_dim != 128) return LA_ERR_UNSUPPORTED;
+  const long T = 1 + (long)(W + G) * (N - 1);
+  if (T > MAX_ROWS) return LA_ERR_UNSUPPORTED;
+  if (ctx_stride % 64 || prefix_len + T > ctx_stride) return LA_ERR_INVALID_ARG;
+  const size_t need = la_attention_workspace_bytes(n_heads, head_dim, ctx_stride, W, N, G);
+  if (!workspace || workspace_bytes < need) return LA_ERR_OUT_OF_CAPACITY;
+  AttnArgs aa;
+  memset(&aa, 0, sizeof(aa));
+  aa.splits = attn_bf16_splits(n_heads, (int)T, ctx_stride);
+  const size_t rows = (size_t)n_heads * aa.splits * ((T + 15) & ~15);
+  aa.part_o = (float*)workspace;
+  aa.part_ml = (float*)((char*)workspace + align_up(rows * head_dim * 4, 256));
+  aa.q = q;
+  aa.k_cache = k_cache;
+  aa.vt_cache = vt_cache;
+  aa.out = out;
+  aa.st = nullptr;
+  aa.L_host = prefix_len;
+  aa.M = (int)T;
+  aa.mode = MODE_STEP;
+  aa.H = n_heads;
+  aa.Hkv = n_kv_heads;
+  aa.dh = head_dim;
+  aa.ctx_stride = ctx_stride;
+  aa.W = W;
+  aa.N = N;
+  launch_attn_bf16(aa, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,193 @@
+// Internal declarations shared by the HIP sources of the lookahead library.
+// Device helpers, the block-row mask, kernel parameter structs and the host
+// launchers each kernel file provides.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+// ---------------------------------------------------------------------------
+// element types
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// bfloat16 <-> float through bit patterns (round to nearest even).
+__host__ __device__ inline float bf2f(uint16_t b) {
+  union { uint32_t u; float f; } v;
+  v.u = (uint32_t)b << 16;
+  return v.f;
+}
+__host__ __device__ inline uint16_t f2bf(float f) {
+  union { uint32_t u; float f; } v;
+  v.f = f;
+  uint32_t u = v.u;
+  if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffff) ? 0x40 : 0));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// Device-resident decoding state.  Scalars that change every step live here
+// (not in launch arguments) so one captured graph replays every step.
+
+struct DevState {
+  int32_t L;       // committed KV length
+  int32_t cur;     // current token (its KV is not committed yet)
+  int32_t n_cand;  // valid candidates in the block being forwarded
+  int32_t L_old;   // committed length before the last commit
+  int32_t k;       // accepted candidate tokens of the last step
+  int32_t winner;  // g* of the last step, -1 without candidates
+  int32_t pad[2];
+};
+
+// Mirror of la_step_result (include/la.h); written by the verify kernel and
+// copied to pinned host memory at the end of a step.
+struct DevResult {
+  int32_t n_emitted;
+  int32_t tokens[32];
+  int32_t accepted;
+  int32_t winner;
+  int32_t n_candidates;
+  int32_t kv_len;
+};
+
+// Mask modes of a forwarded block.
+enum { MODE_STEP = 0, MODE_CAUSAL = 1 };
+
+// ---------------------------------------------------------------------------
+// Block-row layout of one lookahead step ("Break the Sequential Dependency of
+// LLM Inference Using Lookahead Decoding", Summary: the lookahead branch's 2D
+// window and the verification branch run in one forward pass).
+//   row 0                        current token, relative position 0
+//   1 + (l-1)*W + j              window level l (1..N-1), column j;
+//                                relative position l + j
+//   1 + (N-1)*W + g*(N-1) + i-1  candidate g, token i (1..N-1); position i
+// A row sees the whole committed cache plus: row 0 sees itself; window row
+// (l, j) sees row 0, level-1 rows of columns <= j and the rows of column j at
+// levels 2..l; candidate row (g, i) sees row 0 and (g, i') for i' <= i.  So
+// each row sees exactly one causal sequence: its column's diagonal through
+// the window, or its candidate's prefix.
+
+struct RowDesc {
+  int kind;  // 0 current, 1 window, 2 candidate
+  int a, b;  // window: level (1-based), column; candidate: g, i (1-based)
+};
+
+__host__ __device__ inline RowDesc row_desc(int r, int W, int N) {
+  RowDesc d;
+  int nwin = (N - 1) * W;
+  if (r == 0) { d.kind = 0; d.a = 0; d.b = 0; }
+  else if (r <= nwin) { d.kind = 1; d.a = 1 + (r - 1) / W; d.b = (r - 1) % W; }
+  else { d.kind = 2; d.a = (r - 1 - nwin) / (N - 1); d.b = 1 + (r - 1 - nwin) % (N - 1); }
+  return d;
+}
+
+__host__ __device__ inline int row_relpos(const RowDesc& d) {
+  return d.kind == 0 ? 0 : (d.kind == 1 ? d.a + d.b : d.b);
+}
+
+// Does the row described by q see block row described by k?
+__host__ __device__ inline bool row_sees(const RowDesc& q, const RowDesc& k) {
+  if (k.kind == 0) return true;
+  if (q.kind != k.kind) return false;
+  if (q.kind == 1) return k.a == 1 ? k.b <= q.b : (k.b == q.b && k.a <= q.a);
+  return k.a == q.a && k.b <= q.b;
+}
+
+// ---------------------------------------------------------------------------
+// launch parameters
+
+struct ModelDims {
+  int n_layers, d, H, Hkv, dh, ffn, V;
+  int W, N, G;
+  int max_ctx;
+  float eps;
+};
+
+// GEMM epilogues.
+enum { EPI_LOGITS = 0, EPI_RESID = 1, EPI_QKV = 2, EPI_SWIGLU = 3 };
+
+struct EpiArgs {
+  int M;                 // valid rows
+  float* out_f32;        // LOGITS: [M][N]; RESID: residual [M][N], added to
+  void* out_act;         // SWIGLU: [M][ffn] activation; QKV: q [M][H*dh]
+  void* k_cache;         // QKV: [Hkv][max_ctx][dh] of this layer
+  void* vt_cache;        // QKV: [Hkv][dh][max_ctx] of this layer
+  const DevState* st;    // QKV: committed length L
+  const int32_t* relpos; // QKV: relative position of each row
+  const float* rope_cos; // [max_ctx][dh/2]
+  const float* rope_sin;
+  int qdim, kvdim, dh, max_ctx, ld_out;
+};
+
+// ---------------------------------------------------------------------------
+// host launchers (one per kernel family)
+
+// bf16 weights repacked into MFMA A-operand tiles (16 rows x 32 k, 1 KiB):
+// tile (rt, ks) at element offset (rt * (K/32) + ks) * 512; lane l holds
+// W[rt*16 + l%16][ks*32 + (l/16)*8 + e], e = 0..7.
+void launch_repack_bf16(const uint16_t* src, int rows, int K, uint16_t* dst,
+                        int rt_offset, int rt_mult, hipStream_t s);
+
+// Y = X W^T with an epilogue; X bf16 [16*ceil(M/16)][K], W repacked, N rows.
+void launch_gemm_bf16(int epi, const uint16_t* X, const uint16_t* Wp, int K,
+                      int N, int M, int ksplit, float* partial,
+                      int32_t* counters, const EpiArgs& ea, hipStream_t s);
+// Choose a K split for the bf16 GEMM (WG count vs partial-sum traffic).
+int gemm_bf16_ksplit(int N, int K);
+size_t gemm_bf16_partial_floats(int N, int M, int ksplit);
+int gemm_bf16_tiles(int N);
+
+// fp32 path (small models): Y = X W^T with W row-major [N][K] (two
+// matrices for SWIGLU: W2 is the up projection).
+void launch_gemm_f32(int epi, const float* X, const float* W, const float* W2,
+                     int K, int N, int M, const EpiArgs& ea, hipStream_t s);
+
+// masked attention over the cache + block
+struct AttnArgs {
+  const void* q;       // [rows][H*dh] (bf16 or f32)
+  const void* k_cache; // [Hkv][ctx_stride][dh]
+  const void* vt_cache;// [Hkv][dh][ctx_stride]
+  void* out;           // [rows][H*dh]
+  const DevState* st;  // committed length L (device), or NULL: use L_host
+  int L_host;
+  int M;               // rows in the block (valid + padded candidate rows)
+  int mode;            // MODE_STEP / MODE_CAUSAL
+  int H, Hkv, dh, ctx_stride, W, N;
+  float* part_o;       // split-KV partials [H][splits][rows16][dh]
+  float* part_ml;      // [H][splits][rows16][2]
+  int splits;
+};
+void launch_attn_bf16(const AttnArgs& a, hipStream_t s);
+int attn_bf16_splits(int H, int M, int max_ctx);
+size_t attn_bf16_partial_floats(int H, int M, int splits, int dh);
+void launch_attn_f32(const AttnArgs& a, hipStream_t s);
+
+// small kernels
+void launch_fill_u32(void* p, uint32_t v, size_t n, hipStream_t s);
+void launch_assemble(int mode, const DevState* st, const int32_t* win,
+                     const int32_t* pool_len, const int32_t* pool,
+                     const int32_t* prompt, int M, int W, int N, int G,
+                     int32_t* tokens, int32_t* relpos, DevState* st_w,
+                     const void* emb, int d, int bf16, float* x, hipStream_t s);
+void launch_rmsnorm(const float* x, const void* w, int M, int d, float eps,
+                    int bf16, void* out, hipStream_t s);
+void launch_argmax(const float* logits, int M, int V, int32_t* amax,
+                   hipStream_t s);
+void launch_verify(DevState* st, const int32_t* tokens, const int32_t* amax,
+                   int32_t* win, int32_t* pool_len, int32_t* pool, int W,
+                   int N, int G, DevResult* res, hipStream_t s);
+void launch_kv_compact(const DevState* st, int n_layers, int Hkv, int dh,
+                       int max_ctx, int W, int N, int elem, void* k_cache,
+                       void* vt_cache, hipStream_t s);
+void launch_advance(DevState* st, int M, const int32_t* amax, int set_cur,
+                    hipStream_t s);
+void launch_pool_insert(DevState* st, int32_t key, const int32_t* tail_dev,
+                        int32_t* pool_len, int32_t* pool, int N, int G,
+                        hipStream_t s);
+
+}  // namespace la

@@ -1,0 +1,326 @@
+// Small kernels of the lookahead step: block assembly + embedding gather,
+// RMSNorm, per-row argmax, greedy verification with window shift and n-gram
+// pool update, KV compaction, and fills.
+//
+// Method source: "Break the Sequential Dependency of LLM Inference Using
+// Lookahead Decoding" (summary page).  Summary: the lookahead branch keeps a
+// 2D window over recent Jacobi iterations and yields disjoint n-grams; the
+// n-grams are cached in a pool; a verification branch checks pool candidates
+// in the same forward pass so the output equals ordinary decoding.  Key
+// points, "Tuning knobs": W window, N n-gram size, G verification size.
+#include "la_internal.h"
+
+namespace la {
+
+// ---------------------------------------------------------------------------
+
+__global__ void k_fill_u32(uint32_t* p, uint32_t v, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+void launch_fill_u32(void* p, uint32_t v, size_t n, hipStream_t s) {
+  if (!n) return;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t*)p, v, n);
+}
+
+// ---------------------------------------------------------------------------
+// Block assembly: row r's token and relative position, then its embedding.
+//   step mode: row 0 = current token; window row (l, j) = win[l-1][j];
+//   candidate row (g, i) = i-th token of the g-th pool entry of the current
+//   token (oldest entry first), or token 0 for an empty slot (such rows are
+//   isolated by the mask and never committed);
+//   causal mode: row r = prompt[r] at relative position r.
+
+__global__ void k_assemble(int mode, const DevState* __restrict__ st,
+                           const int32_t* __restrict__ win, const int32_t* __restrict__ pool_len,
+                           const int32_t* __restrict__ pool, const int32_t* __restrict__ prompt,
+                           int W, int N, int G, int32_t* tokens, int32_t* relpos,
+                           DevState* st_w, const void* __restrict__ emb, int d, int bf16,
+                           float* __restrict__ x) {
+  const int r = blockIdx.x;
+  int tok, rp;
+  if (mode == MODE_STEP) {
+    const int cur = st->cur;
+    int nc = G > 0 ? pool_len[cur] : 0;
+    nc = nc < G ? nc : G;
+    const RowDesc rd = row_desc(r, W, N);
+    rp = row_relpos(rd);
+    if (rd.kind == 0) tok = cur;
+    else if (rd.kind == 1) tok = win[(rd.a - 1) * W + rd.b];
+    else tok = rd.a < nc ? pool[((size_t)cur * G + rd.a) * (N - 1) + (rd.b - 1)] : 0;
+    if (r == 0 && threadIdx.x == 0) st_w->n_cand = nc;
+  } else {
+    tok = prompt[r];
+    rp = r;
+  }
+  if (threadIdx.x == 0) {
+    tokens[r] = tok;
+    relpos[r] = rp;
+  }
+  float* xr = x + (size_t)r * d;
+  if (bf16) {
+    const uint16_t* e = (const uint16_t*)emb + (size_t)tok * d;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) xr[i] = bf2f(e[i]);
+  } else {
+    const float* e = (const float*)emb + (size_t)tok * d;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) xr[i] = e[i];
+  }
+}
+
+void launch_assemble(int mode, const DevState* st, const int32_t* win,
+                     const int32_t* pool_len, const int32_t* pool, const int32_t* prompt,
+                     int M, int W, int N, int G, int32_t* tokens, int32_t* relpos,
+                     DevState* st_w, const void* emb, int d, int bf16, float* x,
+                     hipStream_t s) {
+  hipLaunchKernelGGL(k_assemble, dim3(M), dim3(256), 0, s, mode, st, win, pool_len, pool,
+                     prompt, W, N, G, tokens, relpos, st_w, emb, d, bf16, x);
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm: out = x / sqrt(mean(x^2) + eps) * w, one workgroup per row
+
+template <typename T>
+__device__ inline float ldw(const void* w, int i);
+template <>
+__device__ inline float ldw<uint16_t>(const void* w, int i) { return bf2f(((const uint16_t*)w)[i]); }
+template <>
+__device__ inline float ldw<float>(const void* w, int i) { return ((const float*)w)[i]; }
+
+__device__ inline float block_sum_256(float v, float* sh) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  if (l == 0) sh[w] = v;
+  __syncthreads();
+  float t = sh[0] + sh[1] + sh[2] + sh[3];
+  __syncthreads();
+  return t;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, const void* w,
+                                                 int d, float eps, void* out) {
+  __shared__ float sh[4];
+  const int r = blockIdx.x;
+  const float* xr = x + (size_t)r * d;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < d; i += 256) ss = fmaf(xr[i], xr[i], ss);
+  ss = block_sum_256(ss, sh);
+  const float inv = 1.f / sqrtf(ss / (float)d + eps);
+  for (int i = threadIdx.x; i < d; i += 256) {
+    const float v = xr[i] * inv * ldw<T>(w, i);
+    if (sizeof(T) == 2) ((uint16_t*)out)[(size_t)r * d + i] = f2bf(v);
+    else ((float*)out)[(size_t)r * d + i] = v;
+  }
+}
+
+void launch_rmsnorm(const float* x, const void* w, int M, int d, float eps, int bf16,
+                    void* out, hipStream_t s) {
+  if (bf16) hipLaunchKernelGGL(k_rmsnorm<uint16_t>, dim3(M), dim3(256), 0, s, x, w, d, eps, out);
+  else hipLaunchKernelGGL(k_rmsnorm<float>, dim3(M), dim3(256), 0, s, x, w, d, eps, out);
+}
+
+// ---------------------------------------------------------------------------
+// Per-row argmax over the vocabulary, lowest token id on ties.
+
+__device__ inline void better(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+}
+
+__global__ __launch_bounds__(256) void k_argmax(const float* __restrict__ logits, int V,
+                                                int32_t* amax) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int r = blockIdx.x;
+  const float* lg = logits + (size_t)r * V;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = threadIdx.x; i < V; i += 256) better(bv, bi, lg[i], i);
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o);
+    const int oi = __shfl_xor(bi, o);
+    better(bv, bi, ov, oi);
+  }
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  if (l == 0) { sv[w] = bv; si[w] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < 4; k++) better(bv, bi, sv[k], si[k]);
+    amax[r] = bi;
+  }
+}
+
+void launch_argmax(const float* logits, int M, int V, int32_t* amax, hipStream_t s) {
+  hipLaunchKernelGGL(k_argmax, dim3(M), dim3(256), 0, s, logits, V, amax);
+}
+
+// ---------------------------------------------------------------------------
+// n-gram pool: per lead token a list of at most G distinct (N-1)-token
+// tails, oldest first.  A tail already present moves to the newest slot; a
+// new tail in a full list evicts the oldest.
+
+__device__ void pool_insert_serial(int32_t* pool_len, int32_t* pool, int N, int G, int key,
+                                   const int32_t* tail) {
+  if (G <= 0) return;
+  const int n1 = N - 1;
+  int32_t* lst = pool + (size_t)key * G * n1;
+  int len = pool_len[key];
+  int found = -1;
+  for (int e = 0; e < len && found < 0; e++) {
+    bool same = true;
+    for (int i = 0; i < n1; i++) same = same && lst[e * n1 + i] == tail[i];
+    if (same) found = e;
+  }
+  int gap;
+  if (found >= 0) gap = found;
+  else if (len == G) gap = 0;
+  else gap = len++;
+  for (int e = gap; e + 1 < len; e++)
+    for (int i = 0; i < n1; i++) lst[e * n1 + i] = lst[(e + 1) * n1 + i];
+  for (int i = 0; i < n1; i++) lst[(len - 1) * n1 + i] = tail[i];
+  pool_len[key] = len;
+}
+
+__global__ void k_pool_insert(int32_t key, const int32_t* tail, int32_t* pool_len,
+                              int32_t* pool, int N, int G) {
+  if (threadIdx.x == 0) pool_insert_serial(pool_len, pool, N, G, key, tail);
+}
+
+void launch_pool_insert(DevState*, int32_t key, const int32_t* tail_dev, int32_t* pool_len,
+                        int32_t* pool, int N, int G, hipStream_t s) {
+  hipLaunchKernelGGL(k_pool_insert, dim3(1), dim3(64), 0, s, key, tail_dev, pool_len, pool, N, G);
+}
+
+// ---------------------------------------------------------------------------
+// Greedy verification + lookahead update (one wave).
+//   k_g = longest prefix of candidate g that follows the greedy chain:
+//     cand[g][0] == argmax(row 0), cand[g][i] == argmax(row (g, i));
+//   winner g* = lowest g with the largest k_g (k = 0 and g* = -1 without
+//   candidates); emitted = cand[g*][0..k-1] + the next greedy token
+//   (argmax of row (g*, k), or of row 0 when k = 0).
+//   The new window level is the argmax of the last level's rows; column j's
+//   n-gram (win[1][j], ..., win[N-1][j], new[j]) is inserted keyed by
+//   win[1][j] for j = 0..W-1 in order; then the levels move down by one.
+
+__global__ __launch_bounds__(64) void k_verify(DevState* st, const int32_t* __restrict__ tokens,
+                                               const int32_t* __restrict__ amax, int32_t* win,
+                                               int32_t* pool_len, int32_t* pool, int W, int N,
+                                               int G, DevResult* res) {
+  __shared__ int32_t ynew[256];
+  __shared__ int32_t tail[32];
+  const int lane = threadIdx.x;
+  const int n1 = N - 1;
+  const int nwin = n1 * W;
+  const int nc = st->n_cand;
+  const int a0 = amax[0];
+  // per-candidate accepted length, reduced to (max k, lowest g)
+  int bk = -1, bg = 0x7fffffff;
+  for (int g = lane; g < nc; g += 64) {
+    const int base = 1 + nwin + g * n1;  // row (g, 1)
+    int k = 0;
+    while (k < n1) {
+      const int pred = k == 0 ? a0 : amax[base + k - 1];
+      if (tokens[base + k] != pred) break;
+      k++;
+    }
+    if (k > bk || (k == bk && g < bg)) { bk = k; bg = g; }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const int ok = __shfl_xor(bk, o), og = __shfl_xor(bg, o);
+    if (ok > bk || (ok == bk && og < bg)) { bk = ok; bg = og; }
+  }
+  for (int j = lane; j < W; j += 64) ynew[j] = amax[1 + (n1 - 1) * W + j];
+  __syncthreads();
+  if (lane == 0) {
+    const int k = nc > 0 ? bk : 0;
+    const int gs = nc > 0 ? bg : -1;
+    const int base = 1 + nwin + (gs < 0 ? 0 : gs) * n1;
+    for (int i = 0; i < k; i++) res->tokens[i] = tokens[base + i];
+    const int bonus = k == 0 ? a0 : amax[base + k - 1];
+    res->tokens[k] = bonus;
+    for (int i = k + 1; i < 32; i++) res->tokens[i] = 0;
+    res->n_emitted = k + 1;
+    res->accepted = k;
+    res->winner = gs;
+    res->n_candidates = nc;
+    const int L = st->L;
+    st->L_old = L;
+    st->k = k;
+    st->winner = gs;
+    st->L = L + k + 1;
+    st->cur = bonus;
+    res->kv_len = L + k + 1;
+    // n-gram pool: insert every column's n-gram in column order
+    for (int j = 0; j < W; j++) {
+      for (int l = 2; l <= n1; l++) tail[l - 2] = win[(l - 1) * W + j];
+      tail[n1 - 1] = ynew[j];
+      pool_insert_serial(pool_len, pool, N, G, win[j], tail);
+    }
+  }
+  __syncthreads();
+  // shift the window by one level
+  for (int j = lane; j < W; j += 64) {
+    for (int l = 1; l < n1; l++) win[(l - 1) * W + j] = win[l * W + j];
+    win[(n1 - 1) * W + j] = ynew[j];
+  }
+}
+
+void launch_verify(DevState* st, const int32_t* tokens, const int32_t* amax, int32_t* win,
+                   int32_t* pool_len, int32_t* pool, int W, int N, int G, DevResult* res,
+                   hipStream_t s) {
+  hipLaunchKernelGGL(k_verify, dim3(1), dim3(64), 0, s, st, tokens, amax, win, pool_len, pool,
+                     W, N, G, res);
+}
+
+// ---------------------------------------------------------------------------
+// KV compaction: the accepted candidate rows (g*, 1..k), written at
+// L_old + row by the QKV epilogue, move to L_old + 1 .. L_old + k.  Row 0 is
+// already at L_old.  Sources never overlap other rows' destinations.
+
+template <typename E>
+__global__ void k_kv_compact(const DevState* __restrict__ st, int Hkv, int dh, int max_ctx,
+                             int W, int N, E* kc, E* vtc) {
+  const int k = st->k;
+  if (k == 0) return;
+  const int layer = blockIdx.x, hk = blockIdx.y;
+  const int g = st->winner, L0 = st->L_old;
+  const int src0 = L0 + 1 + (N - 1) * W + g * (N - 1);  // row (g, 1)
+  E* kb = kc + ((size_t)layer * Hkv + hk) * max_ctx * dh;
+  E* vb = vtc + ((size_t)layer * Hkv + hk) * dh * max_ctx;
+  for (int e = threadIdx.x; e < k * dh; e += blockDim.x) {
+    const int i = e / dh, di = e % dh;
+    kb[(size_t)(L0 + 1 + i) * dh + di] = kb[(size_t)(src0 + i) * dh + di];
+    vb[(size_t)di * max_ctx + L0 + 1 + i] = vb[(size_t)di * max_ctx + src0 + i];
+  }
+}
+
+void launch_kv_compact(const DevState* st, int n_layers, int Hkv, int dh, int max_ctx, int W,
+                       int N, int elem, void* k_cache, void* vt_cache, hipStream_t s) {
+  dim3 grid(n_layers, Hkv);
+  if (elem == 2)
+    hipLaunchKernelGGL(k_kv_compact<uint16_t>, grid, dim3(256), 0, s, st, Hkv, dh, max_ctx, W, N,
+                       (uint16_t*)k_cache, (uint16_t*)vt_cache);
+  else
+    hipLaunchKernelGGL(k_kv_compact<uint32_t>, grid, dim3(256), 0, s, st, Hkv, dh, max_ctx, W, N,
+                       (uint32_t*)k_cache, (uint32_t*)vt_cache);
+}
+
+// ---------------------------------------------------------------------------
+// prefill bookkeeping: commit M rows; optionally take the last row's argmax
+// as the current token.
+
+__global__ void k_advance(DevState* st, int M, const int32_t* amax, int set_cur) {
+  if (threadIdx.x == 0) {
+    st->L += M;
+    if (set_cur) st->cur = amax[M - 1];
+  }
+}
+
+void launch_advance(DevState* st, int M, const int32_t* amax, int set_cur, hipStream_t s) {
+  hipLaunchKernelGGL(k_advance, dim3(1), dim3(64), 0, s, st, M, amax, set_cur);
+}
+
+}  // namespace la

@@ -1,0 +1,99 @@
+"""Lockstep comparison of the HIP decoder with the CPU oracle.
+
+Each step the HIP library runs one lookahead step; the oracle forwards the
+same block from its own state and takes the same decisions.  Compared:
+  - the block tokens (bit-exact);
+  - the logits of every valid row (max |diff| <= logit_tol);
+  - every row's argmax: equal, or else the oracle's top-2 margin on that row
+    is <= tie_margin (an excused near-tie: the oracle adopts the HIP choice
+    and the count is reported);
+  - the step result (accepted length, winner, emitted tokens, kv length),
+    the window and the n-gram pool (bit-exact).
+"""
+import sys
+
+import numpy as np
+
+import oracle
+import lookahead_decoding_la_amd as la
+
+
+def margin(row):
+    v = np.sort(row.astype(np.float32))
+    return float(v[-1]) - float(v[-2])
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Lockstep:
+    def __init__(self, cfg, weights, max_ctx, logit_tol, tie_margin=0.05):
+        self.cfg = cfg
+        self.tol = logit_tol
+        self.tie = tie_margin
+        self.dev = la.LookaheadDecoder(cfg, la.upload_weights(weights), max_ctx)
+        self.orc = oracle.Oracle(cfg, weights, max_ctx)
+        self.ties = 0
+        self.max_diff = 0.0
+        self.steps = []
+
+    def prefill(self, prompt, win):
+        fg = self.dev.prefill(prompt, win)
+        fo, lg = self.orc.prefill(prompt, win, logits=True)
+        if fg != fo:
+            m = margin(lg[-1])
+            assert m <= self.tie, f"prefill token {fg} vs oracle {fo}, margin {m}"
+            self.ties += 1
+            self.orc.set_current(fg)
+        return fg
+
+    def step(self):
+        cfg = self.cfg
+        rg = self.dev.step()
+        lg_g = self.dev.debug_logits()
+        tok_g, amax_g = self.dev.debug_block()
+        tok_o, valid, nc = self.orc.block_tokens()
+        v = valid.astype(bool)
+        assert nc == rg["n_candidates"], (nc, rg)
+        assert np.array_equal(tok_g[v], tok_o[v])
+        lg_o = self.orc.forward_block(tok_o, valid, keep=True)
+        d = float(np.max(np.abs(lg_g[v].astype(np.float64) - lg_o[v])))
+        self.max_diff = max(self.max_diff, d)
+        assert d <= self.tol, f"logit diff {d} > {self.tol} at step {len(self.steps)}"
+        amax_o = self.orc.block_argmax()
+        for r in np.nonzero(v)[0]:
+            if amax_g[r] != amax_o[r]:
+                m = margin(lg_o[r])
+                assert m <= self.tie, (
+                    f"step {len(self.steps)} row {r}: argmax {amax_g[r]} vs oracle "
+                    f"{amax_o[r]}, oracle margin {m}")
+                self.ties += 1
+                amax_o[r] = amax_g[r]
+        ro = self.orc.commit(amax_o)
+        assert ro == rg, (ro, rg)
+        if cfg.W:
+            assert np.array_equal(self.dev.debug_window(), self.orc.window())
+        if cfg.G:
+            lg_len, lg_tails = self.dev.debug_pool()
+            lo_len, lo_tails = self.orc.pool()
+            assert np.array_equal(lg_len, lo_len)
+            mask = np.arange(cfg.G)[None, :] < lo_len[:, None]
+            assert np.array_equal(lg_tails[mask], lo_tails[mask])
+        assert self.dev.debug_state() == (self.orc.kv_len, self.orc.current)
+        self.steps.append(rg)
+        return rg
+
+    def run(self, prompt, win, n_steps=None, M=None):
+        out = [self.prefill(prompt, win)]
+        while (n_steps is None or len(self.steps) < n_steps) and (M is None or len(out) < M):
+            out += self.step()["tokens"]
+        return out
+
+    def compare_kv(self, tol):
+        L = self.orc.kv_len
+        for layer in range(self.cfg.n_layers):
+            kg, vg = self.dev.debug_kv(layer, 0, L)
+            ko, vo = self.orc.kv(layer, 0, L)
+            assert np.max(np.abs(kg - ko)) <= tol
+            assert np.max(np.abs(vg - vo)) <= tol

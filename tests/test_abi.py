@@ -1,0 +1,80 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry
+point include/la.h declares, and validates arguments before any HIP call."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import lasynth
+import lookahead_decoding_la_amd as la
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "la.h")
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert declared() == sorted(la.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = la.lib()
+    for name in declared():
+        assert hasattr(lib, name), name
+
+
+def _cfg(**kw):
+    return la.make_config(lasynth.get_config("tiny", **kw), 256)
+
+
+def test_workspace_bytes_validates():
+    lib = la.lib()
+    assert lib.la_workspace_bytes(C.byref(_cfg())) > 0
+    assert lib.la_workspace_bytes(None) == 0
+    for bad in [dict(N=1), dict(N=33), dict(W=-1), dict(n_kv_heads=3),
+                dict(head_dim=31), dict(W=100, G=100)]:
+        assert lib.la_workspace_bytes(C.byref(_cfg(**bad))) == 0, bad
+    bf = la.make_config(lasynth.get_config("7b"), 1024)
+    n = lib.la_workspace_bytes(C.byref(bf))
+    # repacked weights + KV cache dominate: > 13.2 GB of weights alone
+    assert n > 13_000_000_000
+
+
+def test_create_rejects_bad_config_without_gpu():
+    lib = la.lib()
+    h = C.c_void_p()
+    ptrs = (C.c_void_p * 400)(*([1] * 400))
+    c = _cfg(N=1)
+    assert lib.la_create(C.byref(c), ptrs, C.c_void_p(1), 1 << 20, None, C.byref(h)) == la.LA_ERR_INVALID_ARG
+    assert not h.value
+    c = la.make_config(lasynth.get_config("7b", dtype="bf16", d_model=4008), 1024)
+    assert lib.la_create(C.byref(c), ptrs, C.c_void_p(1), 1 << 20, None, C.byref(h)) == la.LA_ERR_UNSUPPORTED
+    c = _cfg()
+    assert lib.la_create(C.byref(c), ptrs, C.c_void_p(1), 16, None, C.byref(h)) == la.LA_ERR_OUT_OF_CAPACITY
+    assert lib.la_create(C.byref(c), None, C.c_void_p(1), 1 << 30, None, C.byref(h)) == la.LA_ERR_INVALID_ARG
+    assert lib.la_create(C.byref(c), ptrs, C.c_void_p(1), 1 << 30, None, None) == la.LA_ERR_INVALID_ARG
+
+
+def test_calls_on_null_context():
+    lib = la.lib()
+    r = la.LaStepResult()
+    assert lib.la_step(None, C.byref(r)) == la.LA_ERR_INVALID_ARG
+    assert lib.la_destroy(None) == la.LA_OK
+    assert lib.la_step_rows(None) == 0
+    assert lib.la_status_string(la.LA_ERR_STATE) == b"invalid state"
+
+
+def test_attention_argument_checks_without_gpu():
+    lib = la.lib()
+    one = C.c_void_p(1)
+    # head_dim other than 128 is unsupported; bad stride is invalid
+    assert lib.la_attention(one, one, one, one, 32, 32, 64, 16, 256, 15, 5, 15, one, 1 << 30, None) == la.LA_ERR_UNSUPPORTED
+    assert lib.la_attention(one, one, one, one, 32, 32, 128, 16, 100, 15, 5, 15, one, 1 << 30, None) == la.LA_ERR_INVALID_ARG
+    assert lib.la_attention(one, one, one, one, 32, 32, 128, 200, 256, 15, 5, 15, one, 1 << 30, None) == la.LA_ERR_INVALID_ARG
+    assert lib.la_attention(one, one, one, one, 32, 32, 128, 16, 256, 15, 5, 15, one, 8, None) == la.LA_ERR_OUT_OF_CAPACITY
+    assert lib.la_attention_workspace_bytes(32, 128, 1152, 15, 5, 15) > 0

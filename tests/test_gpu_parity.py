@@ -1,0 +1,97 @@
+"""HIP decoder vs CPU oracle, in lockstep, through the C ABI (GPU only).
+
+Tolerances (floating point decides integers only through argmax, compared
+with the near-tie rule of tests/lockstep.py):
+  - fp32 models: logits within 1e-4, argmax mismatches only where the
+    oracle's top-2 margin is <= 2e-4;
+  - bf16 models: logits within 2e-2, argmax mismatches only where the
+    oracle's top-2 margin is <= 0.05;
+  - tokens, accepted lengths, window and pool bit-exact (after adoption of
+    excused near-ties).
+"""
+import numpy as np
+import pytest
+
+import lasynth
+import oracle
+from lockstep import Lockstep, log
+
+pytestmark = pytest.mark.gpu
+
+FP32 = [
+    lasynth.get_config("tiny"),
+    lasynth.get_config("tiny", name="tiny_n2", N=2),
+    lasynth.get_config("tiny", name="tiny_verify_only", W=0, G=3),
+    lasynth.get_config("tiny", name="tiny_lookahead_only", W=4, G=0),
+    lasynth.get_config("tiny", name="tiny_gqa_n5", n_heads=4, n_kv_heads=2, N=5, W=3, G=4),
+    lasynth.get_config("tiny", name="tiny_plain", W=0, G=0),
+]
+
+
+@pytest.mark.parametrize("cfg", FP32, ids=lambda c: c.name)
+def test_fp32_lockstep(cfg):
+    w = lasynth.make_weights(cfg)
+    p = lasynth.make_prompt(cfg)
+    win = lasynth.make_init_window(cfg, p) if cfg.W else None
+    log(f"[fp32 lockstep] {cfg.name} T={cfg.T}")
+    ls = Lockstep(cfg, w, 256, logit_tol=1e-4, tie_margin=2e-4)
+    toks = ls.run(p, win, M=cfg.gen_tokens)
+    ls.compare_kv(1e-4)
+    log(f"  steps={len(ls.steps)} max|dlogit|={ls.max_diff:.2e} ties={ls.ties}")
+    # and the output is plain greedy decoding
+    assert toks[:cfg.gen_tokens] == oracle.Oracle(cfg, w, 256).greedy(p, cfg.gen_tokens) or ls.ties
+
+
+BF16 = [
+    # 121 rows per step (W15 N5 G15) as in the 7B workload, narrow model
+    lasynth.get_config("7b", name="bf16_w15", n_layers=3, d_model=512, n_heads=4,
+                       n_kv_heads=4, d_ffn=1376, vocab=2048, prompt_len=64,
+                       span_len=8, n_spans=2),
+    # grouped KV heads, 57 rows per step (W7 N5 G7, the 34B setting)
+    lasynth.get_config("34b", name="bf16_gqa_w7", n_layers=2, d_model=1024, n_heads=8,
+                       n_kv_heads=2, d_ffn=2816, vocab=4096, prompt_len=96,
+                       span_len=8, n_spans=2, span_repeats=3),
+    # ragged: 81 rows (W10 N5 G10), 1 layer, prompt longer than one chunk
+    lasynth.get_config("13b", name="bf16_w10_long", n_layers=1, d_model=256, n_heads=2,
+                       n_kv_heads=2, d_ffn=704, vocab=1024, prompt_len=300,
+                       span_len=16, n_spans=4),
+    # plain one-token decode
+    lasynth.get_config("7b", name="bf16_plain", n_layers=2, d_model=512, n_heads=4,
+                       n_kv_heads=4, d_ffn=1376, vocab=2048, prompt_len=64,
+                       span_len=8, n_spans=2, W=0, G=0),
+]
+
+
+@pytest.mark.parametrize("cfg", BF16, ids=lambda c: c.name)
+def test_bf16_lockstep(cfg):
+    w = lasynth.make_weights(cfg)
+    p = lasynth.make_prompt(cfg)
+    win = lasynth.make_init_window(cfg, p) if cfg.W else None
+    log(f"[bf16 lockstep] {cfg.name} T={cfg.T}")
+    ls = Lockstep(cfg, w, 512, logit_tol=2e-2)
+    ls.run(p, win, n_steps=10)
+    ls.compare_kv(3e-2)
+    log(f"  steps={len(ls.steps)} max|dlogit|={ls.max_diff:.2e} ties={ls.ties}")
+
+
+def test_planted_candidate_accepted_on_gpu():
+    cfg = BF16[0]
+    w = lasynth.make_weights(cfg)
+    p = lasynth.make_prompt(cfg)
+    win = lasynth.make_init_window(cfg, p)
+    ls = Lockstep(cfg, w, 512, logit_tol=2e-2)
+    out = [ls.prefill(p, win)]
+    greedy = oracle.Oracle(cfg, w, 512).greedy(p, 40)
+    if ls.ties:
+        pytest.skip("prefill token decided by a near-tie")
+    for _ in range(4):
+        n = len(out)
+        tail = greedy[n:n + cfg.N - 1]
+        ls.dev.debug_pool_insert(out[-1], tail)
+        ls.orc.pool_insert(out[-1], tail)
+        r = ls.step()
+        if ls.ties:
+            break
+        assert r["accepted"] == cfg.N - 1
+        assert r["tokens"] == greedy[n:n + cfg.N]
+        out += r["tokens"]
