@@ -84,7 +84,7 @@ def cpu_baseline(cfg, prompt, win, tokens_per_step):
     times = {}
     for nl in (1, 2):
         c = cfg.with_(n_layers=nl)
-        w = lasynth.make_weights(c, seed=0)
+        w = lasynth.host_bits(lasynth.make_weights_device(c, seed=0))
         o = oracle.Oracle(c, w, P + 2 * c.T + 8)
         o.prefill(prompt[:P], win)
         rng = np.random.default_rng(0)
@@ -132,14 +132,13 @@ def main():
     import lasynth
 
     cfg = lasynth.get_config(args.config)
-    log(f"config {cfg.name}: T={cfg.T}, generating weights")
+    log(f"config {cfg.name}: T={cfg.T}, drawing weights on the GPU")
     t0 = time.time()
-    weights = lasynth.make_weights(cfg)
+    dev_w = lasynth.make_weights_device(cfg, seed=0)
     prompt = lasynth.make_prompt(cfg)
     win = lasynth.make_init_window(cfg, prompt)
-    log(f"weights ready in {time.time() - t0:.1f} s; uploading")
-    dev_w = la.upload_weights(weights)
     torch.cuda.synchronize()
+    log(f"weights ready in {time.time() - t0:.1f} s")
     n_prof = 3
     total = args.warmup + args.steps + n_prof
     max_ctx = cfg.prompt_len + (total + 2) * cfg.N + cfg.T + 64

@@ -135,13 +135,14 @@ int32_t la_step_rows(const la_ctx *c);
  * class k and launches[k] (host int32) the number of launches.  The event
  * pairs add small gaps, so the step itself runs slower than la_step. */
 enum {
-  LA_PROF_QKV = 0,    /* fused RMSNorm'd QKV projection + RoPE + KV write */
+  LA_PROF_QKV = 0,    /* fused QKV projection */
   LA_PROF_ATTN = 1,   /* masked attention (+ split merge) */
-  LA_PROF_O = 2,      /* output projection + residual */
-  LA_PROF_GATEUP = 3, /* fused gate/up projection + SwiGLU */
-  LA_PROF_DOWN = 4,   /* down projection + residual */
+  LA_PROF_O = 2,      /* output projection */
+  LA_PROF_GATEUP = 3, /* fused gate/up projection */
+  LA_PROF_DOWN = 4,   /* down projection */
   LA_PROF_LMHEAD = 5, /* LM head (logits) */
-  LA_PROF_NORM = 6,   /* RMSNorm kernels */
+  LA_PROF_REDUCE = 6, /* split-K sums with fused epilogues (RoPE + KV write,
+                         residual + RMSNorm, SwiGLU) and RMSNorm kernels */
   LA_PROF_OTHER = 7,  /* assembly, argmax, verification, KV compaction */
   LA_PROF_CLASSES = 8
 };

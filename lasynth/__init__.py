@@ -188,6 +188,47 @@ def make_weights(cfg: ModelConfig, seed: int = 0, threads: int | None = None):
     return out
 
 
+def _tensor_seed(seed: int, tidx: int) -> int:
+    return int(np.random.SeedSequence(seed, spawn_key=(0, tidx, 1 << 20))
+               .generate_state(1, dtype=np.uint64)[0] & ((1 << 63) - 1))
+
+
+def make_weights_device(cfg: ModelConfig, seed: int = 0, device="cuda"):
+    """Random-init weights drawn on the GPU with torch's seeded generator
+    (for the multi-billion-parameter workloads, where host generation is too
+    slow).  Same recipe as make_weights -- N(0, 0.02) in fp32, rounded to
+    bf16 (torch's float->bfloat16 conversion rounds to nearest even), norm
+    weights 1.0 -- but a different random stream: tensor i is drawn from its
+    own generator seeded from SeedSequence(seed, spawn_key=(0, i, 2**20)).
+    Returns torch tensors (bfloat16 or float32) in weight_shapes order; the
+    oracle side takes host copies of these same tensors (host_bits)."""
+    import torch
+    out = []
+    for ti, (name, shape) in enumerate(weight_shapes(cfg)):
+        if name.endswith("norm"):
+            t = torch.ones(shape, dtype=torch.float32, device=device)
+        else:
+            g = torch.Generator(device=device)
+            g.manual_seed(_tensor_seed(seed, ti))
+            t = torch.randn(shape, generator=g, dtype=torch.float32, device=device)
+            t.mul_(0.02)
+        out.append(t.to(torch.bfloat16) if cfg.dtype == "bf16" else t)
+    return out
+
+
+def host_bits(tensors):
+    """Host numpy copies of device weight tensors: bfloat16 as uint16 bit
+    patterns, float32 as float32 (the layout make_weights returns)."""
+    import torch
+    out = []
+    for t in tensors:
+        if t.dtype == torch.bfloat16:
+            out.append(t.view(torch.int16).cpu().numpy().view(np.uint16))
+        else:
+            out.append(t.cpu().numpy())
+    return out
+
+
 # ----------------------------------------------------------------------------
 # prompts and windows
 # ----------------------------------------------------------------------------

@@ -32,7 +32,7 @@ EXPORTS = [
 ]
 
 PROF_CLASSES = ["qkv", "attention", "o_proj", "gate_up", "down", "lm_head",
-                "rmsnorm", "other"]
+                "reduce", "other"]
 
 
 class LaConfig(C.Structure):

@@ -84,16 +84,19 @@ struct la_ctx {
   DevResult* res_dev = nullptr;
   float *x = nullptr, *logits = nullptr, *rope_cos = nullptr, *rope_sin = nullptr;
   float *gpart = nullptr, *attn_po = nullptr, *attn_pml = nullptr;
-  void *xn = nullptr, *ffa = nullptr, *qb = nullptr;
+  void *xn = nullptr, *ffa = nullptr, *qb = nullptr;  // f32 path: row-major
+  uint16_t *xnf = nullptr, *of = nullptr, *af = nullptr;  // bf16: fragment layout
+  int MTT = 0;
   int32_t *tokens = nullptr, *relpos = nullptr, *amax = nullptr, *prompt_buf = nullptr;
-  int32_t *win = nullptr, *pool_len = nullptr, *pool = nullptr, *counters = nullptr;
+  int32_t *win = nullptr, *pool_len = nullptr, *pool = nullptr;
   int32_t* tail_buf = nullptr;
   void *kcache = nullptr, *vtcache = nullptr;
   size_t kv_layer_elems = 0;  // elements of one layer's K (or V^T) cache
   // weights
   const void *emb = nullptr, *final_norm = nullptr, *lm = nullptr;
   std::vector<Layer> layers;
-  int ks_qkv = 1, ks_o = 1, ks_gu = 1, ks_d = 1, ks_lm = 1, attn_splits = 1;
+  GemmPlan p_qkv{1, 1}, p_o{1, 1}, p_gu{1, 1}, p_d{1, 1}, p_lm{1, 1};
+  int attn_splits = 1;
   // host
   DevResult* res_host = nullptr;  // pinned
   int32_t* pin = nullptr;         // pinned staging
@@ -139,8 +142,8 @@ la_status check_config(const la_config* cfg, std::string* why) {
   if (c.head_dim % 2) return bad("head_dim must be even");
   if (c.dtype == LA_BF16) {
     if (c.head_dim != 128) return uns("bf16 kernels need head_dim 128");
-    if (c.d_model % 32 || c.d_ffn % 32 || c.vocab % 32)
-      return uns("bf16 kernels need d_model, d_ffn and vocab multiples of 32");
+    if (c.d_model % 128 || c.d_ffn % 64 || c.vocab % 128)
+      return uns("bf16 kernels need d_model and vocab multiples of 128, d_ffn of 64");
   } else {
     if (c.head_dim > 256) return uns("f32 kernels need head_dim <= 256");
     if (c.d_model % 2 || c.d_ffn % 2 || c.vocab % 2) return uns("f32 kernels need even sizes");
@@ -166,36 +169,35 @@ size_t carve(la_ctx* c, void* base) {
   c->pool = cv.take<int32_t>((size_t)V * std::max(1, g.G) * (g.N - 1));
   c->x = cv.take<float>((size_t)c->MR * d);
   c->logits = cv.take<float>((size_t)c->MR * V);
-  c->xn = cv.take<char>((size_t)c->MR * std::max(d, c->qdim) * c->elem);
-  c->ffa = cv.take<char>((size_t)c->MR * F * c->elem);
-  c->qb = cv.take<char>((size_t)c->MR * c->qdim * c->elem);
   c->rope_cos = cv.take<float>((size_t)c->ctx_stride * (dh / 2));
   c->rope_sin = cv.take<float>((size_t)c->ctx_stride * (dh / 2));
   c->kv_layer_elems = (size_t)g.n_kv_heads * c->ctx_stride * dh;
   c->kcache = cv.take<char>(c->kv_layer_elems * g.n_layers * c->elem);
   c->vtcache = cv.take<char>(c->kv_layer_elems * g.n_layers * c->elem);
+  c->qb = cv.take<char>((size_t)c->MR * c->qdim * c->elem);
   if (c->bf16) {
-    c->ks_qkv = gemm_bf16_ksplit(c->qkv_rows, d);
-    c->ks_o = gemm_bf16_ksplit(d, c->qdim);
-    c->ks_gu = gemm_bf16_ksplit(2 * F, d);
-    c->ks_d = gemm_bf16_ksplit(d, F);
-    c->ks_lm = gemm_bf16_ksplit(V, d);
+    c->MTT = c->MR / 16;
+    c->xnf = cv.take<uint16_t>((size_t)c->MR * d);
+    c->of = cv.take<uint16_t>((size_t)c->MR * c->qdim);
+    c->af = cv.take<uint16_t>((size_t)c->MR * F);
+    c->p_qkv = gemm_bf16_plan(c->qkv_rows, d);
+    c->p_o = gemm_bf16_plan(d, c->qdim);
+    c->p_gu = gemm_bf16_plan(2 * F, d);
+    c->p_d = gemm_bf16_plan(d, F);
+    c->p_lm = GemmPlan{1, (d / 32) % 2 == 0 ? 2 : 1};
     size_t gp = 0;
-    gp = std::max(gp, gemm_bf16_partial_floats(c->qkv_rows, c->MR, c->ks_qkv));
-    gp = std::max(gp, gemm_bf16_partial_floats(d, c->MR, c->ks_o));
-    gp = std::max(gp, gemm_bf16_partial_floats(2 * F, c->MR, c->ks_gu));
-    gp = std::max(gp, gemm_bf16_partial_floats(d, c->MR, c->ks_d));
-    gp = std::max(gp, gemm_bf16_partial_floats(V, c->MR, c->ks_lm));
-    c->gpart = cv.take<float>(std::max<size_t>(gp, 1));
-    int tiles = std::max(std::max(gemm_bf16_tiles(c->qkv_rows), gemm_bf16_tiles(2 * F)),
-                         std::max(gemm_bf16_tiles(d), gemm_bf16_tiles(V)));
-    c->counters = cv.take<int32_t>(tiles);
+    gp = std::max(gp, (size_t)c->p_qkv.ksplit * c->MR * c->qkv_rows);
+    gp = std::max(gp, (size_t)c->p_o.ksplit * c->MR * d);
+    gp = std::max(gp, (size_t)c->p_gu.ksplit * c->MR * 2 * F);
+    gp = std::max(gp, (size_t)c->p_d.ksplit * c->MR * d);
+    c->gpart = cv.take<float>(gp);
     c->attn_splits = attn_bf16_splits(g.n_heads, c->T, c->ctx_stride);
-    size_t ap = attn_bf16_partial_floats(g.n_heads, c->MR, c->attn_splits, dh);
     size_t rows16 = (size_t)g.n_heads * c->attn_splits * c->MR;
     c->attn_po = cv.take<float>(rows16 * dh);
     c->attn_pml = cv.take<float>(rows16 * 2);
-    (void)ap;
+  } else {
+    c->xn = cv.take<char>((size_t)c->MR * std::max(d, c->qdim) * c->elem);
+    c->ffa = cv.take<char>((size_t)c->MR * F * c->elem);
   }
   // weights owned by the workspace
   c->layers.assign(g.n_layers, Layer{});
@@ -242,16 +244,32 @@ EpiArgs base_epi(la_ctx* c, int M) {
   return ea;
 }
 
-void gemm(la_ctx* c, int epi, const void* X, const void* W, const void* W2, int K, int N,
-          int M, int ks, const EpiArgs& ea, hipStream_t s) {
-  if (c->bf16)
-    launch_gemm_bf16(epi, (const uint16_t*)X, (const uint16_t*)W, K, N, M, ks, c->gpart,
-                     c->counters, ea, s);
-  else
-    launch_gemm_f32(epi, (const float*)X, (const float*)W, (const float*)W2, K, N, M, ea, s);
+AttnArgs attn_args(la_ctx* c, int l, int M, int mode) {
+  const la_config& g = c->cfg;
+  AttnArgs aa;
+  memset(&aa, 0, sizeof(aa));
+  aa.q = c->qb;
+  aa.k_cache = layer_k(c, l);
+  aa.vt_cache = layer_v(c, l);
+  aa.out = c->bf16 ? (void*)c->of : c->xn;
+  aa.out_mtt = c->bf16 ? c->MTT : 0;
+  aa.st = c->st;
+  aa.M = M;
+  aa.mode = mode;
+  aa.H = g.n_heads;
+  aa.Hkv = g.n_kv_heads;
+  aa.dh = g.head_dim;
+  aa.ctx_stride = c->ctx_stride;
+  aa.W = g.W;
+  aa.N = g.N;
+  aa.part_o = c->attn_po;
+  aa.part_ml = c->attn_pml;
+  aa.splits = c->attn_splits;
+  return aa;
 }
 
-// The decoder over the assembled rows (x holds their embeddings).
+// The decoder over the assembled rows.  bf16: x holds their embeddings and
+// xnf the first layer's normalized input; f32: x only.
 void enqueue_layers(la_ctx* c, int M, int mode, hipStream_t s, Prof* pf = nullptr) {
 #define P_BEGIN(k) if (pf) pf->begin(k)
 #define P_END() if (pf) pf->end()
@@ -259,74 +277,102 @@ void enqueue_layers(la_ctx* c, int M, int mode, hipStream_t s, Prof* pf = nullpt
   const int d = g.d_model, F = g.d_ffn;
   for (int l = 0; l < g.n_layers; l++) {
     const Layer& L = c->layers[l];
-    P_BEGIN(LA_PROF_NORM);
-    launch_rmsnorm(c->x, L.anorm, M, d, g.rms_eps, c->bf16, c->xn, s);
-    P_END();
     EpiArgs ea = base_epi(c, M);
     ea.out_act = c->qb;
     ea.k_cache = layer_k(c, l);
     ea.vt_cache = layer_v(c, l);
-    P_BEGIN(LA_PROF_QKV);
-    gemm(c, EPI_QKV, c->xn, L.wqkv, nullptr, d, c->qkv_rows, M, c->ks_qkv, ea, s);
-    P_END();
-    AttnArgs aa;
-    memset(&aa, 0, sizeof(aa));
-    aa.q = c->qb;
-    aa.k_cache = layer_k(c, l);
-    aa.vt_cache = layer_v(c, l);
-    aa.out = c->xn;
-    aa.st = c->st;
-    aa.M = M;
-    aa.mode = mode;
-    aa.H = g.n_heads;
-    aa.Hkv = g.n_kv_heads;
-    aa.dh = g.head_dim;
-    aa.ctx_stride = c->ctx_stride;
-    aa.W = g.W;
-    aa.N = g.N;
-    aa.part_o = c->attn_po;
-    aa.part_ml = c->attn_pml;
-    aa.splits = c->attn_splits;
-    P_BEGIN(LA_PROF_ATTN);
-    if (c->bf16) launch_attn_bf16(aa, s);
-    else launch_attn_f32(aa, s);
-    P_END();
-    ea = base_epi(c, M);
-    ea.out_f32 = c->x;
-    ea.ld_out = d;
-    P_BEGIN(LA_PROF_O);
-    gemm(c, EPI_RESID, c->xn, L.wo, nullptr, c->qdim, d, M, c->ks_o, ea, s);
-    P_END();
-    P_BEGIN(LA_PROF_NORM);
-    launch_rmsnorm(c->x, L.fnorm, M, d, g.rms_eps, c->bf16, c->xn, s);
-    P_END();
-    ea = base_epi(c, M);
-    ea.out_act = c->ffa;
-    ea.ld_out = F;
-    P_BEGIN(LA_PROF_GATEUP);
-    if (c->bf16) gemm(c, EPI_SWIGLU, c->xn, L.wgu, nullptr, d, 2 * F, M, c->ks_gu, ea, s);
-    else gemm(c, EPI_SWIGLU, c->xn, L.wg, L.wu, d, F, M, 1, ea, s);
-    P_END();
-    ea = base_epi(c, M);
-    ea.out_f32 = c->x;
-    ea.ld_out = d;
-    P_BEGIN(LA_PROF_DOWN);
-    gemm(c, EPI_RESID, c->ffa, L.wd, nullptr, F, d, M, c->ks_d, ea, s);
-    P_END();
+    if (c->bf16) {
+      const uint16_t* next_norm =
+          (const uint16_t*)(l + 1 < g.n_layers ? c->layers[l + 1].anorm : c->final_norm);
+      P_BEGIN(LA_PROF_QKV);
+      launch_gemm_bf16(c->xnf, c->MTT, (const uint16_t*)L.wqkv, d, c->qkv_rows, M, c->p_qkv,
+                       c->gpart, s);
+      P_END();
+      P_BEGIN(LA_PROF_REDUCE);
+      launch_red_qkv(c->gpart, c->p_qkv.ksplit, c->qkv_rows, M, ea, s);
+      P_END();
+      P_BEGIN(LA_PROF_ATTN);
+      launch_attn_bf16(attn_args(c, l, M, mode), s);
+      P_END();
+      P_BEGIN(LA_PROF_O);
+      launch_gemm_bf16(c->of, c->MTT, (const uint16_t*)L.wo, c->qdim, d, M, c->p_o, c->gpart, s);
+      P_END();
+      P_BEGIN(LA_PROF_REDUCE);
+      launch_red_resid_norm(c->gpart, c->p_o.ksplit, d, M, c->x, (const uint16_t*)L.fnorm,
+                            g.rms_eps, c->xnf, c->MTT, s);
+      P_END();
+      P_BEGIN(LA_PROF_GATEUP);
+      launch_gemm_bf16(c->xnf, c->MTT, (const uint16_t*)L.wgu, d, 2 * F, M, c->p_gu, c->gpart, s);
+      P_END();
+      P_BEGIN(LA_PROF_REDUCE);
+      launch_red_swiglu(c->gpart, c->p_gu.ksplit, F, M, c->af, c->MTT, s);
+      P_END();
+      P_BEGIN(LA_PROF_DOWN);
+      launch_gemm_bf16(c->af, c->MTT, (const uint16_t*)L.wd, F, d, M, c->p_d, c->gpart, s);
+      P_END();
+      P_BEGIN(LA_PROF_REDUCE);
+      launch_red_resid_norm(c->gpart, c->p_d.ksplit, d, M, c->x, next_norm, g.rms_eps, c->xnf,
+                            c->MTT, s);
+      P_END();
+    } else {
+      P_BEGIN(LA_PROF_REDUCE);
+      launch_rmsnorm(c->x, L.anorm, M, d, g.rms_eps, 0, c->xn, s);
+      P_END();
+      P_BEGIN(LA_PROF_QKV);
+      launch_gemm_f32(EPI_QKV, (const float*)c->xn, (const float*)L.wqkv, nullptr, d,
+                      c->qkv_rows, M, ea, s);
+      P_END();
+      P_BEGIN(LA_PROF_ATTN);
+      launch_attn_f32(attn_args(c, l, M, mode), s);
+      P_END();
+      ea = base_epi(c, M);
+      ea.out_f32 = c->x;
+      ea.ld_out = d;
+      P_BEGIN(LA_PROF_O);
+      launch_gemm_f32(EPI_RESID, (const float*)c->xn, (const float*)L.wo, nullptr, c->qdim, d, M,
+                      ea, s);
+      P_END();
+      P_BEGIN(LA_PROF_REDUCE);
+      launch_rmsnorm(c->x, L.fnorm, M, d, g.rms_eps, 0, c->xn, s);
+      P_END();
+      ea = base_epi(c, M);
+      ea.out_act = c->ffa;
+      ea.ld_out = F;
+      P_BEGIN(LA_PROF_GATEUP);
+      launch_gemm_f32(EPI_SWIGLU, (const float*)c->xn, (const float*)L.wg, (const float*)L.wu, d,
+                      F, M, ea, s);
+      P_END();
+      ea = base_epi(c, M);
+      ea.out_f32 = c->x;
+      ea.ld_out = d;
+      P_BEGIN(LA_PROF_DOWN);
+      launch_gemm_f32(EPI_RESID, (const float*)c->ffa, (const float*)L.wd, nullptr, F, d, M, ea,
+                      s);
+      P_END();
+    }
   }
 }
 
 void enqueue_head(la_ctx* c, int M, hipStream_t s, Prof* pf = nullptr) {
   const la_config& g = c->cfg;
-  P_BEGIN(LA_PROF_NORM);
-  launch_rmsnorm(c->x, c->final_norm, M, g.d_model, g.rms_eps, c->bf16, c->xn, s);
-  P_END();
-  EpiArgs ea = base_epi(c, M);
-  ea.out_f32 = c->logits;
-  ea.ld_out = g.vocab;
-  P_BEGIN(LA_PROF_LMHEAD);
-  gemm(c, EPI_LOGITS, c->xn, c->lm, nullptr, g.d_model, g.vocab, M, c->ks_lm, ea, s);
-  P_END();
+  if (c->bf16) {
+    // xnf already holds the final-norm'd rows
+    P_BEGIN(LA_PROF_LMHEAD);
+    launch_gemm_bf16(c->xnf, c->MTT, (const uint16_t*)c->lm, g.d_model, g.vocab, M, c->p_lm,
+                     c->logits, s);
+    P_END();
+  } else {
+    P_BEGIN(LA_PROF_REDUCE);
+    launch_rmsnorm(c->x, c->final_norm, M, g.d_model, g.rms_eps, 0, c->xn, s);
+    P_END();
+    EpiArgs ea = base_epi(c, M);
+    ea.out_f32 = c->logits;
+    ea.ld_out = g.vocab;
+    P_BEGIN(LA_PROF_LMHEAD);
+    launch_gemm_f32(EPI_LOGITS, (const float*)c->xn, (const float*)c->lm, nullptr, g.d_model,
+                    g.vocab, M, ea, s);
+    P_END();
+  }
   P_BEGIN(LA_PROF_OTHER);
   launch_argmax(c->logits, M, g.vocab, c->amax, s);
   P_END();
@@ -336,7 +382,8 @@ void enqueue_step(la_ctx* c, hipStream_t s, Prof* pf = nullptr) {
   const la_config& g = c->cfg;
   P_BEGIN(LA_PROF_OTHER);
   launch_assemble(MODE_STEP, c->st, c->win, c->pool_len, c->pool, nullptr, c->T, g.W, g.N, g.G,
-                  c->tokens, c->relpos, c->st, c->emb, g.d_model, c->bf16, c->x, s);
+                  c->tokens, c->relpos, c->st, c->emb, g.d_model, c->bf16, c->x,
+                  (const uint16_t*)c->layers[0].anorm, g.rms_eps, c->xnf, c->MTT, s);
   P_END();
   enqueue_layers(c, c->T, MODE_STEP, s, pf);
   enqueue_head(c, c->T, s, pf);
@@ -515,7 +562,8 @@ la_status la_prefill(la_ctx* c, const int32_t* prompt, int32_t n_prompt, const i
     memcpy(c->pin, prompt + p0, sizeof(int32_t) * m);
     LA_HIP(c, hipMemcpyAsync(c->prompt_buf, c->pin, sizeof(int32_t) * m, hipMemcpyHostToDevice, s));
     launch_assemble(MODE_CAUSAL, c->st, c->win, c->pool_len, c->pool, c->prompt_buf, m, g.W, g.N,
-                    g.G, c->tokens, c->relpos, c->st, c->emb, g.d_model, c->bf16, c->x, s);
+                    g.G, c->tokens, c->relpos, c->st, c->emb, g.d_model, c->bf16, c->x,
+                    (const uint16_t*)c->layers[0].anorm, g.rms_eps, c->xnf, c->MTT, s);
     enqueue_layers(c, m, MODE_CAUSAL, s);
     if (last) enqueue_head(c, m, s);
     launch_advance(c->st, m, c->amax, last ? 1 : 0, s);
@@ -726,6 +774,7 @@ la_status la_attention(const void* q, const void* k_cache, const void* vt_cache,
   aa.k_cache = k_cache;
   aa.vt_cache = vt_cache;
   aa.out = out;
+  aa.out_mtt = 0;
   aa.st = nullptr;
   aa.L_host = prefix_len;
   aa.M = (int)T;

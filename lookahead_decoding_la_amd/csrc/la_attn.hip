@@ -17,7 +17,7 @@
 //     layout holds them, V^T is read in the same order);
 //   - splits merge in a second kernel (log-sum-exp weights).
 // The cache stores V transposed ([kv head][dh][position]) for this reason.
-#include "la_internal.h"
+#include "la_epilogue.h"
 
 namespace la {
 
@@ -174,12 +174,16 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
   l_run = wave_sum_groups(l_run);
   if (t >= M) return;
   if (a.splits == 1) {
-    uint16_t* out = (uint16_t*)a.out + (size_t)t * (a.H * A_DH) + h * A_DH;
+    // row-major, or fragment layout (dims dt*16 + 4g + 0..3 stay adjacent)
+    uint16_t* out = (uint16_t*)a.out;
     const float inv = 1.f / l_run;
 #pragma unroll
-    for (int dt = 0; dt < 8; dt++)
+    for (int dt = 0; dt < 8; dt++) {
+      const int k = h * A_DH + dt * 16 + 4 * g;
+      const size_t o0 = a.out_mtt ? frag_index(t, k, a.out_mtt) : (size_t)t * (a.H * A_DH) + k;
 #pragma unroll
-      for (int v = 0; v < 4; v++) out[dt * 16 + 4 * g + v] = f2bf(o[dt][v] * inv);
+      for (int v = 0; v < 4; v++) out[o0 + v] = f2bf(o[dt][v] * inv);
+    }
   } else {
     float* po = a.part_o + (((size_t)h * a.splits + sp) * rows16 + t) * A_DH;
 #pragma unroll
@@ -208,7 +212,9 @@ __global__ void k_attn_merge(AttnArgs a) {
     den += wgt * a.part_ml[b * 2 + 1];
     num += wgt * a.part_o[b * A_DH + i];
   }
-  ((uint16_t*)a.out)[(size_t)t * (a.H * A_DH) + h * A_DH + i] = f2bf(num / den);
+  const int k = h * A_DH + i;
+  const size_t o = a.out_mtt ? frag_index(t, k, a.out_mtt) : (size_t)t * (a.H * A_DH) + k;
+  ((uint16_t*)a.out)[o] = f2bf(num / den);
 }
 
 int attn_bf16_splits(int H, int M, int max_ctx) {

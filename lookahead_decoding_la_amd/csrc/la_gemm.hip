@@ -1,266 +1,157 @@
-// Skinny-M GEMMs of the decoder forward pass: Y[M x N] = X[M x K] W^T with
-// fused epilogues (logits store, residual add, RoPE + KV-cache write for the
-// fused QKV projection, SwiGLU for the fused gate/up projection).
+// Skinny-M GEMMs of the decoder forward pass, Y[M x N] = X[M x K] W^T.
 //
 // The lookahead step forwards 1 + (W+G)(N-1) rows at once ("Break the
 // Sequential Dependency of LLM Inference Using Lookahead Decoding", Key
-// points, "Main limitation": 120 extra rows at the 7B setting), so every
-// weight byte feeds ~121 multiply-adds: still below the MI355X bf16 ridge,
-// so the kernel is built to stream weights at HBM rate while MFMA does the
-// arithmetic on the side.
+// points, "Main limitation": 120 extra rows at the 7B setting), so each
+// weight byte feeds ~121 multiply-adds: still under the MI355X bf16 ridge,
+// so the kernel is built to stream weights while MFMA works on the side.
 //
-// bf16 kernel layout (gfx950, wave64, v_mfma_f32_16x16x32_bf16):
-//   - A operand = weight tile, 16 output rows x 32 k, pre-packed so one wave
-//     load is 1 KiB contiguous (16 B per lane);
-//   - B operand = activation fragment, 32 k x 16 rows of X, read from L2;
-//   - a workgroup (4 waves) owns 32 output rows; its waves interleave over
-//     the k-steps (adjacent 1 KiB tiles stream in parallel) and are reduced
-//     through LDS in a fixed order;
-//   - a K split across workgroups, when the row tiles alone cannot fill 256
-//     CUs, is reduced by the last-arriving workgroup in split order, so the
-//     result is deterministic.
-#include "la_internal.h"
+// bf16 kernel (gfx950, wave64, v_mfma_f32_16x16x32_bf16):
+//   - A operand = weights, pre-packed in 16-row x 32-k tiles so one wave
+//     load is 1 KiB contiguous;
+//   - B operand = activations, stored by their producers in the fragment
+//     layout (la_epilogue.h) so one fragment is 1 KiB contiguous;
+//   - a workgroup of 8 waves owns 128 output rows (one 16-row tile per
+//     wave); all waves walk the same k-steps, so each activation fragment
+//     is fetched once per workgroup and shared through an LDS ring (the
+//     per-wave alternative makes L1->L2 traffic several times the weight
+//     traffic);
+//   - a ring of weight stages in VGPRs keeps several stages in flight; the
+//     order of loads and MFMAs is pinned so loads of later stages stay
+//     outstanding while a stage computes;
+//   - when the row tiles alone cannot fill 256 CUs, K is split across
+//     workgroups; each split writes fp32 partial sums and a reduce kernel
+//     (which also applies the epilogue) adds them in split order, so
+//     results are deterministic and no workgroup waits on another.
+#include "la_epilogue.h"
 
 namespace la {
 
-constexpr int GEMM_NA = 2;     // 16-row A tiles per workgroup (32 rows)
-constexpr int GEMM_NW = 4;     // waves per workgroup
-constexpr int GEMM_THREADS = 64 * GEMM_NW;
+constexpr int G_NW = 8;                 // waves per workgroup
+constexpr int G_ROWS = G_NW * 16;       // output rows per workgroup
+constexpr int G_D = 3;                  // weight stages in the ring
 
-// ---------------------------------------------------------------------------
-// epilogues on a pair of adjacent output columns (n even)
-
-template <typename ACT>
-__device__ inline void store_act(void* base, size_t idx, float v);
-template <>
-__device__ inline void store_act<uint16_t>(void* base, size_t idx, float v) {
-  ((uint16_t*)base)[idx] = f2bf(v);
-}
-template <>
-__device__ inline void store_act<float>(void* base, size_t idx, float v) {
-  ((float*)base)[idx] = v;
-}
-
-template <int EPI, typename ACT>
-__device__ inline void epi_pair(const EpiArgs& ea, int t, int n, float v0, float v1) {
-  if (EPI == EPI_LOGITS) {
-    float* o = ea.out_f32 + (size_t)t * ea.ld_out + n;
-    o[0] = v0;
-    o[1] = v1;
-  } else if (EPI == EPI_RESID) {
-    float* o = ea.out_f32 + (size_t)t * ea.ld_out + n;
-    o[0] += v0;
-    o[1] += v1;
-  } else if (EPI == EPI_QKV) {
-    const int L = ea.st->L;
-    const int dh = ea.dh;
-    if (n < ea.qdim + ea.kvdim) {
-      // rotate the adjacent pair (n, n+1) by angle pos * theta^(-2i/dh)
-      int di = (n < ea.qdim ? n : n - ea.qdim) % dh;
-      int pos = L + ea.relpos[t];
-      float c = ea.rope_cos[(size_t)pos * (dh / 2) + di / 2];
-      float s = ea.rope_sin[(size_t)pos * (dh / 2) + di / 2];
-      float r0 = v0 * c - v1 * s, r1 = v0 * s + v1 * c;
-      if (n < ea.qdim) {
-        size_t o = (size_t)t * ea.qdim + n;
-        store_act<ACT>(ea.out_act, o, r0);
-        store_act<ACT>(ea.out_act, o + 1, r1);
-      } else {
-        int kv = n - ea.qdim, hk = kv / dh;
-        size_t o = ((size_t)hk * ea.max_ctx + L + t) * dh + di;
-        store_act<ACT>(ea.k_cache, o, r0);
-        store_act<ACT>(ea.k_cache, o + 1, r1);
-      }
-    } else {
-      int vv = n - ea.qdim - ea.kvdim, hk = vv / dh, di = vv % dh;
-      size_t o = ((size_t)hk * dh + di) * ea.max_ctx + L + t;
-      store_act<ACT>(ea.vt_cache, o, v0);
-      store_act<ACT>(ea.vt_cache, o + ea.max_ctx, v1);
-    }
-  }
-}
-
-__device__ inline float silu(float g) { return g / (1.0f + expf(-g)); }
-
-template <typename ACT>
-__device__ inline void epi_swiglu_pair(const EpiArgs& ea, int t, int j, float g0,
-                                       float g1, float u0, float u1) {
-  size_t o = (size_t)t * ea.ld_out + j;
-  store_act<ACT>(ea.out_act, o, silu(g0) * u0);
-  store_act<ACT>(ea.out_act, o + 1, silu(g1) * u1);
-}
-
-// ---------------------------------------------------------------------------
-// bf16 MFMA kernel
-
-template <int MT, int EPI>
-__global__ __launch_bounds__(GEMM_THREADS) void k_gemm_bf16(
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wp, int K,
-    int ksplit, float* __restrict__ partial, int32_t* __restrict__ counters,
-    EpiArgs ea) {
-  constexpr int NA = GEMM_NA, NW = GEMM_NW;
-  constexpr int PER_WAVE = NA * MT * 4;  // accumulator floats per lane
-  __shared__ float red[NW * PER_WAVE * 64];
-  __shared__ int s_last;
-
+template <int MT, int J>
+__global__ __launch_bounds__(G_NW * 64) void k_gemm_bf16(
+    const uint16_t* __restrict__ X, int MTT, const uint16_t* __restrict__ Wp, int K,
+    int ksplit, float* __restrict__ P, int N, int M) {
+  constexpr int NF = J * MT;                       // B fragments per stage
+  constexpr int FPW = (NF + G_NW - 1) / G_NW;      // of them loaded per wave
+  constexpr int D = G_D;
+  __shared__ bf16x8 xs[2][NF][64];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int wt = blockIdx.x, kz = blockIdx.y;
   const int KS = K >> 5;
   const int ks0 = (int)((long)KS * kz / ksplit);
-  const int ks1 = (int)((long)KS * (kz + 1) / ksplit);
-  const bf16x8* __restrict__ Wv = (const bf16x8*)Wp;
+  const int nst = ((int)((long)KS * (kz + 1) / ksplit) - ks0) / J;
   const bf16x8* __restrict__ Xv = (const bf16x8*)X;
-  const int K8 = K >> 3;
-  const size_t a_base = (size_t)wt * NA * KS * 64 + l;
-  const int xoff = (l & 15) * K8 + (l >> 4);
+  const bf16x8* __restrict__ wp =
+      (const bf16x8*)Wp + ((size_t)(wt * G_NW + w) * KS) * 64 + l;
 
-  f32x4 acc[NA][MT];
+  f32x4 acc[MT];
 #pragma unroll
-  for (int a = 0; a < NA; a++)
-#pragma unroll
-    for (int m = 0; m < MT; m++) acc[a][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < MT; m++) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 ra[D][J], rx[D][FPW];
 
-  bf16x8 ac[NA], bc[MT];
-  int ks = ks0 + w;
-  if (ks < ks1) {
-#pragma unroll
-    for (int a = 0; a < NA; a++)
-      ac[a] = __builtin_nontemporal_load(&Wv[a_base + ((size_t)a * KS + ks) * 64]);
-#pragma unroll
-    for (int m = 0; m < MT; m++) bc[m] = Xv[(size_t)m * 16 * K8 + xoff + ks * 4];
+  // stage st: J k-steps; this wave's weight tiles and its share of the
+  // J*MT activation fragments
+#define LA_ISSUE(slot, st)                                                        \
+  {                                                                               \
+    const int kb_ = ks0 + (st) * J;                                               \
+    _Pragma("unroll") for (int j = 0; j < J; j++)                                 \
+        ra[slot][j] = __builtin_nontemporal_load(&wp[(size_t)(kb_ + j) * 64]);    \
+    _Pragma("unroll") for (int q = 0; q < FPW; q++) {                             \
+      const int f = w + q * G_NW;                                                 \
+      if (NF % G_NW == 0 || f < NF)                                               \
+        rx[slot][q] = Xv[((size_t)(kb_ + f / MT) * MTT + (f % MT)) * 64 + l];     \
+    }                                                                             \
   }
-  for (; ks < ks1; ks += NW) {
-    const int kn = ks + NW;
-    bf16x8 an[NA], bn[MT];
-    if (kn < ks1) {
-#pragma unroll
-      for (int a = 0; a < NA; a++)
-        an[a] = __builtin_nontemporal_load(&Wv[a_base + ((size_t)a * KS + kn) * 64]);
-#pragma unroll
-      for (int m = 0; m < MT; m++) bn[m] = Xv[(size_t)m * 16 * K8 + xoff + kn * 4];
-    }
-#pragma unroll
-    for (int a = 0; a < NA; a++)
-#pragma unroll
-      for (int m = 0; m < MT; m++)
-        acc[a][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ac[a], bc[m], acc[a][m], 0, 0, 0);
-    if (kn < ks1) {
-#pragma unroll
-      for (int a = 0; a < NA; a++) ac[a] = an[a];
-#pragma unroll
-      for (int m = 0; m < MT; m++) bc[m] = bn[m];
-    }
+#define LA_PUTX(slot, buf)                                                        \
+  {                                                                               \
+    _Pragma("unroll") for (int q = 0; q < FPW; q++) {                             \
+      const int f = w + q * G_NW;                                                 \
+      if (NF % G_NW == 0 || f < NF) xs[buf][f][l] = rx[slot][q];                  \
+    }                                                                             \
+  }
+#define LA_MMAS(slot, buf)                                                        \
+  {                                                                               \
+    _Pragma("unroll") for (int j = 0; j < J; j++) {                               \
+      bf16x8 b_[MT];                                                              \
+      _Pragma("unroll") for (int m = 0; m < MT; m++) b_[m] = xs[buf][j * MT + m][l]; \
+      _Pragma("unroll") for (int m = 0; m < MT; m++)                              \
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[slot][j], b_[m], acc[m], 0, 0, 0); \
+    }                                                                             \
   }
 
-  // intra-workgroup reduction over the 4 waves (fixed order)
 #pragma unroll
-  for (int a = 0; a < NA; a++)
-#pragma unroll
-    for (int m = 0; m < MT; m++)
-#pragma unroll
-      for (int v = 0; v < 4; v++)
-        red[((w * NA + a) * MT + m) * 4 * 64 + v * 64 + l] = acc[a][m][v];
+  for (int s = 0; s < D; s++)
+    if (s < nst) LA_ISSUE(s, s);
+  if (nst > 0) LA_PUTX(0, 0);
   __syncthreads();
-
-  // thread (w, l) finishes token tiles m = w, w + 4, ...
-  float sum[NA][(MT + NW - 1) / NW][4];
+  int st = 0;
+  // steady state: every stage issues the stage D ahead; no branches, so
+  // loads of later stages stay in flight across the MFMAs
+  for (; st + 2 * D <= nst; st += D) {
 #pragma unroll
-  for (int a = 0; a < NA; a++)
-#pragma unroll
-    for (int mi = 0; mi < (MT + NW - 1) / NW; mi++) {
-      const int m = w + mi * NW;
-      if (m < MT) {
-#pragma unroll
-        for (int v = 0; v < 4; v++) {
-          float s = 0.f;
-#pragma unroll
-          for (int ww = 0; ww < NW; ww++)
-            s += red[((ww * NA + a) * MT + m) * 4 * 64 + v * 64 + l];
-          sum[a][mi][v] = s;
-        }
-      }
+    for (int s = 0; s < D; s++) {
+      LA_PUTX((s + 1) % D, (st + s + 1) & 1);
+      LA_MMAS(s, (st + s) & 1);
+      LA_ISSUE(s, st + s + D);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
     }
-
-  if (ksplit > 1) {
-    float* my = partial + ((size_t)wt * ksplit + kz) * (NA * MT * 4 * 64);
-#pragma unroll
-    for (int a = 0; a < NA; a++)
-#pragma unroll
-      for (int mi = 0; mi < (MT + NW - 1) / NW; mi++) {
-        const int m = w + mi * NW;
-        if (m < MT)
-#pragma unroll
-          for (int v = 0; v < 4; v++) my[((a * MT + m) * 4 + v) * 64 + l] = sum[a][mi][v];
-      }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&counters[wt], 1) == ksplit - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    const float* base = partial + (size_t)wt * ksplit * (NA * MT * 4 * 64);
-#pragma unroll
-    for (int a = 0; a < NA; a++)
-#pragma unroll
-      for (int mi = 0; mi < (MT + NW - 1) / NW; mi++) {
-        const int m = w + mi * NW;
-        if (m < MT)
-#pragma unroll
-          for (int v = 0; v < 4; v++) {
-            float s = 0.f;
-            for (int z = 0; z < ksplit; z++)
-              s += __builtin_nontemporal_load(&base[(size_t)z * (NA * MT * 4 * 64) +
-                                                     ((a * MT + m) * 4 + v) * 64 + l]);
-            sum[a][mi][v] = s;
-          }
-      }
-    if (tid == 0) counters[wt] = 0;
   }
-
-  // epilogue: lane l holds rows n = 16*rt + 4*(l/16) + v of token 16*m + l%16
+  for (; st < nst; st += D) {
 #pragma unroll
-  for (int mi = 0; mi < (MT + NW - 1) / NW; mi++) {
-    const int m = w + mi * NW;
-    if (m >= MT) continue;
+    for (int s = 0; s < D; s++) {
+      if (st + s < nst) {
+        if (st + s + 1 < nst) LA_PUTX((s + 1) % D, (st + s + 1) & 1);
+        LA_MMAS(s, (st + s) & 1);
+        if (st + s + D < nst) LA_ISSUE(s, st + s + D);
+      }
+      __syncthreads();
+    }
+  }
+#undef LA_ISSUE
+#undef LA_PUTX
+#undef LA_MMAS
+
+  // lane holds rows n = 16*tile + 4*(l/16) + v of token 16*m + l%16
+  float* out = P + (size_t)kz * M * N;
+  const int n = (wt * G_NW + w) * 16 + (l >> 4) * 4;
+#pragma unroll
+  for (int m = 0; m < MT; m++) {
     const int t = m * 16 + (l & 15);
-    if (t >= ea.M) continue;
-    if (EPI == EPI_SWIGLU) {
-      // tile 0 = gate rows, tile 1 = up rows of FFN columns 16*wt ..
-      const int j = wt * 16 + (l >> 4) * 4;
-      epi_swiglu_pair<uint16_t>(ea, t, j, sum[0][mi][0], sum[0][mi][1], sum[1][mi][0], sum[1][mi][1]);
-      epi_swiglu_pair<uint16_t>(ea, t, j + 2, sum[0][mi][2], sum[0][mi][3], sum[1][mi][2], sum[1][mi][3]);
-    } else {
-#pragma unroll
-      for (int a = 0; a < NA; a++) {
-        const int n = (wt * NA + a) * 16 + (l >> 4) * 4;
-        epi_pair<EPI, uint16_t>(ea, t, n, sum[a][mi][0], sum[a][mi][1]);
-        epi_pair<EPI, uint16_t>(ea, t, n + 2, sum[a][mi][2], sum[a][mi][3]);
-      }
-    }
+    if (t < M) *(f32x4*)&out[(size_t)t * N + n] = acc[m];
   }
 }
 
-int gemm_bf16_tiles(int N) { return N / (16 * GEMM_NA); }
+bool gemm_bf16_shape_ok(int N, int K) { return N % G_ROWS == 0 && K % 32 == 0; }
 
-int gemm_bf16_ksplit(int N, int K) {
-  int tiles = gemm_bf16_tiles(N), KS = K / 32, ks = 1;
-  while (tiles * ks < 512 && KS / (ks * 2) >= 16) ks *= 2;
-  return ks;
+GemmPlan gemm_bf16_plan(int N, int K) {
+  GemmPlan p;
+  const int tiles = N / G_ROWS, KS = K / 32;
+  p.ksplit = 1;
+  p.J = KS % 2 == 0 ? 2 : 1;
+  const int cands[] = {1, 2, 4, 8, 16};
+  for (int ks : cands) {
+    if (KS % ks) continue;
+    const int per = KS / ks;
+    if (per < 6) break;
+    p.ksplit = ks;
+    p.J = per % 2 == 0 ? 2 : 1;
+    if (tiles * ks >= 192) break;
+  }
+  return p;
 }
 
-size_t gemm_bf16_partial_floats(int N, int M, int ksplit) {
-  int MT = (M + 15) / 16;
-  return ksplit > 1 ? (size_t)gemm_bf16_tiles(N) * ksplit * GEMM_NA * MT * 4 * 64 : 0;
-}
-
-template <int EPI>
-static void launch_mt(int MT, dim3 grid, const uint16_t* X, const uint16_t* Wp,
-                      int K, int ksplit, float* partial, int32_t* counters,
-                      const EpiArgs& ea, hipStream_t s) {
-#define LA_GEMM_CASE(mt)                                                         \
-  case mt:                                                                       \
-    hipLaunchKernelGGL((k_gemm_bf16<mt, EPI>), grid, dim3(GEMM_THREADS), 0, s, X, \
-                       Wp, K, ksplit, partial, counters, ea);                    \
+template <int J>
+static void launch_j(int MT, dim3 grid, const uint16_t* X, int MTT, const uint16_t* Wp, int K,
+                     int ks, float* P, int N, int M, hipStream_t s) {
+#define LA_GEMM_CASE(mt)                                                                       \
+  case mt:                                                                                     \
+    hipLaunchKernelGGL((k_gemm_bf16<mt, J>), grid, dim3(G_NW * 64), 0, s, X, MTT, Wp, K, ks, P, \
+                       N, M);                                                                  \
     break;
   switch (MT) {
     LA_GEMM_CASE(1) LA_GEMM_CASE(2) LA_GEMM_CASE(3) LA_GEMM_CASE(4)
@@ -272,17 +163,137 @@ static void launch_mt(int MT, dim3 grid, const uint16_t* X, const uint16_t* Wp,
 #undef LA_GEMM_CASE
 }
 
-void launch_gemm_bf16(int epi, const uint16_t* X, const uint16_t* Wp, int K, int N,
-                      int M, int ksplit, float* partial, int32_t* counters,
-                      const EpiArgs& ea, hipStream_t s) {
+void launch_gemm_bf16(const uint16_t* X, int MTT, const uint16_t* Wp, int K, int N, int M,
+                      const GemmPlan& plan, float* P, hipStream_t s) {
   const int MT = (M + 15) / 16;
-  dim3 grid(gemm_bf16_tiles(N), ksplit);
-  switch (epi) {
-    case EPI_LOGITS: launch_mt<EPI_LOGITS>(MT, grid, X, Wp, K, ksplit, partial, counters, ea, s); break;
-    case EPI_RESID: launch_mt<EPI_RESID>(MT, grid, X, Wp, K, ksplit, partial, counters, ea, s); break;
-    case EPI_QKV: launch_mt<EPI_QKV>(MT, grid, X, Wp, K, ksplit, partial, counters, ea, s); break;
-    case EPI_SWIGLU: launch_mt<EPI_SWIGLU>(MT, grid, X, Wp, K, ksplit, partial, counters, ea, s); break;
+  dim3 grid(N / G_ROWS, plan.ksplit);
+  if (plan.J == 2) launch_j<2>(MT, grid, X, MTT, Wp, K, plan.ksplit, P, N, M, s);
+  else launch_j<1>(MT, grid, X, MTT, Wp, K, plan.ksplit, P, N, M, s);
+}
+
+// ---------------------------------------------------------------------------
+// reduce kernels: sum the K-split partials P[z][t][n] in split order and
+// apply the epilogue.  One workgroup per token row.
+
+// Each thread owns 8 adjacent output columns: two float4 loads per split,
+// and for fragment-layout outputs one 16-byte store (8 adjacent k).
+
+__device__ inline void load8(const float* p, float* v) {
+  const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+__device__ inline uint4 pack8(const float* v) {
+  uint4 r;
+  r.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  r.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  r.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+  r.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+  return r;
+}
+
+// fused QKV: RoPE on q and k, store q (row-major) and the K / V^T cache
+__global__ __launch_bounds__(256) void k_red_qkv(const float* __restrict__ P, int ks, int N,
+                                                 int M, EpiArgs ea) {
+  const int t = blockIdx.y;
+  const int n = (blockIdx.x * 256 + threadIdx.x) * 8;
+  if (n >= N) return;
+  float v[8], p[8];
+  load8(P + (size_t)t * N + n, v);
+  for (int z = 1; z < ks; z++) {
+    load8(P + ((size_t)z * M + t) * N + n, p);
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] += p[i];
   }
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) qkv_pair<uint16_t>(ea, t, n + i, v[i], v[i + 1]);
+}
+
+__device__ inline float block_sum(float v, float* sh) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  if (l == 0) sh[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < (int)(blockDim.x >> 6); i++) t += sh[i];
+  __syncthreads();
+  return t;
+}
+
+// residual add + RMSNorm of the new row into fragment-layout bf16; one
+// workgroup of 512 threads per row, 8 columns per thread per pass
+__global__ __launch_bounds__(512) void k_red_resid_norm(const float* __restrict__ P, int ks,
+                                                        int d, int M, float* __restrict__ x,
+                                                        const uint16_t* __restrict__ w,
+                                                        float eps, uint16_t* __restrict__ xnf,
+                                                        int MTT) {
+  __shared__ float sh[8];
+  const int t = blockIdx.x;
+  float* xr = x + (size_t)t * d;
+  float ss = 0.f;
+  for (int i = threadIdx.x * 8; i < d; i += 512 * 8) {
+    float v[8], p[8];
+    load8(xr + i, v);
+    for (int z = 0; z < ks; z++) {
+      load8(P + ((size_t)z * M + t) * d + i, p);
+#pragma unroll
+      for (int e = 0; e < 8; e++) v[e] += p[e];
+    }
+    *(float4*)(xr + i) = make_float4(v[0], v[1], v[2], v[3]);
+    *(float4*)(xr + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
+#pragma unroll
+    for (int e = 0; e < 8; e++) ss = fmaf(v[e], v[e], ss);
+  }
+  ss = block_sum(ss, sh);
+  const float inv = 1.f / sqrtf(ss / (float)d + eps);
+  for (int i = threadIdx.x * 8; i < d; i += 512 * 8) {
+    float v[8];
+    load8(xr + i, v);
+    const uint4 wv = *(const uint4*)(w + i);
+    const uint32_t wb[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+    for (int e = 0; e < 8; e++)
+      v[e] = v[e] * inv * bf2f((uint16_t)(wb[e >> 1] >> ((e & 1) * 16)));
+    *(uint4*)&xnf[frag_index(t, i, MTT)] = pack8(v);
+  }
+}
+
+// SwiGLU of the fused gate/up output (16-row tiles alternate gate, up)
+__global__ __launch_bounds__(256) void k_red_swiglu(const float* __restrict__ P, int ks, int F,
+                                                    int M, uint16_t* __restrict__ af, int MTT) {
+  const int t = blockIdx.y, N = 2 * F;
+  const int j = (blockIdx.x * 256 + threadIdx.x) * 8;
+  if (j >= F) return;
+  const int cg = (j >> 4) * 32 + (j & 15);
+  float g[8], u[8], p[8];
+  load8(P + (size_t)t * N + cg, g);
+  load8(P + (size_t)t * N + cg + 16, u);
+  for (int z = 1; z < ks; z++) {
+    const float* pr = P + ((size_t)z * M + t) * N;
+    load8(pr + cg, p);
+#pragma unroll
+    for (int e = 0; e < 8; e++) g[e] += p[e];
+    load8(pr + cg + 16, p);
+#pragma unroll
+    for (int e = 0; e < 8; e++) u[e] += p[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; e++) g[e] = silu(g[e]) * u[e];
+  *(uint4*)&af[frag_index(t, j, MTT)] = pack8(g);
+}
+
+void launch_red_qkv(const float* P, int ks, int N, int M, const EpiArgs& ea, hipStream_t s) {
+  hipLaunchKernelGGL(k_red_qkv, dim3((N / 8 + 255) / 256, M), dim3(256), 0, s, P, ks, N, M, ea);
+}
+void launch_red_resid_norm(const float* P, int ks, int d, int M, float* x, const uint16_t* w,
+                           float eps, uint16_t* xnf, int MTT, hipStream_t s) {
+  hipLaunchKernelGGL(k_red_resid_norm, dim3(M), dim3(512), 0, s, P, ks, d, M, x, w, eps, xnf, MTT);
+}
+void launch_red_swiglu(const float* P, int ks, int F, int M, uint16_t* af, int MTT,
+                       hipStream_t s) {
+  hipLaunchKernelGGL(k_red_swiglu, dim3((F / 8 + 255) / 256, M), dim3(256), 0, s, P, ks, F, M, af,
+                     MTT);
 }
 
 // ---------------------------------------------------------------------------
@@ -305,17 +316,18 @@ __global__ void k_repack_bf16(const uint16_t* __restrict__ src, int rows, int K,
   }
 }
 
-void launch_repack_bf16(const uint16_t* src, int rows, int K, uint16_t* dst,
-                        int rt_offset, int rt_mult, hipStream_t s) {
+void launch_repack_bf16(const uint16_t* src, int rows, int K, uint16_t* dst, int rt_offset,
+                        int rt_mult, hipStream_t s) {
   size_t lanes = (size_t)(rows / 16) * (K / 32) * 64;
   int blocks = (int)((lanes + 255) / 256);
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(k_repack_bf16, dim3(blocks), dim3(256), 0, s, src, rows, K, dst,
-                     rt_offset, rt_mult);
+  hipLaunchKernelGGL(k_repack_bf16, dim3(blocks), dim3(256), 0, s, src, rows, K, dst, rt_offset,
+                     rt_mult);
 }
 
 // ---------------------------------------------------------------------------
-// fp32 kernel (small models): one thread per (row, output pair)
+// fp32 kernel (small models): one thread per (row, output pair), direct
+// epilogues on row-major activations
 
 template <int EPI>
 __global__ void k_gemm_f32(const float* __restrict__ X, const float* __restrict__ W,
@@ -339,14 +351,24 @@ __global__ void k_gemm_f32(const float* __restrict__ X, const float* __restrict_
       u0 = fmaf(x[k], u0p[k], u0);
       u1 = fmaf(x[k], u1p[k], u1);
     }
-    epi_swiglu_pair<float>(ea, t, n, s0, s1, u0, u1);
+    float* o = (float*)ea.out_act + (size_t)t * ea.ld_out + n;
+    o[0] = silu(s0) * u0;
+    o[1] = silu(s1) * u1;
+  } else if (EPI == EPI_QKV) {
+    qkv_pair<float>(ea, t, n, s0, s1);
+  } else if (EPI == EPI_RESID) {
+    float* o = ea.out_f32 + (size_t)t * ea.ld_out + n;
+    o[0] += s0;
+    o[1] += s1;
   } else {
-    epi_pair<EPI, float>(ea, t, n, s0, s1);
+    float* o = ea.out_f32 + (size_t)t * ea.ld_out + n;
+    o[0] = s0;
+    o[1] = s1;
   }
 }
 
-void launch_gemm_f32(int epi, const float* X, const float* W, const float* W2, int K,
-                     int N, int M, const EpiArgs& ea, hipStream_t s) {
+void launch_gemm_f32(int epi, const float* X, const float* W, const float* W2, int K, int N,
+                     int M, const EpiArgs& ea, hipStream_t s) {
   dim3 grid((N / 2 + 63) / 64, M), block(64);
   switch (epi) {
     case EPI_LOGITS: hipLaunchKernelGGL(k_gemm_f32<EPI_LOGITS>, grid, block, 0, s, X, W, W2, K, N, M, ea); break;

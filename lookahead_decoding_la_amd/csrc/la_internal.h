@@ -133,14 +133,22 @@ struct EpiArgs {
 void launch_repack_bf16(const uint16_t* src, int rows, int K, uint16_t* dst,
                         int rt_offset, int rt_mult, hipStream_t s);
 
-// Y = X W^T with an epilogue; X bf16 [16*ceil(M/16)][K], W repacked, N rows.
-void launch_gemm_bf16(int epi, const uint16_t* X, const uint16_t* Wp, int K,
-                      int N, int M, int ksplit, float* partial,
-                      int32_t* counters, const EpiArgs& ea, hipStream_t s);
-// Choose a K split for the bf16 GEMM (WG count vs partial-sum traffic).
-int gemm_bf16_ksplit(int N, int K);
-size_t gemm_bf16_partial_floats(int N, int M, int ksplit);
-int gemm_bf16_tiles(int N);
+// bf16 GEMM: P[z][t][n] (fp32, row stride N) = partial sum over the z-th
+// K split of X[t][:] W[n][:]; X in fragment layout with MTT token tiles.
+struct GemmPlan {
+  int ksplit;  // K splits (workgroups per 128-row tile)
+  int J;       // k-steps per pipeline stage
+};
+bool gemm_bf16_shape_ok(int N, int K);
+GemmPlan gemm_bf16_plan(int N, int K);
+void launch_gemm_bf16(const uint16_t* X, int MTT, const uint16_t* Wp, int K, int N, int M,
+                      const GemmPlan& plan, float* P, hipStream_t s);
+// reduce kernels (sum K splits in order + epilogue)
+void launch_red_qkv(const float* P, int ks, int N, int M, const EpiArgs& ea, hipStream_t s);
+void launch_red_resid_norm(const float* P, int ks, int d, int M, float* x, const uint16_t* w,
+                           float eps, uint16_t* xnf, int MTT, hipStream_t s);
+void launch_red_swiglu(const float* P, int ks, int F, int M, uint16_t* af, int MTT,
+                       hipStream_t s);
 
 // fp32 path (small models): Y = X W^T with W row-major [N][K] (two
 // matrices for SWIGLU: W2 is the up projection).
@@ -152,7 +160,8 @@ struct AttnArgs {
   const void* q;       // [rows][H*dh] (bf16 or f32)
   const void* k_cache; // [Hkv][ctx_stride][dh]
   const void* vt_cache;// [Hkv][dh][ctx_stride]
-  void* out;           // [rows][H*dh]
+  void* out;           // f32: [rows][H*dh]; bf16: fragment layout, MTT tiles
+  int out_mtt;
   const DevState* st;  // committed length L (device), or NULL: use L_host
   int L_host;
   int M;               // rows in the block (valid + padded candidate rows)
@@ -169,11 +178,15 @@ void launch_attn_f32(const AttnArgs& a, hipStream_t s);
 
 // small kernels
 void launch_fill_u32(void* p, uint32_t v, size_t n, hipStream_t s);
+// Also writes the first layer's normalized input: bf16 -> fragment layout
+// (xnf, MTT tiles, norm weight nw); f32 -> nothing (a separate RMSNorm).
 void launch_assemble(int mode, const DevState* st, const int32_t* win,
                      const int32_t* pool_len, const int32_t* pool,
                      const int32_t* prompt, int M, int W, int N, int G,
                      int32_t* tokens, int32_t* relpos, DevState* st_w,
-                     const void* emb, int d, int bf16, float* x, hipStream_t s);
+                     const void* emb, int d, int bf16, float* x,
+                     const uint16_t* nw, float eps, uint16_t* xnf, int MTT,
+                     hipStream_t s);
 void launch_rmsnorm(const float* x, const void* w, int M, int d, float eps,
                     int bf16, void* out, hipStream_t s);
 void launch_argmax(const float* logits, int M, int V, int32_t* amax,

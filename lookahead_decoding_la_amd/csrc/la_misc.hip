@@ -8,7 +8,7 @@
 // n-grams are cached in a pool; a verification branch checks pool candidates
 // in the same forward pass so the output equals ordinary decoding.  Key
 // points, "Tuning knobs": W window, N n-gram size, G verification size.
-#include "la_internal.h"
+#include "la_epilogue.h"
 
 namespace la {
 
@@ -40,7 +40,9 @@ __global__ void k_assemble(int mode, const DevState* __restrict__ st,
                            const int32_t* __restrict__ pool, const int32_t* __restrict__ prompt,
                            int W, int N, int G, int32_t* tokens, int32_t* relpos,
                            DevState* st_w, const void* __restrict__ emb, int d, int bf16,
-                           float* __restrict__ x) {
+                           float* __restrict__ x, const uint16_t* __restrict__ nw, float eps,
+                           uint16_t* __restrict__ xnf, int MTT) {
+  __shared__ float sh[4];
   const int r = blockIdx.x;
   int tok, rp;
   if (mode == MODE_STEP) {
@@ -64,7 +66,19 @@ __global__ void k_assemble(int mode, const DevState* __restrict__ st,
   float* xr = x + (size_t)r * d;
   if (bf16) {
     const uint16_t* e = (const uint16_t*)emb + (size_t)tok * d;
-    for (int i = threadIdx.x; i < d; i += blockDim.x) xr[i] = bf2f(e[i]);
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) {
+      const float v = bf2f(e[i]);
+      xr[i] = v;
+      ss = fmaf(v, v, ss);
+    }
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    ss = sh[0] + sh[1] + sh[2] + sh[3];
+    const float inv = 1.f / sqrtf(ss / (float)d + eps);
+    for (int i = threadIdx.x; i < d; i += blockDim.x)
+      xnf[frag_index(r, i, MTT)] = f2bf(xr[i] * inv * bf2f(nw[i]));
   } else {
     const float* e = (const float*)emb + (size_t)tok * d;
     for (int i = threadIdx.x; i < d; i += blockDim.x) xr[i] = e[i];
@@ -75,9 +89,9 @@ void launch_assemble(int mode, const DevState* st, const int32_t* win,
                      const int32_t* pool_len, const int32_t* pool, const int32_t* prompt,
                      int M, int W, int N, int G, int32_t* tokens, int32_t* relpos,
                      DevState* st_w, const void* emb, int d, int bf16, float* x,
-                     hipStream_t s) {
+                     const uint16_t* nw, float eps, uint16_t* xnf, int MTT, hipStream_t s) {
   hipLaunchKernelGGL(k_assemble, dim3(M), dim3(256), 0, s, mode, st, win, pool_len, pool,
-                     prompt, W, N, G, tokens, relpos, st_w, emb, d, bf16, x);
+                     prompt, W, N, G, tokens, relpos, st_w, emb, d, bf16, x, nw, eps, xnf, MTT);
 }
 
 // ---------------------------------------------------------------------------

@@ -1,0 +1,97 @@
+"""The LLaMA-2-7B-shaped workload at full size (GPU only), in the launch
+configuration bench.py times (121 rows per step, W15 N5 G15).
+
+- Sampled rows vs the oracle: after a short prompt, the true greedy
+  continuation is planted as a candidate; the step's row 0 and candidate
+  rows must match the oracle's causal logits of the same tokens (2e-2), the
+  argmax decisions must agree wherever the oracle's margin exceeds 0.05, and
+  the candidate must be accepted in full.
+- A property that holds at any size: the lookahead output equals plain
+  one-token greedy decoding (here both on the GPU, 512-token prompt, 256
+  tokens); a divergence is allowed only at a near-tie (margin <= 0.05).
+"""
+import numpy as np
+import pytest
+import torch
+
+import lasynth
+import lookahead_decoding_la_amd as la
+import oracle
+from lockstep import log, margin
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def w7b():
+    cfg = lasynth.get_config("7b")
+    log("[7b] drawing weights on the GPU")
+    w = lasynth.make_weights_device(cfg, seed=0)
+    torch.cuda.synchronize()
+    yield cfg, w
+    del w
+    torch.cuda.empty_cache()
+
+
+def test_7b_sampled_rows_match_oracle(w7b):
+    cfg, dev_w = w7b
+    c32 = cfg.with_(prompt_len=32, n_spans=1, span_len=8)
+    prompt = [int(x) for x in lasynth.make_prompt(c32)]
+    win = lasynth.make_init_window(cfg, np.array(prompt))
+    P, n1 = len(prompt), cfg.N - 1
+    dec = la.LookaheadDecoder(cfg, dev_w, 512)
+    first = dec.prefill(prompt, win)
+    plain = la.LookaheadDecoder(cfg.with_(W=0, G=0), dev_w, 512)
+    assert plain.prefill(prompt) == first
+    cont = []
+    while len(cont) < cfg.N:
+        cont += plain.step()["tokens"]
+    plain.close()
+    dec.debug_pool_insert(first, cont[:n1])
+    r = dec.step()
+    lg = dec.debug_logits()
+    _, amax = dec.debug_block()
+    log(f"[7b] step: accepted {r['accepted']} of {n1}; oracle forward of {P + cfg.N} rows")
+    orc = oracle.Oracle(cfg, lasynth.host_bits(dev_w), 64)
+    _, lo = orc.extend(prompt + [first] + cont[:n1], logits=True)
+    # GPU row 0 <-> oracle row P; candidate row (0, i) <-> oracle row P + i
+    rows = [0] + [1 + n1 * cfg.W + (i - 1) for i in range(1, cfg.N)]
+    ties = 0
+    for j, r_gpu in enumerate(rows):
+        ref = lo[P + j]
+        d = float(np.max(np.abs(lg[r_gpu].astype(np.float64) - ref)))
+        ref_arg = int(np.argmax(ref.astype(np.float32)))
+        m = margin(ref)
+        log(f"  row {r_gpu}: max|dlogit| {d:.3e}, argmax {amax[r_gpu]} vs {ref_arg} (margin {m:.3f})")
+        assert d <= 2e-2
+        if amax[r_gpu] != ref_arg:
+            assert m <= 0.05
+            ties += 1
+    # the prefill's decision too
+    m = margin(lo[P - 1])
+    assert int(np.argmax(lo[P - 1].astype(np.float32))) == first or m <= 0.05
+    if not ties:
+        assert r["accepted"] == n1 and r["tokens"] == cont
+
+
+def test_7b_lookahead_output_equals_plain_greedy(w7b):
+    cfg, dev_w = w7b
+    prompt = lasynth.make_prompt(cfg)
+    win = lasynth.make_init_window(cfg, prompt)
+    M = cfg.gen_tokens
+    dec = la.LookaheadDecoder(cfg, dev_w, 1024)
+    toks, steps = dec.generate(prompt, win, M)
+    dec.close()
+    acc = sum(s["n_emitted"] for s in steps) / len(steps)
+    log(f"[7b] lookahead: {len(steps)} steps for {M} tokens ({acc:.2f} tokens/step)")
+    plain = la.LookaheadDecoder(cfg.with_(W=0, G=0), dev_w, 1024)
+    ref = [plain.prefill(prompt)]
+    margins = [None]
+    while len(ref) < M:
+        ref += plain.step()["tokens"]
+        margins.append(margin(plain.debug_logits()[0]))
+    plain.close()
+    div = next((i for i in range(M) if toks[i] != ref[i]), None)
+    log(f"[7b] first divergence: {div}")
+    if div is not None:
+        assert div > 0 and margins[div] is not None and margins[div] <= 0.05, (div, margins[div])

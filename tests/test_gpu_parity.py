@@ -45,7 +45,7 @@ def test_fp32_lockstep(cfg):
 BF16 = [
     # 121 rows per step (W15 N5 G15) as in the 7B workload, narrow model
     lasynth.get_config("7b", name="bf16_w15", n_layers=3, d_model=512, n_heads=4,
-                       n_kv_heads=4, d_ffn=1376, vocab=2048, prompt_len=64,
+                       n_kv_heads=4, d_ffn=1408, vocab=2048, prompt_len=64,
                        span_len=8, n_spans=2),
     # grouped KV heads, 57 rows per step (W7 N5 G7, the 34B setting)
     lasynth.get_config("34b", name="bf16_gqa_w7", n_layers=2, d_model=1024, n_heads=8,
@@ -57,7 +57,7 @@ BF16 = [
                        span_len=16, n_spans=4),
     # plain one-token decode
     lasynth.get_config("7b", name="bf16_plain", n_layers=2, d_model=512, n_heads=4,
-                       n_kv_heads=4, d_ffn=1376, vocab=2048, prompt_len=64,
+                       n_kv_heads=4, d_ffn=1408, vocab=2048, prompt_len=64,
                        span_len=8, n_spans=2, W=0, G=0),
 ]
 
