@@ -182,13 +182,12 @@ size_t carve(la_ctx* c, void* base) {
     c->af = cv.take<uint16_t>((size_t)c->MR * F);
     c->p_qkv = gemm_bf16_plan(c->qkv_rows, d);
     c->p_o = gemm_bf16_plan(d, c->qdim);
-    c->p_gu = gemm_bf16_plan(2 * F, d);
+    c->p_gu = GemmPlan{1, (d / 32) % 2 == 0 ? 2 : 1};  // no split: SwiGLU fused
     c->p_d = gemm_bf16_plan(d, F);
     c->p_lm = GemmPlan{1, (d / 32) % 2 == 0 ? 2 : 1};
     size_t gp = 0;
     gp = std::max(gp, (size_t)c->p_qkv.ksplit * c->MR * c->qkv_rows);
     gp = std::max(gp, (size_t)c->p_o.ksplit * c->MR * d);
-    gp = std::max(gp, (size_t)c->p_gu.ksplit * c->MR * 2 * F);
     gp = std::max(gp, (size_t)c->p_d.ksplit * c->MR * d);
     c->gpart = cv.take<float>(gp);
     c->attn_splits = attn_bf16_splits(g.n_heads, c->T, c->ctx_stride);
@@ -302,10 +301,8 @@ void enqueue_layers(la_ctx* c, int M, int mode, hipStream_t s, Prof* pf = nullpt
                             g.rms_eps, c->xnf, c->MTT, s);
       P_END();
       P_BEGIN(LA_PROF_GATEUP);
-      launch_gemm_bf16(c->xnf, c->MTT, (const uint16_t*)L.wgu, d, 2 * F, M, c->p_gu, c->gpart, s);
-      P_END();
-      P_BEGIN(LA_PROF_REDUCE);
-      launch_red_swiglu(c->gpart, c->p_gu.ksplit, F, M, c->af, c->MTT, s);
+      launch_gemm_bf16_swiglu(c->xnf, c->MTT, (const uint16_t*)L.wgu, d, 2 * F, M, c->p_gu.J,
+                              c->af, s);
       P_END();
       P_BEGIN(LA_PROF_DOWN);
       launch_gemm_bf16(c->af, c->MTT, (const uint16_t*)L.wd, F, d, M, c->p_d, c->gpart, s);

@@ -31,14 +31,18 @@ constexpr int G_NW = 8;                 // waves per workgroup
 constexpr int G_ROWS = G_NW * 16;       // output rows per workgroup
 constexpr int G_D = 3;                  // weight stages in the ring
 
-template <int MT, int J>
+// OUT = 0: fp32 partial sums P[kz][t][n]; OUT = 1 (no K split, gate/up
+// packed as alternating 16-row tiles): SwiGLU written to the fragment-layout
+// activation buffer A (FFN width N/2).
+template <int MT, int J, int OUT>
 __global__ __launch_bounds__(G_NW * 64) void k_gemm_bf16(
     const uint16_t* __restrict__ X, int MTT, const uint16_t* __restrict__ Wp, int K,
-    int ksplit, float* __restrict__ P, int N, int M) {
+    int ksplit, float* __restrict__ P, int N, int M, uint16_t* __restrict__ A) {
   constexpr int NF = J * MT;                       // B fragments per stage
   constexpr int FPW = (NF + G_NW - 1) / G_NW;      // of them loaded per wave
   constexpr int D = G_D;
-  __shared__ bf16x8 xs[2][NF][64];
+  constexpr int NFX = (OUT == 1 && NF < 2 * MT) ? 2 * MT : NF;  // room for the exchange
+  __shared__ bf16x8 xs[2][NFX][64];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int wt = blockIdx.x, kz = blockIdx.y;
   const int KS = K >> 5;
@@ -117,12 +121,39 @@ __global__ __launch_bounds__(G_NW * 64) void k_gemm_bf16(
 #undef LA_MMAS
 
   // lane holds rows n = 16*tile + 4*(l/16) + v of token 16*m + l%16
-  float* out = P + (size_t)kz * M * N;
-  const int n = (wt * G_NW + w) * 16 + (l >> 4) * 4;
+  if (OUT == 0) {
+    float* out = P + (size_t)kz * M * N;
+    const int n = (wt * G_NW + w) * 16 + (l >> 4) * 4;
 #pragma unroll
-  for (int m = 0; m < MT; m++) {
-    const int t = m * 16 + (l & 15);
-    if (t < M) *(f32x4*)&out[(size_t)t * N + n] = acc[m];
+    for (int m = 0; m < MT; m++) {
+      const int t = m * 16 + (l & 15);
+      if (t < M) *(f32x4*)&out[(size_t)t * N + n] = acc[m];
+    }
+  } else {
+    // wave 2i holds gate rows, wave 2i+1 the matching up rows (FFN tile
+    // 4*wt + i); the up values pass through LDS
+    static_assert(OUT == 0 || sizeof(xs) >= (G_NW / 2) * MT * 64 * sizeof(f32x4), "LDS exchange");
+    f32x4* ex = (f32x4*)&xs[0][0][0];
+    __syncthreads();
+    if (w & 1) {
+#pragma unroll
+      for (int m = 0; m < MT; m++) ex[((w >> 1) * MT + m) * 64 + l] = acc[m];
+    }
+    __syncthreads();
+    if (!(w & 1)) {
+      const int j = (wt * (G_NW / 2) + (w >> 1)) * 16 + (l >> 4) * 4;
+#pragma unroll
+      for (int m = 0; m < MT; m++) {
+        const int t = m * 16 + (l & 15);
+        if (t >= M) continue;
+        const f32x4 u = ex[((w >> 1) * MT + m) * 64 + l];
+        const size_t o = frag_index(t, j, MTT);
+        uint2 pk;
+        pk.x = (uint32_t)f2bf(silu(acc[m][0]) * u[0]) | ((uint32_t)f2bf(silu(acc[m][1]) * u[1]) << 16);
+        pk.y = (uint32_t)f2bf(silu(acc[m][2]) * u[2]) | ((uint32_t)f2bf(silu(acc[m][3]) * u[3]) << 16);
+        *(uint2*)&A[o] = pk;
+      }
+    }
   }
 }
 
@@ -145,13 +176,13 @@ GemmPlan gemm_bf16_plan(int N, int K) {
   return p;
 }
 
-template <int J>
+template <int J, int OUT>
 static void launch_j(int MT, dim3 grid, const uint16_t* X, int MTT, const uint16_t* Wp, int K,
-                     int ks, float* P, int N, int M, hipStream_t s) {
-#define LA_GEMM_CASE(mt)                                                                       \
-  case mt:                                                                                     \
-    hipLaunchKernelGGL((k_gemm_bf16<mt, J>), grid, dim3(G_NW * 64), 0, s, X, MTT, Wp, K, ks, P, \
-                       N, M);                                                                  \
+                     int ks, float* P, int N, int M, uint16_t* A, hipStream_t s) {
+#define LA_GEMM_CASE(mt)                                                                        \
+  case mt:                                                                                      \
+    hipLaunchKernelGGL((k_gemm_bf16<mt, J, OUT>), grid, dim3(G_NW * 64), 0, s, X, MTT, Wp, K, ks, \
+                       P, N, M, A);                                                             \
     break;
   switch (MT) {
     LA_GEMM_CASE(1) LA_GEMM_CASE(2) LA_GEMM_CASE(3) LA_GEMM_CASE(4)
@@ -167,8 +198,16 @@ void launch_gemm_bf16(const uint16_t* X, int MTT, const uint16_t* Wp, int K, int
                       const GemmPlan& plan, float* P, hipStream_t s) {
   const int MT = (M + 15) / 16;
   dim3 grid(N / G_ROWS, plan.ksplit);
-  if (plan.J == 2) launch_j<2>(MT, grid, X, MTT, Wp, K, plan.ksplit, P, N, M, s);
-  else launch_j<1>(MT, grid, X, MTT, Wp, K, plan.ksplit, P, N, M, s);
+  if (plan.J == 2) launch_j<2, 0>(MT, grid, X, MTT, Wp, K, plan.ksplit, P, N, M, nullptr, s);
+  else launch_j<1, 0>(MT, grid, X, MTT, Wp, K, plan.ksplit, P, N, M, nullptr, s);
+}
+
+void launch_gemm_bf16_swiglu(const uint16_t* X, int MTT, const uint16_t* Wp, int K, int N, int M,
+                             int J, uint16_t* A, hipStream_t s) {
+  const int MT = (M + 15) / 16;
+  dim3 grid(N / G_ROWS, 1);
+  if (J == 2) launch_j<2, 1>(MT, grid, X, MTT, Wp, K, 1, nullptr, N, M, A, s);
+  else launch_j<1, 1>(MT, grid, X, MTT, Wp, K, 1, nullptr, N, M, A, s);
 }
 
 // ---------------------------------------------------------------------------

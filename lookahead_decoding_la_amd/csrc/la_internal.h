@@ -143,6 +143,10 @@ bool gemm_bf16_shape_ok(int N, int K);
 GemmPlan gemm_bf16_plan(int N, int K);
 void launch_gemm_bf16(const uint16_t* X, int MTT, const uint16_t* Wp, int K, int N, int M,
                       const GemmPlan& plan, float* P, hipStream_t s);
+// Fused gate/up (alternating 16-row gate / up tiles, no K split) with the
+// SwiGLU written to fragment-layout A (FFN width N/2).
+void launch_gemm_bf16_swiglu(const uint16_t* X, int MTT, const uint16_t* Wp, int K, int N, int M,
+                             int J, uint16_t* A, hipStream_t s);
 // reduce kernels (sum K splits in order + epilogue)
 void launch_red_qkv(const float* P, int ks, int N, int M, const EpiArgs& ea, hipStream_t s);
 void launch_red_resid_norm(const float* P, int ks, int d, int M, float* x, const uint16_t* w,
