@@ -5,26 +5,28 @@
 // one forward pass; the method works with FlashAttention-style kernels).
 //
 // bf16 kernel (gfx950, head_dim 128):
-//   - grid = heads x 64-row token groups x KV splits (flash-decoding style
-//     split of the key range so short contexts still fill 256 CUs);
-//   - each 64-key chunk of K and of V^T is staged once in LDS (padded rows,
-//     no bank conflicts) and shared by the 4 waves of the workgroup;
-//   - S^T = K Q^T on MFMA, so a lane owns one token's scores; the mask is
-//     computed from (row, key) indices, never loaded; the online softmax
-//     max/sum are wave-level reductions across the 4 lane groups;
+//   - grid = heads x KV splits (flash-decoding style split of the key range
+//     so short contexts still fill the CUs); one workgroup holds every query
+//     row of its head (up to 128 rows with 8 waves: 4 row pairs x 2 key
+//     halves; up to 256 rows: 8 row pairs), so each K/V chunk is read from
+//     HBM once per head;
+//   - Q and 64-key chunks of K and V^T go straight from HBM into LDS
+//     (global_load_lds), XOR-swizzled so the MFMA operand reads are free of
+//     bank conflicts, through a ring of chunk buffers a few chunks deep;
+//   - S^T = K Q^T on MFMA, so a lane owns one token's scores; the block mask
+//     is computed per row as a 256-bit set (closed form of the mask), and
+//     chunks wholly inside the committed prefix skip it;
 //   - O^T = V^T P^T on MFMA: P^T feeds MFMA straight from the score
-//     registers (the 32 keys of one k-step are taken in the order the score
-//     layout holds them, V^T is read in the same order);
+//     registers (keys are assigned to score rows so that the 8 keys a lane
+//     passes on are one contiguous V^T piece);
 //   - splits merge in a second kernel (log-sum-exp weights).
 // The cache stores V transposed ([kv head][dh][position]) for this reason.
 #include "la_epilogue.h"
 
 namespace la {
 
-constexpr int AKC = 64;       // keys per chunk
-constexpr int A_DH = 128;     // head_dim of the bf16 kernel
-constexpr int KPAD = A_DH + 8;  // LDS row stride of K (elements)
-constexpr int VPAD = AKC + 8;   // LDS row stride of V^T (elements)
+constexpr int AKC = 64;        // keys per chunk
+constexpr int A_DH = 128;      // head_dim of the bf16 kernel
 constexpr float LOG2E = 1.4426950408889634f;
 
 __device__ inline float wave_max_groups(float v) {
@@ -48,181 +50,434 @@ __device__ inline bool key_visible(int mode, const RowDesc& rd, int t, int M,
   return row_sees(rd, row_desc(b, W, N));
 }
 
-__global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
-  __shared__ uint16_t Ks[AKC * KPAD];
-  __shared__ uint16_t Vs[A_DH * VPAD];
+// Visible keys of one 64-key chunk for one query row, as a bit per key
+// (bit o: key at block index b0 + o).  Keys before the block (b < 0) are
+// the committed cache, always visible; keys past the block are never.
+//   causal: block row t sees block rows <= t;
+//   step:   rm0..rm3 hold the row's 256-bit block mask.
+__device__ inline uint64_t chunk_window(bool causal, int t, int b0, uint64_t rm0, uint64_t rm1,
+                                        uint64_t rm2, uint64_t rm3) {
+  if (causal) {
+    const int tl = t - b0;  // keys o <= tl visible
+    return tl >= 63 ? ~0ull : (tl < 0 ? 0ull : ((2ull << tl) - 1ull));
+  }
+  if (b0 < 0) {  // -63 <= b0 < 0 for a chunk that reaches into the block
+    const int n = -b0;
+    return (rm0 << n) | ((1ull << n) - 1ull);
+  }
+  const int wi = b0 >> 6, sh = b0 & 63;
+  const uint64_t lo = wi == 0 ? rm0 : wi == 1 ? rm1 : wi == 2 ? rm2 : wi == 3 ? rm3 : 0ull;
+  const uint64_t hi = wi == 0 ? rm1 : wi == 1 ? rm2 : wi == 2 ? rm3 : 0ull;
+  return sh ? (lo >> sh) | (hi << (64 - sh)) : lo;
+}
 
-  const int h = blockIdx.x, tg = blockIdx.y, sp = blockIdx.z;
+// Bits [lo, hi) of word wi (bits 64 wi .. 64 wi + 63) of a 256-bit mask.
+__device__ inline uint64_t range_bits(int wi, int lo, int hi) {
+  const int a = max(lo - 64 * wi, 0), b = min(hi - 64 * wi, 64);
+  if (a >= b) return 0ull;
+  const uint64_t upto = b == 64 ? ~0ull : ((1ull << b) - 1ull);
+  return upto & ~((1ull << a) - 1ull);
+}
+
+// The block rows that step-layout row t sees, as a 256-bit mask m0..m3
+// (the same relation as row_sees, in closed form): every row sees row 0; a
+// window row (level l, column j) sees level-1 columns 0..j and its own
+// column at levels 2..l; candidate row (g, i) sees (g, 1..i).
+__device__ inline void step_row_mask(int t, int W, int N, uint64_t& m0, uint64_t& m1,
+                                     uint64_t& m2, uint64_t& m3) {
+  const RowDesc d = row_desc(t, W, N);
+  int lo = 0, hi = 1;  // one contiguous run besides row 0
+  if (d.kind == 1) { lo = 1; hi = d.b + 2; }
+  if (d.kind == 2) { lo = 1 + (N - 1) * W + d.a * (N - 1); hi = lo + d.b; }
+  m0 = range_bits(0, lo, hi) | 1ull;
+  m1 = range_bits(1, lo, hi);
+  m2 = range_bits(2, lo, hi);
+  m3 = range_bits(3, lo, hi);
+  if (d.kind == 1)
+    for (int lv = 2; lv <= d.a; lv++) {
+      const int b = 1 + (lv - 1) * W + d.b;
+      const uint64_t bit = 1ull << (b & 63);
+      const int wi = b >> 6;
+      m0 |= wi == 0 ? bit : 0ull;
+      m1 |= wi == 1 ? bit : 0ull;
+      m2 |= wi == 2 ? bit : 0ull;
+      m3 |= wi == 3 ? bit : 0ull;
+    }
+}
+
+// s_waitcnt with vmcnt(n), other counters untouched (gfx9 encoding: vmcnt
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int n>
+__device__ inline void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier after this wave's LDS operations have completed
+// (lgkmcnt(0)).  Unlike __syncthreads it does not wait for outstanding
+// global loads, so the chunks in flight stay in flight.
+__device__ inline void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// LDS chunk layouts (16-byte pieces, XOR-swizzled so that the MFMA operand
+// reads below hit 16 distinct bank groups):
+//   K:   key r (0..63) owns bytes [256 r, 256 r + 256); dims 8p..8p+7 sit in
+//        slot p ^ kswz(r);
+//   V^T: dim d (0..127) owns bytes [128 d, 128 d + 128); keys 8p..8p+7 sit
+//        in slot p ^ ((d >> 1) & 7).
+__device__ inline int kswz(int r) { return ((r >> 1) & 12) | (r & 3); }
+constexpr int CH_K_BYTES = AKC * A_DH * 2;  // 16 KiB
+constexpr int CH_BYTES = 2 * CH_K_BYTES;    // K + V^T
+
+// Score tile kt (0..3), row r (0..15) holds key 32(kt/2) + 8(r/4) + 4(kt%2)
+// + r%4 of the chunk.  With this order the P^T operand a lane passes to the
+// PV MFMA (tiles 2 s2 and 2 s2 + 1, rows 4g..4g+3) covers keys
+// 32 s2 + 8g .. 32 s2 + 8g + 7, one contiguous V^T piece.
+__device__ inline int score_key(int kt, int r) {
+  return 32 * (kt >> 1) + 8 * (r >> 2) + 4 * (kt & 1) + (r & 3);
+}
+
+// Softmax reference maxima move only when a score exceeds the current one by
+// more than 2^RESCALE_LOG2: probabilities relative to a stale maximum stay
+// below 2^RESCALE_LOG2 (exact in fp32 sums, same relative precision in
+// bf16), and the rescaling of the output accumulators is rarely needed.
+constexpr float RESCALE_LOG2 = 8.f;
+
+// One workgroup = one head x one range of 64-key chunks, all query rows.
+// NRP x KSPL waves: wave w owns 16-row tiles 2 rp and 2 rp + 1 (rp = w %
+// NRP), so every K / V^T fragment read from LDS feeds two MFMAs, and key
+// part kp = w / NRP of each chunk (KSPL parts); the key parts are merged
+// through LDS at the end.  Chunks go straight from HBM to LDS
+// (global_load_lds, no register staging) through a ring of NBUF buffers,
+// NBUF - 1 chunks ahead of the one being consumed.
+template <int NRP, int KSPL, int NBUF>
+__global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
+  constexpr int NW = NRP * KSPL;
+  constexpr int NT = NW * 64;
+  constexpr int QROWS = 32 * NRP;                // query rows held
+  constexpr int QPT = QROWS * 256 / 1024 / NW;   // Q load instructions per thread
+  constexpr int LPC = 32 / NW;                   // chunk load instructions per thread
+  constexpr int KT = 4 / KSPL;                   // 16-key score tiles per wave and chunk
+  static_assert(QPT * NW * 1024 == QROWS * 256 && LPC * NW == 32 && KT * KSPL == 4, "shape");
+  static_assert(KSPL == 1 || NBUF * CH_BYTES >= NRP * 2 * 8 * 64 * 16 + NRP * 2 * 64 * 8,
+                "key-part exchange fits in the ring");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[NBUF * CH_BYTES + QROWS * 256];
+
+  const int h = blockIdx.x, sp = blockIdx.y;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c16 = l & 15;
+  const int rp = w % NRP, kp = w / NRP;
   const int L = a.st ? a.st->L : a.L_host;
   const int M = a.M;
   const int kvh = (h * a.Hkv) / a.H;
   const int ctx = L + M;
   const int nch = (ctx + AKC - 1) / AKC;
   const int cps = (nch + a.splits - 1) / a.splits;
-  const int c0 = sp * cps, c1 = min(nch, c0 + cps);
-  const int t0 = tg * 64 + w * 16;
-  const bool active = t0 < M;
-  const int t = t0 + c16;
+  const int c0 = min(sp * cps, nch), c1 = min(nch, c0 + cps);
+  const int nloc = c1 - c0;
   const int rows16 = (M + 15) & ~15;
-  const RowDesc rd = row_desc(t < M ? t : 0, a.W, a.N);
   const float sl2 = LOG2E / sqrtf((float)A_DH);
+  const bool causal = a.mode == MODE_CAUSAL;
 
   const uint16_t* kc = (const uint16_t*)a.k_cache + (size_t)kvh * a.ctx_stride * A_DH;
   const uint16_t* vc = (const uint16_t*)a.vt_cache + (size_t)kvh * A_DH * a.ctx_stride;
 
-  bf16x8 qf[4];
-  if (t < M) {
-    const uint16_t* qrow = (const uint16_t*)a.q + (size_t)t * (a.H * A_DH) + h * A_DH;
+  // Row masks of this wave's two tiles (padding tokens take a valid row).
+  // They are computed, not loaded: an ordinary global load in flight next
+  // to the LDS-direct loads makes the compiler wait for every outstanding
+  // load before its first use.
+  uint64_t rm[2][4];
+  int trow[2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ks++) qf[ks] = *(const bf16x8*)(qrow + ks * 32 + g * 8);
-  } else {
+  for (int u = 0; u < 2; u++) {
+    const int t = (2 * rp + u) * 16 + c16;
+    trow[u] = t < M ? t : (causal ? M - 1 : 0);
+#pragma unroll
+    for (int i = 0; i < 4; i++) rm[u][i] = 0ull;
+    if (!causal) step_row_mask(trow[u], a.W, a.N, rm[u][0], rm[u][1], rm[u][2], rm[u][3]);
+  }
+  const bool act = 2 * rp * 16 < M;  // tile 2 rp holds tokens
+  const bool act1 = (2 * rp + 1) * 16 < M;
+
+  // Q of the head: row t (0 .. QROWS - 1, padding rows repeat row M - 1)
+  // owns bytes [256 t, 256 t + 256) after the chunk ring; dims 8p..8p+7 sit
+  // in slot p ^ (t & 15).
+  unsigned char* qb = lds + NBUF * CH_BYTES;
+#pragma unroll
+  for (int q = 0; q < QPT; q++) {
+    const int j = w + q * NW;  // 1 KiB = 4 rows
+    const int t = 4 * j + (l >> 4), sq = l & 15;
+    const uint16_t* gq = (const uint16_t*)a.q + (size_t)min(t, M - 1) * (a.H * A_DH) + h * A_DH +
+                         ((sq ^ (t & 15)) * 8);
+    __builtin_amdgcn_global_load_lds((const void*)gq,
+                                     (__attribute__((address_space(3))) void*)(qb + j * 1024), 16,
+                                     0, 0);
+  }
+
+  // Issue chunk c into ring slot b.  Instruction j of a chunk (wave-uniform
+  // LDS base, 1 KiB per instruction) covers K keys 4j..4j+3 or V^T dims
+  // 8j..8j+7; lane l loads the global piece that belongs at LDS slot l.
+  auto issue = [&](int c, int b) {
+    c = min(c, nch - 1);  // an empty range (c0 == nch) stages a valid chunk
+    unsigned char* kb = lds + b * CH_BYTES;
+    unsigned char* vb = kb + CH_K_BYTES;
+#pragma unroll
+    for (int q = 0; q < LPC / 2; q++) {
+      const int j = w + q * NW;  // 0..15
+      const int r = 4 * j + (l >> 4), sk = l & 15;
+      const uint16_t* gk = kc + (size_t)(c * AKC + r) * A_DH + ((sk ^ kswz(r)) * 8);
+      __builtin_amdgcn_global_load_lds((const void*)gk,
+                                       (__attribute__((address_space(3))) void*)(kb + j * 1024),
+                                       16, 0, 0);
+      const int d = 8 * j + (l >> 3), sv = l & 7;
+      const uint16_t* gv = vc + (size_t)d * a.ctx_stride + c * AKC + ((sv ^ ((d >> 1) & 7)) * 8);
+      __builtin_amdgcn_global_load_lds((const void*)gv,
+                                       (__attribute__((address_space(3))) void*)(vb + j * 1024),
+                                       16, 0, 0);
+    }
+  };
+
+  // prologue: the first NBUF - 1 chunks (chunk indices clamped so that an
+  // empty or short range still issues the same count of loads)
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; i++) issue(c0 + min(i, max(nloc - 1, 0)), i);
+  wait_vm<(NBUF - 2) * LPC>();  // Q (issued first) has landed
+  lds_barrier();
+  bf16x8 qf[2][4];
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    const int t = (2 * rp + u) * 16 + c16;
 #pragma unroll
     for (int ks = 0; ks < 4; ks++)
-#pragma unroll
-      for (int e = 0; e < 8; e++) qf[ks][e] = (__bf16)0.f;
+      qf[u][ks] = *(const bf16x8*)(qb + t * 256 + (((4 * ks + g) ^ c16) << 4));
   }
 
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 o[8];
+  f32x4 o[2][8];
+  float m_run[2], l_run[2];
 #pragma unroll
-  for (int i = 0; i < 8; i++) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < 2; u++) {
+    m_run[u] = -INFINITY;
+    l_run[u] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) o[u][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
-  for (int c = c0; c < c1; c++) {
-    __syncthreads();
-    // stage K [64 keys][128] and V^T [128][64 keys]; chunk c lies inside the
-    // cache allocation because ctx <= max_ctx <= ctx_stride (a multiple of 64)
-#pragma unroll
-    for (int i = tid; i < AKC * A_DH / 8; i += 256) {
-      const int r = i >> 4, cv = i & 15;
-      const uint4 v = *(const uint4*)(kc + (size_t)(c * AKC + r) * A_DH + cv * 8);
-      *(uint4*)&Ks[r * KPAD + cv * 8] = v;
-    }
-#pragma unroll
-    for (int i = tid; i < A_DH * AKC / 8; i += 256) {
-      const int dr = i >> 3, cv = i & 7;
-      const uint4 v = *(const uint4*)(vc + (size_t)dr * a.ctx_stride + c * AKC + cv * 8);
-      *(uint4*)&Vs[dr * VPAD + cv * 8] = v;
-    }
-    __syncthreads();
-    if (!active) continue;
-
-    // scores: s[kt][v] = key c*64 + kt*16 + 4g + v, token c16
-    f32x4 s[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; kt++) {
-      s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ks++) {
-        const bf16x8 kf = *(const bf16x8*)&Ks[(kt * 16 + c16) * KPAD + ks * 32 + g * 8];
-        s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[kt], 0, 0, 0);
-      }
-    }
-    float mx = -INFINITY;
+  for (int i = 0; i < nloc; i++) {
+    const int c = c0 + i;
+    // keep NBUF - 1 chunks in flight: chunk i + NBUF - 1 goes into the slot
+    // chunk i - 1 used (every wave finished with it at the last barrier);
+    // past the end the last chunk is re-issued, never read
+    issue(c0 + min(i + NBUF - 1, nloc - 1), (i + NBUF - 1) % NBUF);
+    wait_vm<(NBUF - 1) * LPC>();  // this thread's part of chunk i has landed
+    lds_barrier();                 // ... and everyone else's
+    unsigned char* kb = lds + (i % NBUF) * CH_BYTES;
+    unsigned char* vb = kb + CH_K_BYTES;
     const bool full = (c + 1) * AKC <= L;  // whole chunk in the committed prefix
+    const int b0 = c * AKC - L;
+    if (act) {
+      f32x4 s[2][KT];
 #pragma unroll
-    for (int kt = 0; kt < 4; kt++)
+      for (int j = 0; j < KT; j++) {
+        const int kt = kp * KT + j;
+        s[0][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        s[1][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int r = score_key(kt, c16);
+        const unsigned char* krow = kb + r * 256;
+        const int sw = kswz(r);
 #pragma unroll
-      for (int v = 0; v < 4; v++) {
-        float x = s[kt][v] * sl2;
-        if (!full) {
-          const int p = c * AKC + kt * 16 + 4 * g + v;
-          if (!key_visible(a.mode, rd, t, M, L, p, a.W, a.N)) x = -INFINITY;
+        for (int ks = 0; ks < 4; ks++) {
+          const bf16x8 kf = *(const bf16x8*)(krow + (((4 * ks + g) ^ sw) << 4));
+          s[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], s[0][j], 0, 0, 0);
+          s[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][ks], s[1][j], 0, 0, 0);
         }
-        s[kt][v] = x;
-        mx = fmaxf(mx, x);
       }
-    mx = wave_max_groups(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
-    float ps = 0.f;
+      bf16x8 pf[2][KT / 2];
 #pragma unroll
-    for (int kt = 0; kt < 4; kt++)
+      for (int u = 0; u < 2; u++) {
+        const uint64_t win = full ? ~0ull
+                                  : chunk_window(causal, trow[u], b0, rm[u][0], rm[u][1],
+                                                 rm[u][2], rm[u][3]) >> (8 * g);
+        float mx = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < 4; v++) {
-        const float p = (m_new == -INFINITY) ? 0.f : exp2f(s[kt][v] - m_new);
-        s[kt][v] = p;
-        ps += p;
+        for (int j = 0; j < KT; j++) {
+          const int kt = kp * KT + j;
+#pragma unroll
+          for (int v = 0; v < 4; v++) {
+            const int bit = 32 * (kt >> 1) + 4 * (kt & 1) + v;
+            const float x = ((win >> bit) & 1ull) ? s[u][j][v] * sl2 : -INFINITY;
+            s[u][j][v] = x;
+            mx = fmaxf(mx, x);
+          }
+        }
+        mx = wave_max_groups(mx);
+        if (__builtin_amdgcn_ballot_w64(mx > m_run[u] + RESCALE_LOG2)) {  // wave-uniform
+          const float m_new = fmaxf(m_run[u], mx);
+          const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[u] - m_new);
+          l_run[u] *= alpha;
+#pragma unroll
+          for (int d = 0; d < 8; d++) o[u][d] *= alpha;
+          m_run[u] = m_new;
+        }
+        const float m_use = m_run[u] == -INFINITY ? 0.f : m_run[u];  // nothing visible yet
+        float ps = 0.f;
+#pragma unroll
+        for (int j = 0; j < KT; j++)
+#pragma unroll
+          for (int v = 0; v < 4; v++) {
+            const float p = __builtin_amdgcn_exp2f(s[u][j][v] - m_use);
+            s[u][j][v] = p;
+            ps += p;
+          }
+        l_run[u] += ps;
+#pragma unroll
+        for (int j2 = 0; j2 < KT / 2; j2++)
+#pragma unroll
+          for (int v = 0; v < 4; v++) {
+            pf[u][j2][v] = (__bf16)s[u][2 * j2][v];
+            pf[u][j2][4 + v] = (__bf16)s[u][2 * j2 + 1][v];
+          }
       }
-    l_run = l_run * alpha + ps;
+      // O^T += V^T P^T over this wave's 32-key steps.  Keys past ctx (last
+      // chunk only) have zero probability, but their V^T entries may be
+      // stale or uninitialised memory: mask them to zero so that no NaN
+      // reaches the MFMA.
+      const int nvk = ctx - c * AKC;
 #pragma unroll
-    for (int i = 0; i < 8; i++) o[i] *= alpha;
-    m_run = m_new;
+      for (int j2 = 0; j2 < KT / 2; j2++) {
+        const int s2 = kp * (KT / 2) + j2;
+        const int kv = nvk - (32 * s2 + 8 * g);  // valid keys among this lane's 8
+        const uint32_t vm0 = kv >= 2 ? ~0u : (kv == 1 ? 0xffffu : 0u);
+        const uint32_t vm1 = kv >= 4 ? ~0u : (kv == 3 ? 0xffffu : 0u);
+        const uint32_t vm2 = kv >= 6 ? ~0u : (kv == 5 ? 0xffffu : 0u);
+        const uint32_t vm3 = kv >= 8 ? ~0u : (kv == 7 ? 0xffffu : 0u);
+#pragma unroll
+        for (int dt = 0; dt < 8; dt++) {
+          const int d = dt * 16 + c16;
+          bf16x8 vf = *(const bf16x8*)(vb + d * 128 + (((4 * s2 + g) ^ ((d >> 1) & 7)) << 4));
+          if (nvk < AKC) {  // uniform
+            uint4 vr = __builtin_bit_cast(uint4, vf);
+            vr.x &= vm0; vr.y &= vm1; vr.z &= vm2; vr.w &= vm3;
+            vf = __builtin_bit_cast(bf16x8, vr);
+          }
+          o[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[0][j2], o[0][dt], 0, 0, 0);
+          o[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[1][j2], o[1][dt], 0, 0, 0);
+        }
+      }
+    }
+    lds_barrier();  // slot i % NBUF is free for the next issue
+  }
+  wait_vm<0>();  // drain the ring's redundant loads (also before LDS reuse)
 
+  float lsum[2];
 #pragma unroll
-    for (int s2 = 0; s2 < 2; s2++) {
-      bf16x8 pf;
+  for (int u = 0; u < 2; u++) lsum[u] = wave_sum_groups(l_run[u]);
+
+  if constexpr (KSPL == 2) {
+    // key part 1 hands (m, l, O) to key part 0 through the (idle) ring
+    lds_barrier();
+    f32x4* xo = (f32x4*)lds;                                     // [rp][u][dt][lane]
+    float* xm = (float*)(lds + NRP * 2 * 8 * 64 * 16);           // [rp][u][lane][2]
+    if (kp == 1) {
 #pragma unroll
-      for (int v = 0; v < 4; v++) {
-        pf[v] = (__bf16)s[2 * s2][v];
-        pf[4 + v] = (__bf16)s[2 * s2 + 1][v];
+      for (int u = 0; u < 2; u++) {
+#pragma unroll
+        for (int dt = 0; dt < 8; dt++) xo[((rp * 2 + u) * 8 + dt) * 64 + l] = o[u][dt];
+        xm[((rp * 2 + u) * 64 + l) * 2] = m_run[u];
+        xm[((rp * 2 + u) * 64 + l) * 2 + 1] = lsum[u];
       }
+    }
+    lds_barrier();
+    if (kp == 1) return;
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const float mb = xm[((rp * 2 + u) * 64 + l) * 2], lb = xm[((rp * 2 + u) * 64 + l) * 2 + 1];
+      const float ms = fmaxf(m_run[u], mb);
+      const float wa = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[u] - ms);
+      const float wb = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mb - ms);
+      lsum[u] = wa * lsum[u] + wb * lb;
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++) o[u][dt] = wa * o[u][dt] + wb * xo[((rp * 2 + u) * 8 + dt) * 64 + l];
+      m_run[u] = ms;
+    }
+  }
+
+  if (!act) return;
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    if (u == 1 && !act1) break;
+    const int t = (2 * rp + u) * 16 + c16;
+    if (t >= M) continue;
+    if (a.splits == 1) {
+      // row-major, or fragment layout (dims dt*16 + 4g + 0..3 stay adjacent)
+      uint16_t* out = (uint16_t*)a.out;
+      const float inv = 1.f / lsum[u];
 #pragma unroll
       for (int dt = 0; dt < 8; dt++) {
-        const uint16_t* vr = &Vs[(dt * 16 + c16) * VPAD + 32 * s2 + 4 * g];
-        const uint2 lo = *(const uint2*)vr;
-        const uint2 hi = *(const uint2*)(vr + 16);
-        bf16x8 vf;
-        uint4 pack = {lo.x, lo.y, hi.x, hi.y};
-        vf = *(bf16x8*)&pack;
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[dt], 0, 0, 0);
+        const int k = h * A_DH + dt * 16 + 4 * g;
+        const size_t o0 = a.out_mtt ? frag_index(t, k, a.out_mtt) : (size_t)t * (a.H * A_DH) + k;
+        uint2 pk;
+        pk.x = (uint32_t)f2bf(o[u][dt][0] * inv) | ((uint32_t)f2bf(o[u][dt][1] * inv) << 16);
+        pk.y = (uint32_t)f2bf(o[u][dt][2] * inv) | ((uint32_t)f2bf(o[u][dt][3] * inv) << 16);
+        *(uint2*)&out[o0] = pk;
       }
-    }
-  }
-
-  if (!active) return;
-  l_run = wave_sum_groups(l_run);
-  if (t >= M) return;
-  if (a.splits == 1) {
-    // row-major, or fragment layout (dims dt*16 + 4g + 0..3 stay adjacent)
-    uint16_t* out = (uint16_t*)a.out;
-    const float inv = 1.f / l_run;
+    } else {
+      float* po = a.part_o + (((size_t)h * a.splits + sp) * rows16 + t) * A_DH;
 #pragma unroll
-    for (int dt = 0; dt < 8; dt++) {
-      const int k = h * A_DH + dt * 16 + 4 * g;
-      const size_t o0 = a.out_mtt ? frag_index(t, k, a.out_mtt) : (size_t)t * (a.H * A_DH) + k;
-#pragma unroll
-      for (int v = 0; v < 4; v++) out[o0 + v] = f2bf(o[dt][v] * inv);
-    }
-  } else {
-    float* po = a.part_o + (((size_t)h * a.splits + sp) * rows16 + t) * A_DH;
-#pragma unroll
-    for (int dt = 0; dt < 8; dt++)
-      *(f32x4*)&po[dt * 16 + 4 * g] = o[dt];
-    if (g == 0) {
-      float* pm = a.part_ml + (((size_t)h * a.splits + sp) * rows16 + t) * 2;
-      pm[0] = m_run;
-      pm[1] = l_run;
+      for (int dt = 0; dt < 8; dt++) *(f32x4*)&po[dt * 16 + 4 * g] = o[u][dt];
+      if (g == 0) {
+        float* pm = a.part_ml + (((size_t)h * a.splits + sp) * rows16 + t) * 2;
+        pm[0] = m_run[u];
+        pm[1] = lsum[u];
+      }
     }
   }
 }
 
-// combine the splits of one (row, head): weights 2^(m_s - m*)
-__global__ void k_attn_merge(AttnArgs a) {
-  const int t = blockIdx.x, h = blockIdx.y, i = threadIdx.x;  // i < dh
+// Combine the splits of each (row, head) with log-sum-exp weights
+// 2^(m_s - m*).  A workgroup covers 8 rows of one head; a thread, 4 dims.
+__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+  const int h = blockIdx.y, t = blockIdx.x * 8 + (threadIdx.x >> 5), i = (threadIdx.x & 31) * 4;
+  if (t >= a.M) return;
   const int rows16 = (a.M + 15) & ~15;
   float mstar = -INFINITY;
   for (int s = 0; s < a.splits; s++)
     mstar = fmaxf(mstar, a.part_ml[(((size_t)h * a.splits + s) * rows16 + t) * 2]);
-  float den = 0.f, num = 0.f;
+  float den = 0.f;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < a.splits; s++) {
     const size_t b = ((size_t)h * a.splits + s) * rows16 + t;
     const float m = a.part_ml[b * 2];
     const float wgt = (m == -INFINITY) ? 0.f : exp2f(m - mstar);
     den += wgt * a.part_ml[b * 2 + 1];
-    num += wgt * a.part_o[b * A_DH + i];
+    num += wgt * *(const f32x4*)&a.part_o[b * A_DH + i];
   }
+  const float inv = 1.f / den;
   const int k = h * A_DH + i;
   const size_t o = a.out_mtt ? frag_index(t, k, a.out_mtt) : (size_t)t * (a.H * A_DH) + k;
-  ((uint16_t*)a.out)[o] = f2bf(num / den);
+  uint2 pk;
+  pk.x = (uint32_t)f2bf(num[0] * inv) | ((uint32_t)f2bf(num[1] * inv) << 16);
+  pk.y = (uint32_t)f2bf(num[2] * inv) | ((uint32_t)f2bf(num[3] * inv) << 16);
+  *(uint2*)&((uint16_t*)a.out)[o] = pk;
 }
 
+constexpr int A_NBUF = 4;  // ring depth (chunks) of the bf16 kernel
+
 int attn_bf16_splits(int H, int M, int max_ctx) {
-  const int tgs = (M + 63) / 64;
+  (void)M;
   const int max_chunks = (max_ctx + AKC - 1) / AKC;
-  int s = 1;
-  while (H * tgs * s < 512 && s * 2 <= max_chunks && s < 64) s *= 2;
-  return s;
+  // about A_NBUF chunks per split at the largest context, and enough
+  // workgroups to spread over the CUs
+  int s = (max_chunks + A_NBUF - 1) / A_NBUF;
+  const int fill = (128 + H - 1) / H;
+  if (s < fill) s = fill;
+  if (s > max_chunks) s = max_chunks;
+  if (s > 16) s = 16;
+  return s < 1 ? 1 : s;
 }
 
 size_t attn_bf16_partial_floats(int H, int M, int splits, int dh) {
@@ -231,10 +486,13 @@ size_t attn_bf16_partial_floats(int H, int M, int splits, int dh) {
 }
 
 void launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
-  dim3 grid(a.H, (a.M + 63) / 64, a.splits);
-  hipLaunchKernelGGL(k_attn_bf16, grid, dim3(256), 0, s, a);
+  dim3 grid(a.H, a.splits);
+  if (a.M <= 128)
+    hipLaunchKernelGGL((k_attn_bf16<4, 2, A_NBUF>), grid, dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_attn_bf16<8, 1, 2>), grid, dim3(512), 0, s, a);
   if (a.splits > 1)
-    hipLaunchKernelGGL(k_attn_merge, dim3(a.M, a.H), dim3(A_DH), 0, s, a);
+    hipLaunchKernelGGL(k_attn_merge, dim3((a.M + 7) / 8, a.H), dim3(256), 0, s, a);
 }
 
 // ---------------------------------------------------------------------------
