@@ -60,8 +60,8 @@ typedef struct {
   int32_t max_ctx;  /* KV capacity in tokens (prompt + generated + one step's rows) */
   int32_t dtype;    /* la_dtype of weights, activations and KV cache */
 } la_config;
-/* Supported shapes.  LA_BF16: head_dim 128, d_model % 32 == 0,
- * d_ffn % 32 == 0, vocab % 32 == 0.  LA_F32 (small models): head_dim even and
+/* Supported shapes.  LA_BF16: head_dim 128, d_model % 128 == 0,
+ * d_ffn % 64 == 0, vocab % 128 == 0.  LA_F32 (small models): head_dim even and
  * <= 256, d_model, d_ffn and vocab even, max_ctx <= 16384.  Both:
  * n_heads % n_kv_heads == 0 and 1 + (W + G)(N - 1) <= 256.  W = G = 0 gives
  * the plain one-token greedy decode step. */
@@ -138,11 +138,11 @@ enum {
   LA_PROF_QKV = 0,    /* fused QKV projection */
   LA_PROF_ATTN = 1,   /* masked attention (+ split merge) */
   LA_PROF_O = 2,      /* output projection */
-  LA_PROF_GATEUP = 3, /* fused gate/up projection */
+  LA_PROF_GATEUP = 3, /* fused gate/up projection with the SwiGLU */
   LA_PROF_DOWN = 4,   /* down projection */
   LA_PROF_LMHEAD = 5, /* LM head (logits) */
   LA_PROF_REDUCE = 6, /* split-K sums with fused epilogues (RoPE + KV write,
-                         residual + RMSNorm, SwiGLU) and RMSNorm kernels */
+                         residual + RMSNorm) and RMSNorm kernels */
   LA_PROF_OTHER = 7,  /* assembly, argmax, verification, KV compaction */
   LA_PROF_CLASSES = 8
 };
