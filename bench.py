@@ -74,41 +74,103 @@ def traffic_from_profiles(kernel_key: str):
     return None
 
 
-def cpu_baseline(cfg, prompt, win, tokens_per_step):
-    """Time the CPU oracle on a bounded sample of the same workload: one
-    lookahead step (all 121 rows valid: G candidates planted) on the 7B-width
-    model cut to 1 and to 2 layers after a 16-token prompt; the step time is
-    extrapolated linearly to the full layer count."""
+COPY_PROBE_BYTES = 1 << 29  # bytes read (and written) by one --copy-probe launch
+GATEUP_RE = r"k_gemm_bf16<\d+, \d+, 1>"
+COPY_RE = r"neg_kernel"
+
+
+def copy_probe():
+    """A plain copy of known size for counter calibration: 5 launches of one
+    elementwise kernel reading COPY_PROBE_BYTES and writing as many."""
+    import torch
+    src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy probe: 5 x {COPY_PROBE_BYTES} B read + written")
+
+
+def _counter_kb(run_dir, counter, name_re):
+    """Mean per-dispatch value (KiB) of one counter in a rocprofv3 csv run,
+    over the dispatches whose kernel name matches name_re."""
+    import csv
+    import glob
+    import re
+    vals = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row["Counter_Name"] != counter:
+                    continue
+                vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    hits = [v for k, vs in vals.items() if re.search(name_re, k) for v in vs]
+    if not hits:
+        raise SystemExit(f"no {counter} dispatches matching {name_re} under {run_dir}")
+    return sum(hits) / len(hits), len(hits)
+
+
+def write_traffic(dirs, config_name):
+    """profiles/traffic.json + a markdown summary from four counter runs:
+    FETCH_SIZE and WRITE_SIZE over the bench, then over the copy probe."""
+    cfg = lasynth.get_config(config_name)
+    gu_f, n_f = _counter_kb(dirs[0], "FETCH_SIZE", GATEUP_RE)
+    gu_w, n_w = _counter_kb(dirs[1], "WRITE_SIZE", GATEUP_RE)
+    cp_f, _ = _counter_kb(dirs[2], "FETCH_SIZE", COPY_RE)
+    cp_w, _ = _counter_kb(dirs[3], "WRITE_SIZE", COPY_RE)
+    sf = COPY_PROBE_BYTES / (cp_f * 1024.0)
+    sw = COPY_PROBE_BYTES / (cp_w * 1024.0)
+    fetch, write = gu_f * 1024.0 * sf, gu_w * 1024.0 * sw
+    src = os.path.join(ROOT, "lookahead_decoding_la_amd", "csrc", "la_gemm.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    alg = gateup_bytes_per_launch(cfg, cfg.T)
+    entry = {"bytes_per_launch": round(fetch + write), "fetch_bytes": round(fetch),
+             "write_bytes": round(write), "fetch_kib_raw": gu_f, "write_kib_raw": gu_w,
+             "dispatches": [n_f, n_w], "copy_fetch_kib_raw": cp_f, "copy_write_kib_raw": cp_w,
+             "copy_scale_fetch": sf, "copy_scale_write": sw,
+             "algorithmic_bytes_per_launch": alg, "source_sha256_16": digest}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        t = {}
+    t[f"gate_up_{cfg.name}"] = entry
+    with open(path, "w") as f:
+        json.dump(t, f, indent=1)
+    print(json.dumps(entry))
+
+
+def cpu_baseline(cfg, prompt, win, n_steps=3):
+    """Time the CPU oracle (as it stands) on a bounded sample of the same
+    workload: the full model and step shape, n_steps lookahead steps after a
+    16-token prompt, with G candidates planted under each step's current
+    token so that every step forwards all T rows."""
     import oracle
     P = 16
-    times = {}
-    for nl in (1, 2):
-        c = cfg.with_(n_layers=nl)
-        w = lasynth.host_bits(lasynth.make_weights_device(c, seed=0))
-        o = oracle.Oracle(c, w, P + 2 * c.T + 8)
-        o.prefill(prompt[:P], win)
-        rng = np.random.default_rng(0)
-        for _ in range(c.G):
-            o.pool_insert(o.current, rng.integers(0, c.vocab, size=c.N - 1))
+    w = lasynth.host_bits(lasynth.make_weights_device(cfg, seed=0))
+    o = oracle.Oracle(cfg, w, P + (n_steps + 1) * cfg.T + 8)
+    o.prefill(prompt[:P], win)
+    rng = np.random.default_rng(0)
+    secs, emitted = 0.0, 0
+    for _ in range(n_steps):
+        for _ in range(cfg.G):
+            o.pool_insert(o.current, rng.integers(0, cfg.vocab, size=cfg.N - 1))
         t0 = time.perf_counter()
-        o.step()
-        times[nl] = time.perf_counter() - t0
-        log(f"cpu oracle, {nl} layer(s): {times[nl]:.2f} s per step")
-        del o, w
-    per_layer = max(times[2] - times[1], 0.0)
-    head = max(times[1] - per_layer, 0.0)
-    step_s = head + cfg.n_layers * per_layer
+        r = o.step()
+        secs += time.perf_counter() - t0
+        emitted += r["n_emitted"]
+    log(f"cpu oracle: {n_steps} steps in {secs:.1f} s ({oracle.max_threads()} threads)")
+    del o, w
     return {
-        "value": tokens_per_step / step_s,
+        "value": emitted / secs,
         "unit": "tokens/s",
         "cores": oracle.max_threads(),
         "kind": "oracle",
-        "sample": (f"one lookahead step (121 valid rows) of the fp64 oracle on the "
-                   f"{cfg.name} widths cut to 1 and 2 layers after a 16-token prompt "
-                   f"({times[1]:.2f} s, {times[2]:.2f} s); step time extrapolated to "
-                   f"{cfg.n_layers} layers = {step_s:.1f} s; tokens per step taken "
-                   f"from the GPU run (the outputs are identical)"),
-        "ms_per_step": step_s * 1e3,
+        "sample": (f"{n_steps} lookahead steps of the fp64 oracle on the full {cfg.name} "
+                   f"model ({cfg.T} rows each, G candidates planted per step) after a "
+                   f"{P}-token prompt: {secs:.1f} s, {emitted} tokens"),
+        "ms_per_step": secs / n_steps * 1e3,
     }
 
 
@@ -120,7 +182,20 @@ def main():
     ap.add_argument("--config", default="7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-plain", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only the copy kernel used to calibrate HBM counters")
+    ap.add_argument("--write-traffic", nargs=4, metavar="DIR",
+                    help="rocprofv3 csv runs: bench FETCH_SIZE, bench WRITE_SIZE, "
+                         "copy FETCH_SIZE, copy WRITE_SIZE; writes profiles/traffic.json")
     args = ap.parse_args()
+    global lasynth
+    import lasynth
+    if args.write_traffic:
+        write_traffic(args.write_traffic, args.config)
+        return
+    if args.copy_probe:
+        copy_probe()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the "
               "lookahead step runs on a single MI355X", file=sys.stderr)
@@ -128,8 +203,6 @@ def main():
 
     import torch
     import lookahead_decoding_la_amd as la
-    global lasynth
-    import lasynth
 
     cfg = lasynth.get_config(args.config)
     log(f"config {cfg.name}: T={cfg.T}, drawing weights on the GPU")
@@ -182,14 +255,23 @@ def main():
     step_ms_by_class = {k: v[0] / n_prof for k, v in prof.items()}
     log("per-step ms by kernel class: " +
         ", ".join(f"{k} {v:.3f}" for k, v in step_ms_by_class.items()))
-    gu_s = avg_ms["gate_up"] * 1e-3
+    # The dominant kernel's launch duration: launched back to back over the
+    # 32 layers' weights (so no launch finds its weights in the last-level
+    # cache) between two HIP events on the context's stream.  The per-launch
+    # event pairs of the profiled steps add their own overhead to every
+    # launch; that figure is reported beside it.
+    gu_s = dec.profile_kernel("gate_up", 64) * 1e-6
+    gu_step = avg_ms["gate_up"]
+    log(f"gate/up kernel: {gu_s * 1e6:.2f} us per launch alone, "
+        f"{gu_step * 1e3:.2f} us with events around each launch in a step")
     gu_bytes = gateup_bytes_per_launch(cfg, cfg.T)
     achieved = gu_bytes / gu_s / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profiles(f"gate_up_{cfg.name}"),
                 "kernel": "k_gemm_bf16 (fused gate/up + SwiGLU)",
-                "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_s * 1e6, 2)}
+                "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_s * 1e6, 2),
+                "avg_launch_us_step_events": round(gu_step * 1e3, 2)}
     dec.close()
 
     plain = None
@@ -212,7 +294,7 @@ def main():
     if not args.no_cpu_baseline:
         del dev_w
         torch.cuda.empty_cache()
-        cpu = cpu_baseline(cfg, prompt, win, emitted / args.steps)
+        cpu = cpu_baseline(cfg, prompt, win)
 
     per_ms = np.array(per) * 1e3
     out = {

@@ -149,6 +149,18 @@ enum {
 la_status la_profile_step(la_ctx *c, float *ms, int32_t *launches,
                           la_step_result *out);
 
+/* Mean duration of one launch of a single kernel class, without per-launch
+ * event overhead: the kernel(s) of class klass (LA_PROF_QKV, LA_PROF_ATTN,
+ * LA_PROF_O, LA_PROF_GATEUP or LA_PROF_DOWN) launched reps times back to
+ * back (1..100000), launch i on layer i % n_layers, on the context's current
+ * buffers, between two HIP events on the context's stream; *us_per_launch
+ * (host) receives the mean in microseconds.
+ * The decoding state is unchanged (only scratch buffers that every step
+ * rewrites are written).  bf16 contexts only, after la_prefill.
+ * Errors: LA_ERR_INVALID_ARG, LA_ERR_STATE, LA_ERR_UNSUPPORTED, LA_ERR_HIP. */
+la_status la_profile_kernel(la_ctx *c, int32_t klass, int32_t reps,
+                            float *us_per_launch);
+
 /* ---- inspection (tests, debugging); each synchronizes the stream ------- */
 
 /* Logits of the last step's rows, host float [rows][vocab]; n = element

@@ -29,6 +29,7 @@ EXPORTS = [
     "la_debug_block", "la_debug_window", "la_debug_pool",
     "la_debug_pool_insert", "la_debug_kv", "la_debug_state",
     "la_attention_workspace_bytes", "la_attention", "la_profile_step",
+    "la_profile_kernel",
 ]
 
 PROF_CLASSES = ["qkv", "attention", "o_proj", "gate_up", "down", "lm_head",
@@ -91,6 +92,7 @@ def lib():
             "la_attention": (C.c_int, [P, P, P, P, I32, I32, I32, I32, I32, I32, I32,
                                        I32, P, SZ, P]),
             "la_profile_step": (C.c_int, [P, pf, pi, C.POINTER(LaStepResult)]),
+            "la_profile_kernel": (C.c_int, [P, I32, I32, pf]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -207,6 +209,14 @@ class LookaheadDecoder:
                    accepted=int(r.accepted), winner=int(r.winner),
                    n_candidates=int(r.n_candidates), kv_len=int(r.kv_len))
         return res, {c: (float(ms[i]), int(n[i])) for i, c in enumerate(PROF_CLASSES)}
+
+    def profile_kernel(self, klass: str, reps: int = 32) -> float:
+        """Mean microseconds per launch of one kernel class (layer 0's), from
+        reps back-to-back launches between two HIP events."""
+        us = C.c_float()
+        self._check(lib().la_profile_kernel(self._h, PROF_CLASSES.index(klass), int(reps),
+                                            C.byref(us)), "la_profile_kernel")
+        return float(us.value)
 
     def generate(self, prompt, init_window, M: int):
         out = [self.prefill(prompt, init_window)]

@@ -624,6 +624,60 @@ la_status la_profile_step(la_ctx* c, float* ms, int32_t* launches, la_step_resul
   return LA_OK;
 }
 
+la_status la_profile_kernel(la_ctx* c, int32_t klass, int32_t reps, float* us_per_launch) {
+  la_status us = check_usable(c);
+  if (us != LA_OK) return us;
+  if (!us_per_launch || reps < 1 || reps > 100000)
+    return fail(c, LA_ERR_INVALID_ARG, "reps must be in 1..100000 and the output non-NULL");
+  if (!c->prefilled) return fail(c, LA_ERR_STATE, "la_profile_kernel before la_prefill");
+  if (!c->bf16) return fail(c, LA_ERR_UNSUPPORTED, "la_profile_kernel needs the bf16 kernels");
+  if (klass != LA_PROF_QKV && klass != LA_PROF_ATTN && klass != LA_PROF_O &&
+      klass != LA_PROF_GATEUP && klass != LA_PROF_DOWN)
+    return fail(c, LA_ERR_INVALID_ARG, "klass must be QKV, ATTN, O, GATEUP or DOWN");
+  const la_config& g = c->cfg;
+  const int d = g.d_model, F = g.d_ffn, M = c->T;
+  const hipStream_t s = c->stream;
+  // launch i runs layer i % n_layers, so the weights streamed differ from
+  // one launch to the next (no help from the last-level cache)
+  auto launch = [&](int l) {
+    const Layer& L = c->layers[l];
+    switch (klass) {
+      case LA_PROF_QKV:
+        launch_gemm_bf16(c->xnf, c->MTT, (const uint16_t*)L.wqkv, d, c->qkv_rows, M, c->p_qkv,
+                         c->gpart, s);
+        break;
+      case LA_PROF_ATTN:
+        launch_attn_bf16(attn_args(c, l, M, MODE_STEP), s);
+        break;
+      case LA_PROF_O:
+        launch_gemm_bf16(c->of, c->MTT, (const uint16_t*)L.wo, c->qdim, d, M, c->p_o, c->gpart, s);
+        break;
+      case LA_PROF_GATEUP:
+        launch_gemm_bf16_swiglu(c->xnf, c->MTT, (const uint16_t*)L.wgu, d, 2 * F, M, c->p_gu.J,
+                                c->af, s);
+        break;
+      default:
+        launch_gemm_bf16(c->af, c->MTT, (const uint16_t*)L.wd, F, d, M, c->p_d, c->gpart, s);
+        break;
+    }
+  };
+  while (c->events.size() < 2) {
+    hipEvent_t e;
+    LA_HIP(c, hipEventCreate(&e));
+    c->events.push_back(e);
+  }
+  LA_HIP(c, hipStreamSynchronize(s));
+  LA_HIP(c, hipEventRecord(c->events[0], s));
+  for (int i = 0; i < reps; i++) launch(i % g.n_layers);
+  LA_HIP(c, hipEventRecord(c->events[1], s));
+  LA_HIP(c, hipGetLastError());
+  LA_HIP(c, hipEventSynchronize(c->events[1]));
+  float ms = 0.f;
+  LA_HIP(c, hipEventElapsedTime(&ms, c->events[0], c->events[1]));
+  *us_per_launch = ms * 1e3f / reps;
+  return LA_OK;
+}
+
 la_status la_destroy(la_ctx* c) {
   if (!c) return LA_OK;
   (void)hipStreamSynchronize(c->stream);
