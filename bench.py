@@ -141,6 +141,51 @@ def write_traffic(dirs, config_name):
     print(json.dumps(entry))
 
 
+SWEEP_WG = (1, 2, 3, 5, 7, 10, 15, 20, 25)
+
+
+def linear_flops(cfg, rows) -> int:
+    """Multiply-add flops of the projections and the LM head for `rows` rows."""
+    d, f = cfg.d_model, cfg.d_ffn
+    qd, kvd = cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
+    per_layer = (qd + 2 * kvd) * d + d * qd + 3 * d * f
+    return 2 * rows * (cfg.n_layers * per_layer + cfg.vocab * d)
+
+
+def sweep(cfg, dev_w, prompt, steps, warmup):
+    """Step time, kernel-class times and GEMM MFMA throughput as W = G grows
+    (N fixed): one context per setting, `steps` graph-replayed steps."""
+    import lookahead_decoding_la_amd as la
+    import torch
+    rows = []
+    for wg in SWEEP_WG:
+        c = cfg.with_(W=wg, G=wg)
+        win = lasynth.make_init_window(c, prompt)
+        max_ctx = c.prompt_len + (warmup + steps + 4) * c.N + c.T + 64
+        dec = la.LookaheadDecoder(c, dev_w, max_ctx)
+        dec.prefill(prompt, win)
+        for _ in range(warmup):
+            dec.step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            dec.step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / steps * 1e3
+        _, p = dec.profile_step()
+        gemm_ms = sum(p[k][0] for k in ("qkv", "o_proj", "gate_up", "down", "lm_head"))
+        dec.close()
+        fl = linear_flops(c, c.T)
+        r = {"W": wg, "G": wg, "N": c.N, "rows": c.T, "ms_per_step": round(ms, 4),
+             "kernel_ms": {k: round(v[0], 4) for k, v in p.items()},
+             "gemm_tflops": round(fl / (gemm_ms * 1e-3) / 1e12, 1),
+             "gemm_mfma_frac_of_2500": round(fl / (gemm_ms * 1e-3) / 2.5e15, 4)}
+        log(f"sweep W=G={wg:2d} T={c.T:3d}: {ms:.3f} ms/step, GEMMs {gemm_ms:.3f} ms "
+            f"({r['gemm_tflops']} TFLOP/s)")
+        rows.append(r)
+    return rows
+
+
 def cpu_baseline(cfg, prompt, win, n_steps=3):
     """Time the CPU oracle (as it stands) on a bounded sample of the same
     workload: the full model and step shape, n_steps lookahead steps after a
@@ -182,6 +227,9 @@ def main():
     ap.add_argument("--config", default="7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-plain", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="W = G sweep at N fixed (step ms, kernel classes, GEMM MFMA "
+                         "throughput); prints one JSON line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only the copy kernel used to calibrate HBM counters")
     ap.add_argument("--write-traffic", nargs=4, metavar="DIR",
@@ -212,6 +260,11 @@ def main():
     win = lasynth.make_init_window(cfg, prompt)
     torch.cuda.synchronize()
     log(f"weights ready in {time.time() - t0:.1f} s")
+    if args.sweep:
+        out = {"metric": "lookahead step ms vs W = G (N = %d)" % cfg.N, "config": cfg.name,
+               "sweep": sweep(cfg, dev_w, prompt, args.steps, args.warmup)}
+        print(json.dumps(out), flush=True)
+        return
     n_prof = 3
     total = args.warmup + args.steps + n_prof
     max_ctx = cfg.prompt_len + (total + 2) * cfg.N + cfg.T + 64

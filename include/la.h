@@ -60,8 +60,8 @@ typedef struct {
   int32_t max_ctx;  /* KV capacity in tokens (prompt + generated + one step's rows) */
   int32_t dtype;    /* la_dtype of weights, activations and KV cache */
 } la_config;
-/* Supported shapes.  LA_BF16: head_dim 128, d_model % 128 == 0,
- * d_ffn % 64 == 0, vocab % 128 == 0.  LA_F32 (small models): head_dim even and
+/* Supported shapes.  LA_BF16: head_dim 128, d_model % 128 == 0 and
+ * <= 8192, d_ffn % 64 == 0, vocab % 128 == 0.  LA_F32 (small models): head_dim even and
  * <= 256, d_model, d_ffn and vocab even, max_ctx <= 16384.  Both:
  * n_heads % n_kv_heads == 0 and 1 + (W + G)(N - 1) <= 256.  W = G = 0 gives
  * the plain one-token greedy decode step. */

@@ -144,6 +144,7 @@ la_status check_config(const la_config* cfg, std::string* why) {
     if (c.head_dim != 128) return uns("bf16 kernels need head_dim 128");
     if (c.d_model % 128 || c.d_ffn % 64 || c.vocab % 128)
       return uns("bf16 kernels need d_model and vocab multiples of 128, d_ffn of 64");
+    if (c.d_model > 8192) return uns("bf16 kernels need d_model <= 8192");
   } else {
     if (c.head_dim > 256) return uns("f32 kernels need head_dim <= 256");
     if (c.d_model % 2 || c.d_ffn % 2 || c.vocab % 2) return uns("f32 kernels need even sizes");

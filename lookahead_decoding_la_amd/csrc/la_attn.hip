@@ -105,26 +105,6 @@ __device__ inline void step_row_mask(int t, int W, int N, uint64_t& m0, uint64_t
     }
 }
 
-// s_waitcnt with vmcnt(n), other counters untouched (gfx9 encoding: vmcnt
-// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-template <int n>
-__device__ inline void wait_vm() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-  asm volatile("" ::: "memory");
-}
-
-// Workgroup barrier after this wave's LDS operations have completed
-// (lgkmcnt(0)).  Unlike __syncthreads it does not wait for outstanding
-// global loads, so the chunks in flight stay in flight.
-__device__ inline void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // LDS chunk layouts (16-byte pieces, XOR-swizzled so that the MFMA operand
 // reads below hit 16 distinct bank groups):
 //   K:   key r (0..63) owns bytes [256 r, 256 r + 256); dims 8p..8p+7 sit in

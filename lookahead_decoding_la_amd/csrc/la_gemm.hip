@@ -157,6 +157,110 @@ __global__ __launch_bounds__(G_NW * 64) void k_gemm_bf16(
   }
 }
 
+// The same product with every operand loaded straight into LDS
+// (global_load_lds, 1 KiB per wave instruction): no staging registers, so
+// the ring can hold G_DD stages (each J k-steps of this workgroup's eight
+// weight tiles and the J*MT activation fragments) and every wave only
+// waits for the stage it is about to use.  One barrier per stage: after
+// it, every wave has finished the previous stage, whose slot is refilled.
+template <int MT, int J, int OUT>
+__global__ __launch_bounds__(G_NW * 64) void k_gemm_dma(
+    const uint16_t* __restrict__ X, int MTT, const uint16_t* __restrict__ Wp, int K,
+    int ksplit, float* __restrict__ P, int N, int M, uint16_t* __restrict__ A) {
+  constexpr int NF = J * MT;                   // activation fragments per stage
+  constexpr int FPW = (NF + G_NW - 1) / G_NW;  // of them loaded per wave
+  constexpr int LPS = J + FPW;                 // load instructions per thread per stage
+  constexpr int WKB = G_NW * J;                // weight KiB per stage
+  constexpr int STAGE = (WKB + NF) * 1024;
+  constexpr int D = STAGE * 4 <= 160 * 1024 ? 4 : 3;
+  static_assert(D * STAGE <= 160 * 1024 && (D - 2) * LPS < 64, "ring");
+  static_assert(OUT == 0 || D * STAGE >= (G_NW / 2) * MT * 64 * 16, "LDS exchange");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[D * STAGE];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int wt = blockIdx.x, kz = blockIdx.y;
+  const int KS = K >> 5;
+  const int ks0 = (int)((long)KS * kz / ksplit);
+  const int nst = ((int)((long)KS * (kz + 1) / ksplit) - ks0) / J;
+  const uint16_t* wb = Wp + (size_t)(wt * G_NW + w) * KS * 512 + l * 8;
+
+  // stage st into ring slot b; past the end the last stage is re-issued
+  // (same count of loads every stage), never read
+  auto issue = [&](int st, int b) {
+    st = min(st, nst - 1);
+    const int kb = ks0 + st * J;
+    unsigned char* sb = lds + b * STAGE;
+#pragma unroll
+    for (int j = 0; j < J; j++)
+      __builtin_amdgcn_global_load_lds((const void*)(wb + (size_t)(kb + j) * 512),
+                                       (__attribute__((address_space(3))) void*)(sb + (w * J + j) * 1024),
+                                       16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < FPW; q++) {
+      const int f = (w + q * G_NW) % NF;  // waves past NF repeat a fragment: same bytes, same slot
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(X + ((size_t)(kb + f / MT) * MTT + f % MT) * 512 + l * 8),
+          (__attribute__((address_space(3))) void*)(sb + (WKB + f) * 1024), 16, 0, 0);
+    }
+  };
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; m++) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < D - 1; i++) issue(i, i);
+  for (int st = 0; st < nst; st++) {
+    wait_vm<(D - 2) * LPS>();  // this thread's part of stage st has landed
+    lds_barrier();              // ... everyone's; and stage st-1 is consumed
+    issue(st + D - 1, (st + D - 1) % D);
+    const unsigned char* sb = lds + (st % D) * STAGE;
+#pragma unroll
+    for (int j = 0; j < J; j++) {
+      const bf16x8 a = *(const bf16x8*)(sb + (w * J + j) * 1024 + l * 16);
+      bf16x8 b[MT];
+#pragma unroll
+      for (int m = 0; m < MT; m++) b[m] = *(const bf16x8*)(sb + (WKB + j * MT + m) * 1024 + l * 16);
+#pragma unroll
+      for (int m = 0; m < MT; m++) acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[m], acc[m], 0, 0, 0);
+    }
+  }
+  wait_vm<0>();  // drain the re-issued stages before the LDS is reused or freed
+
+  // lane holds rows n = 16*tile + 4*(l/16) + v of token 16*m + l%16
+  if (OUT == 0) {
+    float* out = P + (size_t)kz * M * N;
+    const int n = (wt * G_NW + w) * 16 + (l >> 4) * 4;
+#pragma unroll
+    for (int m = 0; m < MT; m++) {
+      const int t = m * 16 + (l & 15);
+      if (t < M) *(f32x4*)&out[(size_t)t * N + n] = acc[m];
+    }
+  } else {
+    // wave 2i holds gate rows, wave 2i+1 the matching up rows (FFN tile
+    // 4*wt + i); the up values pass through the (idle) ring
+    f32x4* ex = (f32x4*)lds;
+    lds_barrier();
+    if (w & 1) {
+#pragma unroll
+      for (int m = 0; m < MT; m++) ex[((w >> 1) * MT + m) * 64 + l] = acc[m];
+    }
+    lds_barrier();
+    if (!(w & 1)) {
+      const int j = (wt * (G_NW / 2) + (w >> 1)) * 16 + (l >> 4) * 4;
+#pragma unroll
+      for (int m = 0; m < MT; m++) {
+        const int t = m * 16 + (l & 15);
+        if (t >= M) continue;
+        const f32x4 u = ex[((w >> 1) * MT + m) * 64 + l];
+        const size_t o = frag_index(t, j, MTT);
+        uint2 pk;
+        pk.x = (uint32_t)f2bf(silu(acc[m][0]) * u[0]) | ((uint32_t)f2bf(silu(acc[m][1]) * u[1]) << 16);
+        pk.y = (uint32_t)f2bf(silu(acc[m][2]) * u[2]) | ((uint32_t)f2bf(silu(acc[m][3]) * u[3]) << 16);
+        *(uint2*)&A[o] = pk;
+      }
+    }
+  }
+}
+
 bool gemm_bf16_shape_ok(int N, int K) { return N % G_ROWS == 0 && K % 32 == 0; }
 
 GemmPlan gemm_bf16_plan(int N, int K) {
@@ -202,12 +306,30 @@ void launch_gemm_bf16(const uint16_t* X, int MTT, const uint16_t* Wp, int K, int
   else launch_j<1, 0>(MT, grid, X, MTT, Wp, K, plan.ksplit, P, N, M, nullptr, s);
 }
 
+template <int J>
+static void launch_dma_swiglu(int MT, dim3 grid, const uint16_t* X, int MTT, const uint16_t* Wp,
+                              int K, int N, int M, uint16_t* A, hipStream_t s) {
+#define LA_GEMM_CASE(mt)                                                                    \
+  case mt:                                                                                  \
+    hipLaunchKernelGGL((k_gemm_dma<mt, J, 1>), grid, dim3(G_NW * 64), 0, s, X, MTT, Wp, K, 1, \
+                       nullptr, N, M, A);                                                   \
+    break;
+  switch (MT) {
+    LA_GEMM_CASE(1) LA_GEMM_CASE(2) LA_GEMM_CASE(3) LA_GEMM_CASE(4)
+    LA_GEMM_CASE(5) LA_GEMM_CASE(6) LA_GEMM_CASE(7) LA_GEMM_CASE(8)
+    LA_GEMM_CASE(9) LA_GEMM_CASE(10) LA_GEMM_CASE(11) LA_GEMM_CASE(12)
+    LA_GEMM_CASE(13) LA_GEMM_CASE(14) LA_GEMM_CASE(15) LA_GEMM_CASE(16)
+    default: break;
+  }
+#undef LA_GEMM_CASE
+}
+
 void launch_gemm_bf16_swiglu(const uint16_t* X, int MTT, const uint16_t* Wp, int K, int N, int M,
                              int J, uint16_t* A, hipStream_t s) {
   const int MT = (M + 15) / 16;
   dim3 grid(N / G_ROWS, 1);
-  if (J == 2) launch_j<2, 1>(MT, grid, X, MTT, Wp, K, 1, nullptr, N, M, A, s);
-  else launch_j<1, 1>(MT, grid, X, MTT, Wp, K, 1, nullptr, N, M, A, s);
+  if (J == 2) launch_dma_swiglu<2>(MT, grid, X, MTT, Wp, K, N, M, A, s);
+  else launch_dma_swiglu<1>(MT, grid, X, MTT, Wp, K, N, M, A, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -232,21 +354,86 @@ __device__ inline uint4 pack8(const float* v) {
   return r;
 }
 
-// fused QKV: RoPE on q and k, store q (row-major) and the K / V^T cache
+// Fused QKV: sum the K splits of one 128-column block (one q, k or v head)
+// for 32 tokens, then RoPE + store q (row-major) or k (cache rows), or
+// transpose v through LDS so that the V^T cache rows (positions of one
+// dimension) are written as contiguous runs.  Thread: token tid/8, columns
+// 16*(tid%8) .. +16 of the block.
+constexpr int RQ_TOK = 32;
+
 __global__ __launch_bounds__(256) void k_red_qkv(const float* __restrict__ P, int ks, int N,
                                                  int M, EpiArgs ea) {
-  const int t = blockIdx.y;
-  const int n = (blockIdx.x * 256 + threadIdx.x) * 8;
-  if (n >= N) return;
-  float v[8], p[8];
-  load8(P + (size_t)t * N + n, v);
-  for (int z = 1; z < ks; z++) {
-    load8(P + ((size_t)z * M + t) * N + n, p);
+  __shared__ float vt[RQ_TOK][128 + 1];
+  const int cb = blockIdx.x, tid = threadIdx.x;
+  const int tl = tid >> 3, c0 = (tid & 7) * 16;
+  const int t = blockIdx.y * RQ_TOK + tl;
+  const int n0 = cb * 128 + c0;
+  const int L = ea.st->L;
+  const bool is_v = cb * 128 >= ea.qdim + ea.kvdim;
+  const int tc = min(t, M - 1);  // rows past M repeat a valid row, never stored
+  const int pos = L + ea.relpos[tc];
+  float v[16];
+  {
+    const float* pr = P + (size_t)tc * N + n0;
 #pragma unroll
-    for (int i = 0; i < 8; i++) v[i] += p[i];
+    for (int e = 0; e < 16; e += 4) {
+      const float4 a = *(const float4*)(pr + e);
+      v[e] = a.x; v[e + 1] = a.y; v[e + 2] = a.z; v[e + 3] = a.w;
+    }
+    for (int z = 1; z < ks; z++) {
+      const float* pz = P + ((size_t)z * M + tc) * N + n0;
+#pragma unroll
+      for (int e = 0; e < 16; e += 4) {
+        const float4 a = *(const float4*)(pz + e);
+        v[e] += a.x; v[e + 1] += a.y; v[e + 2] += a.z; v[e + 3] += a.w;
+      }
+    }
+  }
+  if (!is_v) {
+    // rotary angle of pair i (dims 2i, 2i+1 of the head) at pos
+    const float* cs = ea.rope_cos + (size_t)pos * 64 + c0 / 2;
+    const float* sn = ea.rope_sin + (size_t)pos * 64 + c0 / 2;
+    uint16_t o[16];
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      const float c = cs[e], s = sn[e];
+      o[2 * e] = f2bf(v[2 * e] * c - v[2 * e + 1] * s);
+      o[2 * e + 1] = f2bf(v[2 * e] * s + v[2 * e + 1] * c);
+    }
+    if (t < M) {
+      uint16_t* dst;
+      if (n0 < ea.qdim) {
+        dst = (uint16_t*)ea.out_act + (size_t)t * ea.qdim + n0;
+      } else {
+        const int hk = (n0 - ea.qdim) >> 7;
+        dst = (uint16_t*)ea.k_cache + ((size_t)hk * ea.max_ctx + L + t) * 128 + c0;
+      }
+      uint4 a, b;
+      a.x = o[0] | ((uint32_t)o[1] << 16); a.y = o[2] | ((uint32_t)o[3] << 16);
+      a.z = o[4] | ((uint32_t)o[5] << 16); a.w = o[6] | ((uint32_t)o[7] << 16);
+      b.x = o[8] | ((uint32_t)o[9] << 16); b.y = o[10] | ((uint32_t)o[11] << 16);
+      b.z = o[12] | ((uint32_t)o[13] << 16); b.w = o[14] | ((uint32_t)o[15] << 16);
+      *(uint4*)dst = a;
+      *(uint4*)(dst + 8) = b;
+    }
+    return;  // uniform per workgroup
   }
 #pragma unroll
-  for (int i = 0; i < 8; i += 2) qkv_pair<uint16_t>(ea, t, n + i, v[i], v[i + 1]);
+  for (int e = 0; e < 16; e++) vt[tl][c0 + e] = v[e];
+  __syncthreads();
+  // V^T[hk][d][L + t]: lane = token, so one store instruction writes
+  // contiguous positions of two dimension rows
+  const int hk = (cb * 128 - ea.qdim - ea.kvdim) >> 7;
+  const int tt = tid & 31, dg = tid >> 5;
+  const int tw = blockIdx.y * RQ_TOK + tt;
+  if (tw < M) {
+    uint16_t* base = (uint16_t*)ea.vt_cache + (size_t)hk * 128 * ea.max_ctx + L + tw;
+#pragma unroll
+    for (int e = 0; e < 16; e++) {
+      const int d = dg * 16 + e;
+      base[(size_t)d * ea.max_ctx] = f2bf(vt[tt][d]);
+    }
+  }
 }
 
 __device__ inline float block_sum(float v, float* sh) {
@@ -261,7 +448,9 @@ __device__ inline float block_sum(float v, float* sh) {
 }
 
 // residual add + RMSNorm of the new row into fragment-layout bf16; one
-// workgroup of 512 threads per row, 8 columns per thread per pass
+// workgroup of 512 threads per row, 8 columns per thread per pass (up to
+// two passes: d <= 8192); the row stays in registers between the sum of
+// squares and the scaling
 __global__ __launch_bounds__(512) void k_red_resid_norm(const float* __restrict__ P, int ks,
                                                         int d, int M, float* __restrict__ x,
                                                         const uint16_t* __restrict__ w,
@@ -270,31 +459,38 @@ __global__ __launch_bounds__(512) void k_red_resid_norm(const float* __restrict_
   __shared__ float sh[8];
   const int t = blockIdx.x;
   float* xr = x + (size_t)t * d;
+  float v[2][8];
+  uint4 wv[2];
   float ss = 0.f;
-  for (int i = threadIdx.x * 8; i < d; i += 512 * 8) {
-    float v[8], p[8];
-    load8(xr + i, v);
+#pragma unroll
+  for (int it = 0; it < 2; it++) {
+    const int i = (it * 512 + threadIdx.x) * 8;
+    if (i >= d) continue;
+    wv[it] = *(const uint4*)(w + i);
+    load8(xr + i, v[it]);
     for (int z = 0; z < ks; z++) {
+      float p[8];
       load8(P + ((size_t)z * M + t) * d + i, p);
 #pragma unroll
-      for (int e = 0; e < 8; e++) v[e] += p[e];
+      for (int e = 0; e < 8; e++) v[it][e] += p[e];
     }
-    *(float4*)(xr + i) = make_float4(v[0], v[1], v[2], v[3]);
-    *(float4*)(xr + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    *(float4*)(xr + i) = make_float4(v[it][0], v[it][1], v[it][2], v[it][3]);
+    *(float4*)(xr + i + 4) = make_float4(v[it][4], v[it][5], v[it][6], v[it][7]);
 #pragma unroll
-    for (int e = 0; e < 8; e++) ss = fmaf(v[e], v[e], ss);
+    for (int e = 0; e < 8; e++) ss = fmaf(v[it][e], v[it][e], ss);
   }
   ss = block_sum(ss, sh);
   const float inv = 1.f / sqrtf(ss / (float)d + eps);
-  for (int i = threadIdx.x * 8; i < d; i += 512 * 8) {
-    float v[8];
-    load8(xr + i, v);
-    const uint4 wv = *(const uint4*)(w + i);
-    const uint32_t wb[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+  for (int it = 0; it < 2; it++) {
+    const int i = (it * 512 + threadIdx.x) * 8;
+    if (i >= d) continue;
+    const uint32_t wb[4] = {wv[it].x, wv[it].y, wv[it].z, wv[it].w};
+    float o[8];
 #pragma unroll
     for (int e = 0; e < 8; e++)
-      v[e] = v[e] * inv * bf2f((uint16_t)(wb[e >> 1] >> ((e & 1) * 16)));
-    *(uint4*)&xnf[frag_index(t, i, MTT)] = pack8(v);
+      o[e] = v[it][e] * inv * bf2f((uint16_t)(wb[e >> 1] >> ((e & 1) * 16)));
+    *(uint4*)&xnf[frag_index(t, i, MTT)] = pack8(o);
   }
 }
 
@@ -323,7 +519,8 @@ __global__ __launch_bounds__(256) void k_red_swiglu(const float* __restrict__ P,
 }
 
 void launch_red_qkv(const float* P, int ks, int N, int M, const EpiArgs& ea, hipStream_t s) {
-  hipLaunchKernelGGL(k_red_qkv, dim3((N / 8 + 255) / 256, M), dim3(256), 0, s, P, ks, N, M, ea);
+  hipLaunchKernelGGL(k_red_qkv, dim3(N / 128, (M + RQ_TOK - 1) / RQ_TOK), dim3(256), 0, s, P, ks,
+                     N, M, ea);
 }
 void launch_red_resid_norm(const float* P, int ks, int d, int M, float* x, const uint16_t* w,
                            float eps, uint16_t* xnf, int MTT, hipStream_t s) {

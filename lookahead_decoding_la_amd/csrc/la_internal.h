@@ -31,6 +31,32 @@ __host__ __device__ inline uint16_t f2bf(float f) {
 }
 
 // ---------------------------------------------------------------------------
+// Waits and barriers for kernels that load through global_load_lds (LDS
+// direct loads): the compiler does not order those loads against LDS reads
+// of other waves, so the kernels wait on vmcnt themselves and then meet at
+// a barrier.
+
+// s_waitcnt with vmcnt(n), other counters untouched (gfx9 encoding: vmcnt
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int n>
+__device__ inline void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier after this wave's LDS operations have completed
+// (lgkmcnt(0)).  Unlike __syncthreads it does not wait for outstanding
+// global loads, so the chunks in flight stay in flight.
+__device__ inline void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
 // Device-resident decoding state.  Scalars that change every step live here
 // (not in launch arguments) so one captured graph replays every step.
 

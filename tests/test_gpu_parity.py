@@ -55,6 +55,11 @@ BF16 = [
     lasynth.get_config("13b", name="bf16_w10_long", n_layers=1, d_model=256, n_heads=2,
                        n_kv_heads=2, d_ffn=704, vocab=1024, prompt_len=300,
                        span_len=16, n_spans=4),
+    # 161 rows (W20 N5 G20): the attention variant for more than 128 rows,
+    # in the step and in 192-row prefill chunks
+    lasynth.get_config("7b", name="bf16_w20_t161", n_layers=2, d_model=256, n_heads=2,
+                       n_kv_heads=2, d_ffn=704, vocab=1024, prompt_len=300, W=20, G=20,
+                       span_len=8, n_spans=2),
     # plain one-token decode
     lasynth.get_config("7b", name="bf16_plain", n_layers=2, d_model=512, n_heads=4,
                        n_kv_heads=4, d_ffn=1408, vocab=2048, prompt_len=64,
