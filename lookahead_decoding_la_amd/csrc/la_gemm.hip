@@ -298,10 +298,34 @@ static void launch_j(int MT, dim3 grid, const uint16_t* X, int MTT, const uint16
 #undef LA_GEMM_CASE
 }
 
+template <int J>
+static void launch_dma_part(int MT, dim3 grid, const uint16_t* X, int MTT, const uint16_t* Wp,
+                            int K, int ks, float* P, int N, int M, hipStream_t s) {
+#define LA_GEMM_CASE(mt)                                                                     \
+  case mt:                                                                                   \
+    hipLaunchKernelGGL((k_gemm_dma<mt, J, 0>), grid, dim3(G_NW * 64), 0, s, X, MTT, Wp, K, ks, \
+                       P, N, M, nullptr);                                                    \
+    break;
+  switch (MT) {
+    LA_GEMM_CASE(4) LA_GEMM_CASE(5) LA_GEMM_CASE(6) LA_GEMM_CASE(7)
+    LA_GEMM_CASE(8) LA_GEMM_CASE(9) LA_GEMM_CASE(10) LA_GEMM_CASE(11)
+    LA_GEMM_CASE(12) LA_GEMM_CASE(13) LA_GEMM_CASE(14) LA_GEMM_CASE(15)
+    LA_GEMM_CASE(16)
+    default: break;
+  }
+#undef LA_GEMM_CASE
+}
+
 void launch_gemm_bf16(const uint16_t* X, int MTT, const uint16_t* Wp, int K, int N, int M,
                       const GemmPlan& plan, float* P, hipStream_t s) {
   const int MT = (M + 15) / 16;
   dim3 grid(N / G_ROWS, plan.ksplit);
+  // from 4 token tiles on, the LDS-direct kernel (deeper ring) is faster;
+  // below, the register-ring kernel
+  if (MT >= 4 && plan.J == 2) {
+    launch_dma_part<2>(MT, grid, X, MTT, Wp, K, plan.ksplit, P, N, M, s);
+    return;
+  }
   if (plan.J == 2) launch_j<2, 0>(MT, grid, X, MTT, Wp, K, plan.ksplit, P, N, M, nullptr, s);
   else launch_j<1, 0>(MT, grid, X, MTT, Wp, K, plan.ksplit, P, N, M, nullptr, s);
 }
