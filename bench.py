@@ -75,7 +75,7 @@ def traffic_from_profiles(kernel_key: str):
 
 
 COPY_PROBE_BYTES = 1 << 29  # bytes read (and written) by one --copy-probe launch
-GATEUP_RE = r"k_gemm_bf16<\d+, \d+, 1>"
+GATEUP_RE = r"k_gemm_(bf16|dma)<\d+, \d+, 1>"
 COPY_RE = r"neg_kernel"
 
 
@@ -186,6 +186,40 @@ def sweep(cfg, dev_w, prompt, steps, warmup):
     return rows
 
 
+def sweep_counters(run_dir):
+    """MFMA busy fraction of the GEMM dispatches of each sweep setting, from
+    a rocprofv3 run of `--sweep` with SQ_VALU_MFMA_BUSY_CYCLES and
+    GRBM_GUI_ACTIVE.  Settings are told apart by the workspace-clearing fill
+    each context starts with.  MFMA_BUSY counts busy SIMD-cycles summed over
+    the chip and GRBM_GUI_ACTIVE active cycles summed over the 8 XCDs, so
+    every SIMD busy every cycle reads 4 SIMDs x 32 CUs = 128 per GUI cycle."""
+    import csv
+    import glob
+    import re
+    disp = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                d = disp.setdefault(int(row["Dispatch_Id"]),
+                                    {"name": row["Kernel_Name"], "grid": int(row["Grid_Size"])})
+                d[row["Counter_Name"]] = float(row["Counter_Value"])
+    segs, cur = [], None
+    for _, d in sorted(disp.items()):
+        if "k_fill_u32" in d["name"] and d["grid"] >= (1 << 20):
+            cur = []
+            segs.append(cur)
+        if cur is not None:
+            cur.append(d)
+    out = []
+    for wg, seg in zip(SWEEP_WG, segs):
+        g = [d for d in seg if re.search(r"k_gemm_(bf16|dma)<", d["name"])]
+        mf = sum(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in g)
+        gui = sum(d["GRBM_GUI_ACTIVE"] for d in g)
+        out.append({"W": wg, "G": wg, "gemm_dispatches": len(g),
+                    "gemm_mfma_busy_frac": round(mf / gui / 128.0, 4)})
+    return out
+
+
 def cpu_baseline(cfg, prompt, win, n_steps=3):
     """Time the CPU oracle (as it stands) on a bounded sample of the same
     workload: the full model and step shape, n_steps lookahead steps after a
@@ -230,6 +264,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="W = G sweep at N fixed (step ms, kernel classes, GEMM MFMA "
                          "throughput); prints one JSON line")
+    ap.add_argument("--sweep-counters", metavar="DIR",
+                    help="MFMA busy fraction per sweep setting from a rocprofv3 counter run "
+                         "of --sweep; prints one JSON line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only the copy kernel used to calibrate HBM counters")
     ap.add_argument("--write-traffic", nargs=4, metavar="DIR",
@@ -240,6 +277,9 @@ def main():
     import lasynth
     if args.write_traffic:
         write_traffic(args.write_traffic, args.config)
+        return
+    if args.sweep_counters:
+        print(json.dumps({"sweep_counters": sweep_counters(args.sweep_counters)}))
         return
     if args.copy_probe:
         copy_probe()
