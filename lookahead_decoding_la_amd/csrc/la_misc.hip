@@ -65,20 +65,53 @@ __global__ void k_assemble(int mode, const DevState* __restrict__ st,
   }
   float* xr = x + (size_t)r * d;
   if (bf16) {
+    // 8 columns per thread per pass (d % 128 == 0 for the bf16 kernels,
+    // d <= 8192: at most 4 passes of 256 threads); the row stays in
+    // registers between the sum of squares and the scaling
     const uint16_t* e = (const uint16_t*)emb + (size_t)tok * d;
+    uint4 ev[4], wv[4];
     float ss = 0.f;
-    for (int i = threadIdx.x; i < d; i += blockDim.x) {
-      const float v = bf2f(e[i]);
-      xr[i] = v;
-      ss = fmaf(v, v, ss);
+#pragma unroll
+    for (int it = 0; it < 4; it++) {
+      const int i = (it * 256 + threadIdx.x) * 8;
+      if (i >= d) continue;
+      ev[it] = *(const uint4*)(e + i);
+      wv[it] = *(const uint4*)(nw + i);
+    }
+#pragma unroll
+    for (int it = 0; it < 4; it++) {
+      const int i = (it * 256 + threadIdx.x) * 8;
+      if (i >= d) continue;
+      const uint32_t ew[4] = {ev[it].x, ev[it].y, ev[it].z, ev[it].w};
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; q++) {
+        v[q] = bf2f((uint16_t)(ew[q >> 1] >> ((q & 1) * 16)));
+        ss = fmaf(v[q], v[q], ss);
+      }
+      *(float4*)(xr + i) = make_float4(v[0], v[1], v[2], v[3]);
+      *(float4*)(xr + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
     }
     for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
     if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = ss;
     __syncthreads();
     ss = sh[0] + sh[1] + sh[2] + sh[3];
     const float inv = 1.f / sqrtf(ss / (float)d + eps);
-    for (int i = threadIdx.x; i < d; i += blockDim.x)
-      xnf[frag_index(r, i, MTT)] = f2bf(xr[i] * inv * bf2f(nw[i]));
+#pragma unroll
+    for (int it = 0; it < 4; it++) {
+      const int i = (it * 256 + threadIdx.x) * 8;
+      if (i >= d) continue;
+      const uint32_t ew[4] = {ev[it].x, ev[it].y, ev[it].z, ev[it].w};
+      const uint32_t ww[4] = {wv[it].x, wv[it].y, wv[it].z, wv[it].w};
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const float v0 = bf2f((uint16_t)(ew[q] & 0xffff)) * inv * bf2f((uint16_t)(ww[q] & 0xffff));
+        const float v1 = bf2f((uint16_t)(ew[q] >> 16)) * inv * bf2f((uint16_t)(ww[q] >> 16));
+        o[q] = (uint32_t)f2bf(v0) | ((uint32_t)f2bf(v1) << 16);
+      }
+      *(uint4*)&xnf[frag_index(r, i, MTT)] = uint4{o[0], o[1], o[2], o[3]};
+    }
   } else {
     const float* e = (const float*)emb + (size_t)tok * d;
     for (int i = threadIdx.x; i < d; i += blockDim.x) xr[i] = e[i];
@@ -152,7 +185,34 @@ __global__ __launch_bounds__(256) void k_argmax(const float* __restrict__ logits
   const float* lg = logits + (size_t)r * V;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int i = threadIdx.x; i < V; i += 256) better(bv, bi, lg[i], i);
+  // float4 loads, 8 in flight per thread (V % 4 == 0 when vectorized)
+  if ((V & 3) == 0) {
+    const float4* l4 = (const float4*)lg;
+    const int V4 = V >> 2;
+    int i = threadIdx.x;
+    for (; i + 7 * 256 < V4; i += 8 * 256) {
+      float4 q[8];
+#pragma unroll
+      for (int u = 0; u < 8; u++) q[u] = l4[i + u * 256];
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        const int b = (i + u * 256) * 4;
+        better(bv, bi, q[u].x, b);
+        better(bv, bi, q[u].y, b + 1);
+        better(bv, bi, q[u].z, b + 2);
+        better(bv, bi, q[u].w, b + 3);
+      }
+    }
+    for (; i < V4; i += 256) {
+      const float4 q = l4[i];
+      better(bv, bi, q.x, 4 * i);
+      better(bv, bi, q.y, 4 * i + 1);
+      better(bv, bi, q.z, 4 * i + 2);
+      better(bv, bi, q.w, 4 * i + 3);
+    }
+  } else {
+    for (int i = threadIdx.x; i < V; i += 256) better(bv, bi, lg[i], i);
+  }
   for (int o = 32; o > 0; o >>= 1) {
     const float ov = __shfl_xor(bv, o);
     const int oi = __shfl_xor(bi, o);
@@ -219,17 +279,47 @@ void launch_pool_insert(DevState*, int32_t key, const int32_t* tail_dev, int32_t
 //   n-gram (win[1][j], ..., win[N-1][j], new[j]) is inserted keyed by
 //   win[1][j] for j = 0..W-1 in order; then the levels move down by one.
 
+// Pool lists of the W keys a step touches are staged in LDS when they fit:
+// the inserts (strictly in column order, keys may repeat) then run on LDS
+// copies, and each distinct key's list is written back once.
+constexpr int POOL_LDS_INTS = 6144;
+
+// Insert tail into list lst (len entries of n1 tokens, oldest first).
+__device__ inline int pool_insert_list(int32_t* lst, int len, int n1, int G, const int32_t* tail) {
+  int found = -1;
+  for (int e = 0; e < len && found < 0; e++) {
+    bool same = true;
+    for (int i = 0; i < n1; i++) same = same && lst[e * n1 + i] == tail[i];
+    if (same) found = e;
+  }
+  int gap;
+  if (found >= 0) gap = found;
+  else if (len == G) gap = 0;
+  else gap = len++;
+  for (int e = gap; e + 1 < len; e++)
+    for (int i = 0; i < n1; i++) lst[e * n1 + i] = lst[(e + 1) * n1 + i];
+  for (int i = 0; i < n1; i++) lst[(len - 1) * n1 + i] = tail[i];
+  return len;
+}
+
 __global__ __launch_bounds__(64) void k_verify(DevState* st, const int32_t* __restrict__ tokens,
                                                const int32_t* __restrict__ amax, int32_t* win,
                                                int32_t* pool_len, int32_t* pool, int W, int N,
                                                int G, DevResult* res) {
   __shared__ int32_t ynew[256];
+  __shared__ int32_t lwin[256];             // window, (N-1) x W <= 255
   __shared__ int32_t tail[32];
+  __shared__ int32_t lkey[256], lslot[256], llen[256];
+  __shared__ int32_t llist[POOL_LDS_INTS];
   const int lane = threadIdx.x;
   const int n1 = N - 1;
   const int nwin = n1 * W;
   const int nc = st->n_cand;
   const int a0 = amax[0];
+  const int per = G * n1;  // ints per key list
+  const bool staged = G > 0 && W > 0 && W * per <= POOL_LDS_INTS;
+  for (int i = lane; i < nwin; i += 64) lwin[i] = win[i];
+  for (int j = lane; j < W; j += 64) ynew[j] = amax[1 + (n1 - 1) * W + j];
   // per-candidate accepted length, reduced to (max k, lowest g)
   int bk = -1, bg = 0x7fffffff;
   for (int g = lane; g < nc; g += 64) {
@@ -246,8 +336,26 @@ __global__ __launch_bounds__(64) void k_verify(DevState* st, const int32_t* __re
     const int ok = __shfl_xor(bk, o), og = __shfl_xor(bg, o);
     if (ok > bk || (ok == bk && og < bg)) { bk = ok; bg = og; }
   }
-  for (int j = lane; j < W; j += 64) ynew[j] = amax[1 + (n1 - 1) * W + j];
   __syncthreads();
+  if (staged) {
+    for (int j = lane; j < W; j += 64) {
+      const int key = lwin[j];
+      lkey[j] = key;
+      llen[j] = pool_len[key];
+    }
+    __syncthreads();
+    for (int j = lane; j < W; j += 64) {
+      int sl = j;
+      for (int q = 0; q < j; q++)
+        if (lkey[q] == lkey[j]) { sl = q; break; }
+      lslot[j] = sl;
+    }
+    for (int idx = lane; idx < W * per; idx += 64) {
+      const int j = idx / per, rem = idx - j * per;
+      if (rem < llen[j] * n1) llist[idx] = pool[(size_t)lkey[j] * per + rem];
+    }
+    __syncthreads();
+  }
   if (lane == 0) {
     const int k = nc > 0 ? bk : 0;
     const int gs = nc > 0 ? bg : -1;
@@ -269,15 +377,28 @@ __global__ __launch_bounds__(64) void k_verify(DevState* st, const int32_t* __re
     res->kv_len = L + k + 1;
     // n-gram pool: insert every column's n-gram in column order
     for (int j = 0; j < W; j++) {
-      for (int l = 2; l <= n1; l++) tail[l - 2] = win[(l - 1) * W + j];
+      for (int l = 2; l <= n1; l++) tail[l - 2] = lwin[(l - 1) * W + j];
       tail[n1 - 1] = ynew[j];
-      pool_insert_serial(pool_len, pool, N, G, win[j], tail);
+      if (staged) {
+        const int sl = lslot[j];
+        llen[sl] = pool_insert_list(llist + sl * per, llen[sl], n1, G, tail);
+      } else {
+        pool_insert_serial(pool_len, pool, N, G, lwin[j], tail);
+      }
     }
   }
   __syncthreads();
+  if (staged) {
+    for (int j = lane; j < W; j += 64)
+      if (lslot[j] == j) pool_len[lkey[j]] = llen[j];
+    for (int idx = lane; idx < W * per; idx += 64) {
+      const int j = idx / per, rem = idx - j * per;
+      if (lslot[j] == j && rem < llen[j] * n1) pool[(size_t)lkey[j] * per + rem] = llist[idx];
+    }
+  }
   // shift the window by one level
   for (int j = lane; j < W; j += 64) {
-    for (int l = 1; l < n1; l++) win[(l - 1) * W + j] = win[l * W + j];
+    for (int l = 1; l < n1; l++) win[(l - 1) * W + j] = lwin[l * W + j];
     win[(n1 - 1) * W + j] = ynew[j];
   }
 }
