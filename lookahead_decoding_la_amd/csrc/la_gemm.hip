@@ -322,8 +322,9 @@ void launch_gemm_bf16(const uint16_t* X, int MTT, const uint16_t* Wp, int K, int
   dim3 grid(N / G_ROWS, plan.ksplit);
   // from 4 token tiles on, the LDS-direct kernel (deeper ring) is faster;
   // below, the register-ring kernel
-  if (MT >= 4 && plan.J == 2) {
-    launch_dma_part<2>(MT, grid, X, MTT, Wp, K, plan.ksplit, P, N, M, s);
+  if (MT >= 4) {
+    if (plan.J == 2) launch_dma_part<2>(MT, grid, X, MTT, Wp, K, plan.ksplit, P, N, M, s);
+    else launch_dma_part<1>(MT, grid, X, MTT, Wp, K, plan.ksplit, P, N, M, s);
     return;
   }
   if (plan.J == 2) launch_j<2, 0>(MT, grid, X, MTT, Wp, K, plan.ksplit, P, N, M, nullptr, s);
