@@ -420,29 +420,46 @@ __global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
 
 // Combine the splits of each (row, head) with log-sum-exp weights
 // 2^(m_s - m*).  A workgroup covers 8 rows of one head; a thread, 4 dims.
+// All splits' (m, l, O) are loaded up front (one round trip; splits <= 16).
+constexpr int A_MAX_SPLITS = 16;
+
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const int h = blockIdx.y, t = blockIdx.x * 8 + (threadIdx.x >> 5), i = (threadIdx.x & 31) * 4;
   if (t >= a.M) return;
   const int rows16 = (a.M + 15) & ~15;
+  float m[A_MAX_SPLITS], l[A_MAX_SPLITS];
+  f32x4 o[A_MAX_SPLITS];
+#pragma unroll
+  for (int s = 0; s < A_MAX_SPLITS; s++) {
+    if (s < a.splits) {
+      const size_t b = ((size_t)h * a.splits + s) * rows16 + t;
+      const float2 ml = *(const float2*)&a.part_ml[b * 2];
+      m[s] = ml.x;
+      l[s] = ml.y;
+      o[s] = *(const f32x4*)&a.part_o[b * A_DH + i];
+    }
+  }
   float mstar = -INFINITY;
-  for (int s = 0; s < a.splits; s++)
-    mstar = fmaxf(mstar, a.part_ml[(((size_t)h * a.splits + s) * rows16 + t) * 2]);
+#pragma unroll
+  for (int s = 0; s < A_MAX_SPLITS; s++)
+    if (s < a.splits) mstar = fmaxf(mstar, m[s]);
   float den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < a.splits; s++) {
-    const size_t b = ((size_t)h * a.splits + s) * rows16 + t;
-    const float m = a.part_ml[b * 2];
-    const float wgt = (m == -INFINITY) ? 0.f : exp2f(m - mstar);
-    den += wgt * a.part_ml[b * 2 + 1];
-    num += wgt * *(const f32x4*)&a.part_o[b * A_DH + i];
+#pragma unroll
+  for (int s = 0; s < A_MAX_SPLITS; s++) {
+    if (s < a.splits) {
+      const float wgt = (m[s] == -INFINITY) ? 0.f : exp2f(m[s] - mstar);
+      den += wgt * l[s];
+      num += wgt * o[s];
+    }
   }
   const float inv = 1.f / den;
   const int k = h * A_DH + i;
-  const size_t o = a.out_mtt ? frag_index(t, k, a.out_mtt) : (size_t)t * (a.H * A_DH) + k;
+  const size_t oi = a.out_mtt ? frag_index(t, k, a.out_mtt) : (size_t)t * (a.H * A_DH) + k;
   uint2 pk;
   pk.x = (uint32_t)f2bf(num[0] * inv) | ((uint32_t)f2bf(num[1] * inv) << 16);
   pk.y = (uint32_t)f2bf(num[2] * inv) | ((uint32_t)f2bf(num[3] * inv) << 16);
-  *(uint2*)&((uint16_t*)a.out)[o] = pk;
+  *(uint2*)&((uint16_t*)a.out)[oi] = pk;
 }
 
 constexpr int A_NBUF = 4;  // ring depth (chunks) of the bf16 kernel
@@ -456,7 +473,7 @@ int attn_bf16_splits(int H, int M, int max_ctx) {
   const int fill = (128 + H - 1) / H;
   if (s < fill) s = fill;
   if (s > max_chunks) s = max_chunks;
-  if (s > 16) s = 16;
+  if (s > A_MAX_SPLITS) s = A_MAX_SPLITS;
   return s < 1 ? 1 : s;
 }
 
