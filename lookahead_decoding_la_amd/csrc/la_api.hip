@@ -84,6 +84,8 @@ struct la_ctx {
   DevResult* res_dev = nullptr;
   float *x = nullptr, *logits = nullptr, *rope_cos = nullptr, *rope_sin = nullptr;
   float *gpart = nullptr, *attn_po = nullptr, *attn_pml = nullptr;
+  float* ssq = nullptr;  // bf16: per-row partial sums of squares (deferred RMSNorm)
+  int ssn = 1;
   void *xn = nullptr, *ffa = nullptr, *qb = nullptr;  // f32 path: row-major
   uint16_t *xnf = nullptr, *of = nullptr, *af = nullptr;  // bf16: fragment layout
   int MTT = 0;
@@ -195,6 +197,8 @@ size_t carve(la_ctx* c, void* base) {
     size_t rows16 = (size_t)g.n_heads * c->attn_splits * c->MR;
     c->attn_po = cv.take<float>(rows16 * dh);
     c->attn_pml = cv.take<float>(rows16 * 2);
+    c->ssq = cv.take<float>((size_t)c->MR * SSQ_STRIDE);
+    c->ssn = (d + SSQ_CHUNK - 1) / SSQ_CHUNK;
   } else {
     c->xn = cv.take<char>((size_t)c->MR * std::max(d, c->qdim) * c->elem);
     c->ffa = cv.take<char>((size_t)c->MR * F * c->elem);
@@ -281,6 +285,10 @@ void enqueue_layers(la_ctx* c, int M, int mode, hipStream_t s, Prof* pf = nullpt
     ea.out_act = c->qb;
     ea.k_cache = layer_k(c, l);
     ea.vt_cache = layer_v(c, l);
+    ea.ssq = c->ssq;
+    ea.ssn = c->ssn;
+    ea.dmodel = d;
+    ea.eps = g.rms_eps;
     if (c->bf16) {
       const uint16_t* next_norm =
           (const uint16_t*)(l + 1 < g.n_layers ? c->layers[l + 1].anorm : c->final_norm);
@@ -298,19 +306,23 @@ void enqueue_layers(la_ctx* c, int M, int mode, hipStream_t s, Prof* pf = nullpt
       launch_gemm_bf16(c->of, c->MTT, (const uint16_t*)L.wo, c->qdim, d, M, c->p_o, c->gpart, s);
       P_END();
       P_BEGIN(LA_PROF_REDUCE);
-      launch_red_resid_norm(c->gpart, c->p_o.ksplit, d, M, c->x, (const uint16_t*)L.fnorm,
-                            g.rms_eps, c->xnf, c->MTT, s);
+      launch_red_resid_scale(c->gpart, c->p_o.ksplit, d, M, c->x, (const uint16_t*)L.fnorm,
+                             c->xnf, c->MTT, c->ssq, s);
       P_END();
       P_BEGIN(LA_PROF_GATEUP);
       launch_gemm_bf16_swiglu(c->xnf, c->MTT, (const uint16_t*)L.wgu, d, 2 * F, M, c->p_gu.J,
-                              c->af, s);
+                              c->af, c->ssq, c->ssn, g.rms_eps, s);
       P_END();
       P_BEGIN(LA_PROF_DOWN);
       launch_gemm_bf16(c->af, c->MTT, (const uint16_t*)L.wd, F, d, M, c->p_d, c->gpart, s);
       P_END();
       P_BEGIN(LA_PROF_REDUCE);
-      launch_red_resid_norm(c->gpart, c->p_d.ksplit, d, M, c->x, next_norm, g.rms_eps, c->xnf,
-                            c->MTT, s);
+      if (l + 1 < g.n_layers)  // the next layer's QKV reduce applies the row scale
+        launch_red_resid_scale(c->gpart, c->p_d.ksplit, d, M, c->x, next_norm, c->xnf, c->MTT,
+                               c->ssq, s);
+      else  // the LM head takes fully normalized rows
+        launch_red_resid_norm(c->gpart, c->p_d.ksplit, d, M, c->x, next_norm, g.rms_eps,
+                              c->xnf, c->MTT, s);
       P_END();
     } else {
       P_BEGIN(LA_PROF_REDUCE);
@@ -381,7 +393,7 @@ void enqueue_step(la_ctx* c, hipStream_t s, Prof* pf = nullptr) {
   P_BEGIN(LA_PROF_OTHER);
   launch_assemble(MODE_STEP, c->st, c->win, c->pool_len, c->pool, nullptr, c->T, g.W, g.N, g.G,
                   c->tokens, c->relpos, c->st, c->emb, g.d_model, c->bf16, c->x,
-                  (const uint16_t*)c->layers[0].anorm, g.rms_eps, c->xnf, c->MTT, s);
+                  (const uint16_t*)c->layers[0].anorm, g.rms_eps, c->xnf, c->MTT, c->ssq, s);
   P_END();
   enqueue_layers(c, c->T, MODE_STEP, s, pf);
   enqueue_head(c, c->T, s, pf);
@@ -561,7 +573,7 @@ la_status la_prefill(la_ctx* c, const int32_t* prompt, int32_t n_prompt, const i
     LA_HIP(c, hipMemcpyAsync(c->prompt_buf, c->pin, sizeof(int32_t) * m, hipMemcpyHostToDevice, s));
     launch_assemble(MODE_CAUSAL, c->st, c->win, c->pool_len, c->pool, c->prompt_buf, m, g.W, g.N,
                     g.G, c->tokens, c->relpos, c->st, c->emb, g.d_model, c->bf16, c->x,
-                    (const uint16_t*)c->layers[0].anorm, g.rms_eps, c->xnf, c->MTT, s);
+                    (const uint16_t*)c->layers[0].anorm, g.rms_eps, c->xnf, c->MTT, c->ssq, s);
     enqueue_layers(c, m, MODE_CAUSAL, s);
     if (last) enqueue_head(c, m, s);
     launch_advance(c->st, m, c->amax, last ? 1 : 0, s);
@@ -655,7 +667,7 @@ la_status la_profile_kernel(la_ctx* c, int32_t klass, int32_t reps, float* us_pe
         break;
       case LA_PROF_GATEUP:
         launch_gemm_bf16_swiglu(c->xnf, c->MTT, (const uint16_t*)L.wgu, d, 2 * F, M, c->p_gu.J,
-                                c->af, s);
+                                c->af, c->ssq, c->ssn, g.rms_eps, s);
         break;
       default:
         launch_gemm_bf16(c->af, c->MTT, (const uint16_t*)L.wd, F, d, M, c->p_d, c->gpart, s);

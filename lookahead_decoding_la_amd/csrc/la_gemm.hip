@@ -166,7 +166,8 @@ __global__ __launch_bounds__(G_NW * 64) void k_gemm_bf16(
 template <int MT, int J, int OUT>
 __global__ __launch_bounds__(G_NW * 64) void k_gemm_dma(
     const uint16_t* __restrict__ X, int MTT, const uint16_t* __restrict__ Wp, int K,
-    int ksplit, float* __restrict__ P, int N, int M, uint16_t* __restrict__ A) {
+    int ksplit, float* __restrict__ P, int N, int M, uint16_t* __restrict__ A,
+    const float* __restrict__ ssq, int ssn, float eps) {
   constexpr int NF = J * MT;                   // activation fragments per stage
   constexpr int FPW = (NF + G_NW - 1) / G_NW;  // of them loaded per wave
   constexpr int LPS = J + FPW;                 // load instructions per thread per stage
@@ -236,25 +237,31 @@ __global__ __launch_bounds__(G_NW * 64) void k_gemm_dma(
     }
   } else {
     // wave 2i holds gate rows, wave 2i+1 the matching up rows (FFN tile
-    // 4*wt + i); the up values pass through the (idle) ring
+    // 4*wt + i); the up values pass through the (idle) ring.  The input
+    // rows were not normalized: both products take the row's 1/rms here.
     f32x4* ex = (f32x4*)lds;
+    float* invs = (float*)(lds + (G_NW / 2) * MT * 64 * 16);  // 1/rms of each token row
+    static_assert(OUT == 0 || D * STAGE >= (G_NW / 2) * MT * 64 * 16 + MT * 16 * 4, "LDS");
     lds_barrier();
+    if (tid < M) invs[tid] = row_inv_rms(ssq, ssn, tid, K, eps);
     if (w & 1) {
 #pragma unroll
       for (int m = 0; m < MT; m++) ex[((w >> 1) * MT + m) * 64 + l] = acc[m];
     }
-    lds_barrier();
+    __syncthreads();
     if (!(w & 1)) {
       const int j = (wt * (G_NW / 2) + (w >> 1)) * 16 + (l >> 4) * 4;
 #pragma unroll
       for (int m = 0; m < MT; m++) {
         const int t = m * 16 + (l & 15);
         if (t >= M) continue;
-        const f32x4 u = ex[((w >> 1) * MT + m) * 64 + l];
+        const float inv = invs[t];
+        const f32x4 u = ex[((w >> 1) * MT + m) * 64 + l] * inv;
+        const f32x4 gt = acc[m] * inv;
         const size_t o = frag_index(t, j, MTT);
         uint2 pk;
-        pk.x = (uint32_t)f2bf(silu(acc[m][0]) * u[0]) | ((uint32_t)f2bf(silu(acc[m][1]) * u[1]) << 16);
-        pk.y = (uint32_t)f2bf(silu(acc[m][2]) * u[2]) | ((uint32_t)f2bf(silu(acc[m][3]) * u[3]) << 16);
+        pk.x = (uint32_t)f2bf(silu(gt[0]) * u[0]) | ((uint32_t)f2bf(silu(gt[1]) * u[1]) << 16);
+        pk.y = (uint32_t)f2bf(silu(gt[2]) * u[2]) | ((uint32_t)f2bf(silu(gt[3]) * u[3]) << 16);
         *(uint2*)&A[o] = pk;
       }
     }
@@ -304,7 +311,7 @@ static void launch_dma_part(int MT, dim3 grid, const uint16_t* X, int MTT, const
 #define LA_GEMM_CASE(mt)                                                                     \
   case mt:                                                                                   \
     hipLaunchKernelGGL((k_gemm_dma<mt, J, 0>), grid, dim3(G_NW * 64), 0, s, X, MTT, Wp, K, ks, \
-                       P, N, M, nullptr);                                                    \
+                       P, N, M, nullptr, nullptr, 0, 0.f);                                   \
     break;
   switch (MT) {
     LA_GEMM_CASE(4) LA_GEMM_CASE(5) LA_GEMM_CASE(6) LA_GEMM_CASE(7)
@@ -333,11 +340,12 @@ void launch_gemm_bf16(const uint16_t* X, int MTT, const uint16_t* Wp, int K, int
 
 template <int J>
 static void launch_dma_swiglu(int MT, dim3 grid, const uint16_t* X, int MTT, const uint16_t* Wp,
-                              int K, int N, int M, uint16_t* A, hipStream_t s) {
+                              int K, int N, int M, uint16_t* A, const float* ssq, int ssn,
+                              float eps, hipStream_t s) {
 #define LA_GEMM_CASE(mt)                                                                    \
   case mt:                                                                                  \
     hipLaunchKernelGGL((k_gemm_dma<mt, J, 1>), grid, dim3(G_NW * 64), 0, s, X, MTT, Wp, K, 1, \
-                       nullptr, N, M, A);                                                   \
+                       nullptr, N, M, A, ssq, ssn, eps);                                    \
     break;
   switch (MT) {
     LA_GEMM_CASE(1) LA_GEMM_CASE(2) LA_GEMM_CASE(3) LA_GEMM_CASE(4)
@@ -350,11 +358,12 @@ static void launch_dma_swiglu(int MT, dim3 grid, const uint16_t* X, int MTT, con
 }
 
 void launch_gemm_bf16_swiglu(const uint16_t* X, int MTT, const uint16_t* Wp, int K, int N, int M,
-                             int J, uint16_t* A, hipStream_t s) {
+                             int J, uint16_t* A, const float* ssq, int ssn, float eps,
+                             hipStream_t s) {
   const int MT = (M + 15) / 16;
   dim3 grid(N / G_ROWS, 1);
-  if (J == 2) launch_dma_swiglu<2>(MT, grid, X, MTT, Wp, K, N, M, A, s);
-  else launch_dma_swiglu<1>(MT, grid, X, MTT, Wp, K, N, M, A, s);
+  if (J == 2) launch_dma_swiglu<2>(MT, grid, X, MTT, Wp, K, N, M, A, ssq, ssn, eps, s);
+  else launch_dma_swiglu<1>(MT, grid, X, MTT, Wp, K, N, M, A, ssq, ssn, eps, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -414,6 +423,12 @@ __global__ __launch_bounds__(256) void k_red_qkv(const float* __restrict__ P, in
       }
     }
   }
+  {
+    // the input rows were not normalized (deferred RMSNorm)
+    const float inv = row_inv_rms(ea.ssq, ea.ssn, tc, ea.dmodel, ea.eps);
+#pragma unroll
+    for (int e = 0; e < 16; e++) v[e] *= inv;
+  }
   if (!is_v) {
     // rotary angle of pair i (dims 2i, 2i+1 of the head) at pos
     const float* cs = ea.rope_cos + (size_t)pos * 64 + c0 / 2;
@@ -470,6 +485,48 @@ __device__ inline float block_sum(float v, float* sh) {
   for (int i = 0; i < (int)(blockDim.x >> 6); i++) t += sh[i];
   __syncthreads();
   return t;
+}
+
+// residual add; the next GEMM's input bf16(x * w) in fragment layout
+// (deferred RMSNorm) and this chunk's sum of squares.  Workgroup (c, t):
+// columns c*SSQ_CHUNK .. +SSQ_CHUNK of row t, 8 per thread.
+__global__ __launch_bounds__(SSQ_CHUNK / 8) void k_red_resid_scale(
+    const float* __restrict__ P, int ks, int d, int M, float* __restrict__ x,
+    const uint16_t* __restrict__ w, uint16_t* __restrict__ xnf, int MTT, float* __restrict__ ssq) {
+  __shared__ float sh[SSQ_CHUNK / 8 / 64];
+  const int c = blockIdx.x, t = blockIdx.y;
+  const int i = c * SSQ_CHUNK + threadIdx.x * 8;
+  float ss = 0.f;
+  if (i < d) {
+    float* xr = x + (size_t)t * d;
+    const uint4 wv = *(const uint4*)(w + i);
+    float v[8];
+    load8(xr + i, v);
+    for (int z = 0; z < ks; z++) {
+      float p[8];
+      load8(P + ((size_t)z * M + t) * d + i, p);
+#pragma unroll
+      for (int e = 0; e < 8; e++) v[e] += p[e];
+    }
+    *(float4*)(xr + i) = make_float4(v[0], v[1], v[2], v[3]);
+    *(float4*)(xr + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    const uint32_t wb[4] = {wv.x, wv.y, wv.z, wv.w};
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      ss = fmaf(v[e], v[e], ss);
+      o[e] = v[e] * bf2f((uint16_t)(wb[e >> 1] >> ((e & 1) * 16)));
+    }
+    *(uint4*)&xnf[frag_index(t, i, MTT)] = pack8(o);
+  }
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float tot = 0.f;
+    for (int q = 0; q < SSQ_CHUNK / 8 / 64; q++) tot += sh[q];
+    ssq[t * SSQ_STRIDE + c] = tot;
+  }
 }
 
 // residual add + RMSNorm of the new row into fragment-layout bf16; one
@@ -546,6 +603,11 @@ __global__ __launch_bounds__(256) void k_red_swiglu(const float* __restrict__ P,
 void launch_red_qkv(const float* P, int ks, int N, int M, const EpiArgs& ea, hipStream_t s) {
   hipLaunchKernelGGL(k_red_qkv, dim3(N / 128, (M + RQ_TOK - 1) / RQ_TOK), dim3(256), 0, s, P, ks,
                      N, M, ea);
+}
+void launch_red_resid_scale(const float* P, int ks, int d, int M, float* x, const uint16_t* w,
+                            uint16_t* xnf, int MTT, float* ssq, hipStream_t s) {
+  hipLaunchKernelGGL(k_red_resid_scale, dim3((d + SSQ_CHUNK - 1) / SSQ_CHUNK, M),
+                     dim3(SSQ_CHUNK / 8), 0, s, P, ks, d, M, x, w, xnf, MTT, ssq);
 }
 void launch_red_resid_norm(const float* P, int ks, int d, int M, float* x, const uint16_t* w,
                            float eps, uint16_t* xnf, int MTT, hipStream_t s) {

@@ -148,7 +148,22 @@ struct EpiArgs {
   const float* rope_cos; // [max_ctx][dh/2]
   const float* rope_sin;
   int qdim, kvdim, dh, max_ctx, ld_out;
+  const float* ssq;      // bf16 QKV: per-row partial sums of squares of the
+  int ssn, dmodel;       //   un-normalized input [rows][8] (ssn used), so
+  float eps;             //   outputs are scaled by the row's 1/rms here
 };
+
+// Deferred RMSNorm.  A GEMM input written as bf16(x * w) (norm weight w,
+// without the row's 1/rms) gives outputs that the consumer scales by
+// row_inv_rms: the row scale commutes with the product.  ssq[t][0..ssn)
+// hold partial sums of x^2 over column chunks, summed in chunk order.
+constexpr int SSQ_STRIDE = 8;
+constexpr int SSQ_CHUNK = 1024;  // columns per partial sum
+__device__ inline float row_inv_rms(const float* ssq, int ssn, int t, int d, float eps) {
+  float s = 0.f;
+  for (int i = 0; i < ssn; i++) s += ssq[t * SSQ_STRIDE + i];
+  return 1.f / sqrtf(s / (float)d + eps);
+}
 
 // ---------------------------------------------------------------------------
 // host launchers (one per kernel family)
@@ -172,9 +187,15 @@ void launch_gemm_bf16(const uint16_t* X, int MTT, const uint16_t* Wp, int K, int
 // Fused gate/up (alternating 16-row gate / up tiles, no K split) with the
 // SwiGLU written to fragment-layout A (FFN width N/2).
 void launch_gemm_bf16_swiglu(const uint16_t* X, int MTT, const uint16_t* Wp, int K, int N, int M,
-                             int J, uint16_t* A, hipStream_t s);
+                             int J, uint16_t* A, const float* ssq, int ssn, float eps,
+                             hipStream_t s);
 // reduce kernels (sum K splits in order + epilogue)
 void launch_red_qkv(const float* P, int ks, int N, int M, const EpiArgs& ea, hipStream_t s);
+// residual add; next GEMM input bf16(x * w) in fragment layout and the
+// row's partial sums of squares (deferred RMSNorm), one workgroup per
+// SSQ_CHUNK columns of a row
+void launch_red_resid_scale(const float* P, int ks, int d, int M, float* x, const uint16_t* w,
+                            uint16_t* xnf, int MTT, float* ssq, hipStream_t s);
 void launch_red_resid_norm(const float* P, int ks, int d, int M, float* x, const uint16_t* w,
                            float eps, uint16_t* xnf, int MTT, hipStream_t s);
 void launch_red_swiglu(const float* P, int ks, int F, int M, uint16_t* af, int MTT,
@@ -216,7 +237,7 @@ void launch_assemble(int mode, const DevState* st, const int32_t* win,
                      int32_t* tokens, int32_t* relpos, DevState* st_w,
                      const void* emb, int d, int bf16, float* x,
                      const uint16_t* nw, float eps, uint16_t* xnf, int MTT,
-                     hipStream_t s);
+                     float* ssq, hipStream_t s);
 void launch_rmsnorm(const float* x, const void* w, int M, int d, float eps,
                     int bf16, void* out, hipStream_t s);
 void launch_argmax(const float* logits, int M, int V, int32_t* amax,

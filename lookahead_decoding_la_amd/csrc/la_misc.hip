@@ -41,7 +41,7 @@ __global__ void k_assemble(int mode, const DevState* __restrict__ st,
                            int W, int N, int G, int32_t* tokens, int32_t* relpos,
                            DevState* st_w, const void* __restrict__ emb, int d, int bf16,
                            float* __restrict__ x, const uint16_t* __restrict__ nw, float eps,
-                           uint16_t* __restrict__ xnf, int MTT) {
+                           uint16_t* __restrict__ xnf, int MTT, float* __restrict__ ssq) {
   __shared__ float sh[4];
   const int r = blockIdx.x;
   int tok, rp;
@@ -96,7 +96,11 @@ __global__ void k_assemble(int mode, const DevState* __restrict__ st,
     if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = ss;
     __syncthreads();
     ss = sh[0] + sh[1] + sh[2] + sh[3];
-    const float inv = 1.f / sqrtf(ss / (float)d + eps);
+    // deferred RMSNorm: the GEMM input is bf16(x * w); the consumers scale
+    // by 1/rms from the row's sum of squares (here in one piece)
+    if (threadIdx.x < SSQ_STRIDE) ssq[r * SSQ_STRIDE + threadIdx.x] = threadIdx.x == 0 ? ss : 0.f;
+    const float inv = 1.f;
+    (void)eps;
 #pragma unroll
     for (int it = 0; it < 4; it++) {
       const int i = (it * 256 + threadIdx.x) * 8;
@@ -122,9 +126,11 @@ void launch_assemble(int mode, const DevState* st, const int32_t* win,
                      const int32_t* pool_len, const int32_t* pool, const int32_t* prompt,
                      int M, int W, int N, int G, int32_t* tokens, int32_t* relpos,
                      DevState* st_w, const void* emb, int d, int bf16, float* x,
-                     const uint16_t* nw, float eps, uint16_t* xnf, int MTT, hipStream_t s) {
+                     const uint16_t* nw, float eps, uint16_t* xnf, int MTT, float* ssq,
+                     hipStream_t s) {
   hipLaunchKernelGGL(k_assemble, dim3(M), dim3(256), 0, s, mode, st, win, pool_len, pool,
-                     prompt, W, N, G, tokens, relpos, st_w, emb, d, bf16, x, nw, eps, xnf, MTT);
+                     prompt, W, N, G, tokens, relpos, st_w, emb, d, bf16, x, nw, eps, xnf, MTT,
+                     ssq);
 }
 
 // ---------------------------------------------------------------------------
