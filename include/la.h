@@ -118,6 +118,18 @@ la_status la_prefill(la_ctx *c, const int32_t *prompt, int32_t n_prompt,
  * (kv_len + step rows > max_ctx), LA_ERR_INVALID_ARG (out NULL), LA_ERR_HIP. */
 la_status la_step(la_ctx *c, la_step_result *out);
 
+/* Seed the n-gram pool with every N-gram of a token sequence (host int32
+ * [n], ids < vocab), in position order: key seq[p], tail seq[p+1 .. p+N-1]
+ * for p = 0 .. n-N, each inserted with the pool's policy (distinct tails per
+ * key, a repeat moves to the newest slot, the oldest of G is evicted).
+ * "Break the Sequential Dependency of LLM Inference Using Lookahead
+ * Decoding", Key points, "Ablation": n-grams taken from the prompt raise
+ * the speedup.  Call after la_prefill (which empties the pool), typically
+ * with the prompt.  Blocks until done.
+ * Errors: LA_ERR_INVALID_ARG, LA_ERR_STATE (before prefill or poisoned),
+ * LA_ERR_HIP. */
+la_status la_seed_pool(la_ctx *c, const int32_t *seq, int32_t n);
+
 /* Destroy a context (NULL is fine).  Waits for the context's queued work. */
 la_status la_destroy(la_ctx *c);
 

@@ -29,7 +29,7 @@ EXPORTS = [
     "la_debug_block", "la_debug_window", "la_debug_pool",
     "la_debug_pool_insert", "la_debug_kv", "la_debug_state",
     "la_attention_workspace_bytes", "la_attention", "la_profile_step",
-    "la_profile_kernel",
+    "la_profile_kernel", "la_seed_pool",
 ]
 
 PROF_CLASSES = ["qkv", "attention", "o_proj", "gate_up", "down", "lm_head",
@@ -93,6 +93,7 @@ def lib():
                                        I32, P, SZ, P]),
             "la_profile_step": (C.c_int, [P, pf, pi, C.POINTER(LaStepResult)]),
             "la_profile_kernel": (C.c_int, [P, I32, I32, pf]),
+            "la_seed_pool": (C.c_int, [P, pi, I32]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -209,6 +210,13 @@ class LookaheadDecoder:
                    accepted=int(r.accepted), winner=int(r.winner),
                    n_candidates=int(r.n_candidates), kv_len=int(r.kv_len))
         return res, {c: (float(ms[i]), int(n[i])) for i, c in enumerate(PROF_CLASSES)}
+
+    def seed_pool(self, seq) -> None:
+        """Insert every N-gram of seq (e.g. the prompt) into the pool, in
+        position order; call after prefill."""
+        a = np.ascontiguousarray(np.asarray(seq, dtype=np.int32))
+        self._check(lib().la_seed_pool(self._h, a.ctypes.data_as(C.POINTER(C.c_int32)), len(a)),
+                    "la_seed_pool")
 
     def profile_kernel(self, klass: str, reps: int = 32) -> float:
         """Mean microseconds per launch of one kernel class (layer 0's), from

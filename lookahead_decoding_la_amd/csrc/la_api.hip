@@ -745,6 +745,30 @@ la_status la_debug_pool(la_ctx* c, int32_t* len, int32_t* tails) {
   return LA_OK;
 }
 
+la_status la_seed_pool(la_ctx* c, const int32_t* seq, int32_t n) {
+  la_status us = check_usable(c);
+  if (us != LA_OK) return us;
+  const la_config& g = c->cfg;
+  if (n < 0 || (n > 0 && !seq)) return fail(c, LA_ERR_INVALID_ARG, "seq/n");
+  for (int i = 0; i < n; i++)
+    if (seq[i] < 0 || seq[i] >= g.vocab) return fail(c, LA_ERR_INVALID_ARG, "token out of range");
+  if (!c->prefilled) return fail(c, LA_ERR_STATE, "la_seed_pool before la_prefill");
+  const int n1 = g.N - 1;
+  if (g.G == 0 || n <= n1) return LA_OK;
+  LA_HIP(c, hipStreamSynchronize(c->stream));
+  // chunks of MR tokens overlapping by N-1, so every n-gram lies in one chunk
+  for (int p0 = 0; p0 + n1 < n; p0 += c->MR - n1) {
+    const int m = std::min(c->MR, n - p0);
+    memcpy(c->pin, seq + p0, sizeof(int32_t) * m);
+    LA_HIP(c, hipMemcpyAsync(c->prompt_buf, c->pin, sizeof(int32_t) * m, hipMemcpyHostToDevice,
+                             c->stream));
+    launch_seed_pool(c->prompt_buf, m, c->pool_len, c->pool, g.N, g.G, c->stream);
+    LA_HIP(c, hipGetLastError());
+    LA_HIP(c, hipStreamSynchronize(c->stream));
+  }
+  return LA_OK;
+}
+
 la_status la_debug_pool_insert(la_ctx* c, int32_t key, const int32_t* tail) {
   la_status us = check_usable(c);
   if (us != LA_OK) return us;

@@ -250,6 +250,9 @@ void launch_kv_compact(const DevState* st, int n_layers, int Hkv, int dh,
                        void* vt_cache, hipStream_t s);
 void launch_advance(DevState* st, int M, const int32_t* amax, int set_cur,
                     hipStream_t s);
+// insert every N-gram of the device sequence seq[0..m), in position order
+void launch_seed_pool(const int32_t* seq_dev, int m, int32_t* pool_len, int32_t* pool, int N,
+                      int G, hipStream_t s);
 void launch_pool_insert(DevState* st, int32_t key, const int32_t* tail_dev,
                         int32_t* pool_len, int32_t* pool, int N, int G,
                         hipStream_t s);

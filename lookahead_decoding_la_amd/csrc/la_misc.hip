@@ -269,6 +269,20 @@ __global__ void k_pool_insert(int32_t key, const int32_t* tail, int32_t* pool_le
   if (threadIdx.x == 0) pool_insert_serial(pool_len, pool, N, G, key, tail);
 }
 
+// Every N-gram of seq[0..m) in position order: key seq[p], tail
+// seq[p+1 .. p+N-1] ("Key points", "Ablation": n-grams from the prompt in
+// the pool).  One lane: inserts are strictly sequential.
+__global__ void k_seed_pool(const int32_t* seq, int m, int32_t* pool_len, int32_t* pool, int N,
+                            int G) {
+  if (threadIdx.x != 0) return;
+  for (int p = 0; p + N - 1 < m; p++) pool_insert_serial(pool_len, pool, N, G, seq[p], seq + p + 1);
+}
+
+void launch_seed_pool(const int32_t* seq_dev, int m, int32_t* pool_len, int32_t* pool, int N,
+                      int G, hipStream_t s) {
+  hipLaunchKernelGGL(k_seed_pool, dim3(1), dim3(64), 0, s, seq_dev, m, pool_len, pool, N, G);
+}
+
 void launch_pool_insert(DevState*, int32_t key, const int32_t* tail_dev, int32_t* pool_len,
                         int32_t* pool, int N, int G, hipStream_t s) {
   hipLaunchKernelGGL(k_pool_insert, dim3(1), dim3(64), 0, s, key, tail_dev, pool_len, pool, N, G);

@@ -77,6 +77,7 @@ def lib():
             "orc_step": (I, [P, C.POINTER(_Res), D]),
             "orc_greedy_next": (I, [P, D]),
             "orc_pool_insert": (None, [P, C.c_int32, I32]),
+            "orc_seed_pool": (I, [P, I32, I]),
             "orc_get_window": (None, [P, I32]),
             "orc_set_window": (None, [P, I32]),
             "orc_set_current": (None, [P, C.c_int32]),
@@ -201,6 +202,12 @@ class Oracle:
         a, p = _i32(tail)
         lib().orc_pool_insert(self._h, int(key), p)
 
+    def seed_pool(self, seq) -> None:
+        """Insert every N-gram of seq into the pool, in position order."""
+        a, p = _i32(seq)
+        if lib().orc_seed_pool(self._h, p, len(a)) != 0:
+            raise ValueError("bad token sequence")
+
     def kv(self, layer: int, pos0: int, n: int):
         c = self.cfg
         k = np.zeros((c.n_kv_heads, n, c.head_dim), np.float64)
@@ -277,9 +284,12 @@ class Oracle:
         return (int(t), lg[0]) if logits else int(t)
 
     # -- whole runs -------------------------------------------------------
-    def generate(self, prompt, init_window, M: int):
-        """Lookahead decoding of M tokens (the prefill's token included)."""
+    def generate(self, prompt, init_window, M: int, seed_prompt: bool = False):
+        """Lookahead decoding of M tokens (the prefill's token included);
+        seed_prompt: the pool starts with the prompt's n-grams."""
         out = [self.prefill(prompt, init_window)]
+        if seed_prompt:
+            self.seed_pool(prompt)
         steps = []
         while len(out) < M:
             r = self.step()

@@ -511,6 +511,20 @@ int orc_extend(orc *o, const int32_t *seq, int n, double *logits_all) {
  * token, returned), install the initial window (N-1 levels x W, level 1
  * first; reading: the window starts full, no warm-up) and empty the pool.
  */
+/* Seed the pool with every N-gram of a token sequence, in position order:
+ * key seq[p], tail seq[p+1 .. p+N-1], for p = 0 .. n-N, each inserted with
+ * the pool's policy (Key points, "Ablation": adding n-grams taken from the
+ * prompt to the pool raises the speedup; reading: all prompt n-grams, in
+ * order).  Returns 0, or -1 for a bad argument. */
+int orc_seed_pool(orc *o, const int32_t *seq, int n) {
+  const int n1 = o->c.N - 1;
+  if (n < 0 || (n > 0 && !seq)) return -1;
+  for (int i = 0; i < n; i++)
+    if (seq[i] < 0 || seq[i] >= o->c.vocab) return -1;
+  for (int p = 0; p + n1 < n; p++) orc_pool_insert(o, seq[p], seq + p + 1);
+  return 0;
+}
+
 int orc_prefill(orc *o, const int32_t *prompt, int n, const int32_t *init_window,
                 double *logits_all) {
   const orc_config *c = &o->c;

@@ -48,6 +48,16 @@ class Lockstep:
             self.orc.set_current(fg)
         return fg
 
+    def seed(self, seq):
+        """Seed both pools with the n-grams of seq; the pools must agree."""
+        self.dev.seed_pool(seq)
+        self.orc.seed_pool(seq)
+        lg_len, lg_tails = self.dev.debug_pool()
+        lo_len, lo_tails = self.orc.pool()
+        assert np.array_equal(lg_len, lo_len)
+        for key in np.nonzero(lo_len)[0]:
+            assert np.array_equal(lg_tails[key][:lo_len[key]], lo_tails[key][:lo_len[key]])
+
     def step(self):
         cfg = self.cfg
         rg = self.dev.step()

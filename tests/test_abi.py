@@ -67,6 +67,10 @@ def test_calls_on_null_context():
     assert lib.la_destroy(None) == la.LA_OK
     assert lib.la_step_rows(None) == 0
     assert lib.la_status_string(la.LA_ERR_STATE) == b"invalid state"
+    toks = (C.c_int32 * 4)(1, 2, 3, 4)
+    assert lib.la_seed_pool(None, toks, 4) == la.LA_ERR_INVALID_ARG
+    us = C.c_float()
+    assert lib.la_profile_kernel(None, 3, 8, C.byref(us)) == la.LA_ERR_INVALID_ARG
 
 
 def test_attention_argument_checks_without_gpu():

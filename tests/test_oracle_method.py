@@ -257,3 +257,15 @@ def test_window_shift_and_pool_update(tiny):
         for key in range(cfg.vocab):
             assert ln[key] == len(model.get(key, []))
             assert [list(map(int, t)) for t in tl[key][:ln[key]]] == model.get(key, [])
+
+
+def test_prompt_seeded_pool_keeps_greedy_output(tiny):
+    """With the pool seeded from the prompt (Key points, "Ablation") the
+    output is still plain greedy decoding: seeding changes which candidates
+    are verified, never what is emitted."""
+    cfg, w, p, win = tiny
+    M = 48
+    ref = oracle.Oracle(cfg, w, 256).greedy(p, M)
+    toks, steps = oracle.Oracle(cfg, w, 256).generate(p, win, M, seed_prompt=True)
+    assert toks == ref
+    assert all(1 <= s["n_emitted"] <= cfg.N for s in steps)

@@ -56,3 +56,27 @@ def test_random_streams_match_list_model(G, N):
         lst.append(tail)
         if it % 50 == 49:
             assert _lists(cfg, o) == {k: v for k, v in model.items() if v}
+
+
+def test_seed_pool_hand_worked():
+    """Prompt n-gram seeding (Key points, "Ablation"): every N-gram of the
+    sequence in position order, with the pool's policy.  Worked by hand for
+    N = 3, G = 2 over 5 6 7 5 6 8 5 6 7: the n-grams keyed 5 are (6 7),
+    (6 8), (6 7) again, which moves to the newest slot."""
+    cfg, o = _ctx(2, 3)
+    o.prefill([1, 2], np.zeros((2, 2), np.int32))
+    o.seed_pool([5, 6, 7, 5, 6, 8, 5, 6, 7])
+    assert _lists(cfg, o) == {5: [[6, 8], [6, 7]], 6: [[7, 5], [8, 5]],
+                              7: [[5, 6]], 8: [[5, 6]]}
+
+
+def test_seed_pool_equals_explicit_inserts():
+    cfg, o = _ctx(3, 4, vocab=6)
+    cfg2, o2 = _ctx(3, 4, vocab=6)
+    seq = [int(x) for x in np.random.default_rng(3).integers(0, 6, size=200)]
+    o.seed_pool(seq)
+    for p in range(len(seq) - 3):
+        o2.pool_insert(seq[p], seq[p + 1:p + 4])
+    assert _lists(cfg, o) == _lists(cfg2, o2)
+    with pytest.raises(ValueError):
+        o.seed_pool([0, 1, 99])
