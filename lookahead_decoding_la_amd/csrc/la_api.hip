@@ -85,6 +85,7 @@ struct la_ctx {
   float *x = nullptr, *logits = nullptr, *rope_cos = nullptr, *rope_sin = nullptr;
   float *gpart = nullptr, *attn_po = nullptr, *attn_pml = nullptr;
   float* ssq = nullptr;  // bf16: per-row partial sums of squares (deferred RMSNorm)
+  float* rope_rows = nullptr;  // bf16: per block row cos[64], sin[64]
   int ssn = 1;
   void *xn = nullptr, *ffa = nullptr, *qb = nullptr;  // f32 path: row-major
   uint16_t *xnf = nullptr, *of = nullptr, *af = nullptr;  // bf16: fragment layout
@@ -198,6 +199,7 @@ size_t carve(la_ctx* c, void* base) {
     c->attn_po = cv.take<float>(rows16 * dh);
     c->attn_pml = cv.take<float>(rows16 * 2);
     c->ssq = cv.take<float>((size_t)c->MR * SSQ_STRIDE);
+    c->rope_rows = cv.take<float>((size_t)c->MR * 128);
     c->ssn = (d + SSQ_CHUNK - 1) / SSQ_CHUNK;
   } else {
     c->xn = cv.take<char>((size_t)c->MR * std::max(d, c->qdim) * c->elem);
@@ -286,6 +288,7 @@ void enqueue_layers(la_ctx* c, int M, int mode, hipStream_t s, Prof* pf = nullpt
     ea.k_cache = layer_k(c, l);
     ea.vt_cache = layer_v(c, l);
     ea.ssq = c->ssq;
+    ea.rope_rows = c->rope_rows;
     ea.ssn = c->ssn;
     ea.dmodel = d;
     ea.eps = g.rms_eps;
@@ -393,7 +396,8 @@ void enqueue_step(la_ctx* c, hipStream_t s, Prof* pf = nullptr) {
   P_BEGIN(LA_PROF_OTHER);
   launch_assemble(MODE_STEP, c->st, c->win, c->pool_len, c->pool, nullptr, c->T, g.W, g.N, g.G,
                   c->tokens, c->relpos, c->st, c->emb, g.d_model, c->bf16, c->x,
-                  (const uint16_t*)c->layers[0].anorm, g.rms_eps, c->xnf, c->MTT, c->ssq, s);
+                  (const uint16_t*)c->layers[0].anorm, g.rms_eps, c->xnf, c->MTT, c->ssq,
+                  c->rope_cos, c->rope_sin, c->rope_rows, s);
   P_END();
   enqueue_layers(c, c->T, MODE_STEP, s, pf);
   enqueue_head(c, c->T, s, pf);
@@ -573,7 +577,8 @@ la_status la_prefill(la_ctx* c, const int32_t* prompt, int32_t n_prompt, const i
     LA_HIP(c, hipMemcpyAsync(c->prompt_buf, c->pin, sizeof(int32_t) * m, hipMemcpyHostToDevice, s));
     launch_assemble(MODE_CAUSAL, c->st, c->win, c->pool_len, c->pool, c->prompt_buf, m, g.W, g.N,
                     g.G, c->tokens, c->relpos, c->st, c->emb, g.d_model, c->bf16, c->x,
-                    (const uint16_t*)c->layers[0].anorm, g.rms_eps, c->xnf, c->MTT, c->ssq, s);
+                    (const uint16_t*)c->layers[0].anorm, g.rms_eps, c->xnf, c->MTT, c->ssq,
+                  c->rope_cos, c->rope_sin, c->rope_rows, s);
     enqueue_layers(c, m, MODE_CAUSAL, s);
     if (last) enqueue_head(c, m, s);
     launch_advance(c->st, m, c->amax, last ? 1 : 0, s);

@@ -405,7 +405,6 @@ __global__ __launch_bounds__(256) void k_red_qkv(const float* __restrict__ P, in
   const int L = ea.st->L;
   const bool is_v = cb * 128 >= ea.qdim + ea.kvdim;
   const int tc = min(t, M - 1);  // rows past M repeat a valid row, never stored
-  const int pos = L + ea.relpos[tc];
   float v[16];
   {
     const float* pr = P + (size_t)tc * N + n0;
@@ -431,8 +430,8 @@ __global__ __launch_bounds__(256) void k_red_qkv(const float* __restrict__ P, in
   }
   if (!is_v) {
     // rotary angle of pair i (dims 2i, 2i+1 of the head) at pos
-    const float* cs = ea.rope_cos + (size_t)pos * 64 + c0 / 2;
-    const float* sn = ea.rope_sin + (size_t)pos * 64 + c0 / 2;
+    const float* cs = ea.rope_rows + (size_t)tc * 128 + c0 / 2;
+    const float* sn = cs + 64;
     uint16_t o[16];
 #pragma unroll
     for (int e = 0; e < 8; e++) {

@@ -148,6 +148,8 @@ struct EpiArgs {
   const float* rope_cos; // [max_ctx][dh/2]
   const float* rope_sin;
   int qdim, kvdim, dh, max_ctx, ld_out;
+  const float* rope_rows;  // bf16 QKV: per block row, cos[64] then sin[64] at
+                           // the row's absolute position (written by assembly)
   const float* ssq;      // bf16 QKV: per-row partial sums of squares of the
   int ssn, dmodel;       //   un-normalized input [rows][8] (ssn used), so
   float eps;             //   outputs are scaled by the row's 1/rms here
@@ -237,7 +239,8 @@ void launch_assemble(int mode, const DevState* st, const int32_t* win,
                      int32_t* tokens, int32_t* relpos, DevState* st_w,
                      const void* emb, int d, int bf16, float* x,
                      const uint16_t* nw, float eps, uint16_t* xnf, int MTT,
-                     float* ssq, hipStream_t s);
+                     float* ssq, const float* rope_cos, const float* rope_sin,
+                     float* rope_rows, hipStream_t s);
 void launch_rmsnorm(const float* x, const void* w, int M, int d, float eps,
                     int bf16, void* out, hipStream_t s);
 void launch_argmax(const float* logits, int M, int V, int32_t* amax,

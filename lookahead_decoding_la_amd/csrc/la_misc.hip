@@ -41,7 +41,9 @@ __global__ void k_assemble(int mode, const DevState* __restrict__ st,
                            int W, int N, int G, int32_t* tokens, int32_t* relpos,
                            DevState* st_w, const void* __restrict__ emb, int d, int bf16,
                            float* __restrict__ x, const uint16_t* __restrict__ nw, float eps,
-                           uint16_t* __restrict__ xnf, int MTT, float* __restrict__ ssq) {
+                           uint16_t* __restrict__ xnf, int MTT, float* __restrict__ ssq,
+                           const float* __restrict__ rope_cos, const float* __restrict__ rope_sin,
+                           float* __restrict__ rope_rows) {
   __shared__ float sh[4];
   const int r = blockIdx.x;
   int tok, rp;
@@ -65,6 +67,14 @@ __global__ void k_assemble(int mode, const DevState* __restrict__ st,
   }
   float* xr = x + (size_t)r * d;
   if (bf16) {
+    // this row's rotary factors (head_dim 128: 64 pairs), gathered once per
+    // block for every layer's QKV reduce
+    if (threadIdx.x < 128) {
+      const size_t pos = (size_t)(st->L + rp);
+      const int i = threadIdx.x & 63;
+      rope_rows[r * 128 + threadIdx.x] =
+          threadIdx.x < 64 ? rope_cos[pos * 64 + i] : rope_sin[pos * 64 + i];
+    }
     // 8 columns per thread per pass (d % 128 == 0 for the bf16 kernels,
     // d <= 8192: at most 4 passes of 256 threads); the row stays in
     // registers between the sum of squares and the scaling
@@ -127,10 +137,11 @@ void launch_assemble(int mode, const DevState* st, const int32_t* win,
                      int M, int W, int N, int G, int32_t* tokens, int32_t* relpos,
                      DevState* st_w, const void* emb, int d, int bf16, float* x,
                      const uint16_t* nw, float eps, uint16_t* xnf, int MTT, float* ssq,
+                     const float* rope_cos, const float* rope_sin, float* rope_rows,
                      hipStream_t s) {
   hipLaunchKernelGGL(k_assemble, dim3(M), dim3(256), 0, s, mode, st, win, pool_len, pool,
                      prompt, W, N, G, tokens, relpos, st_w, emb, d, bf16, x, nw, eps, xnf, MTT,
-                     ssq);
+                     ssq, rope_cos, rope_sin, rope_rows);
 }
 
 // ---------------------------------------------------------------------------
@@ -330,24 +341,32 @@ __global__ __launch_bounds__(64) void k_verify(DevState* st, const int32_t* __re
   __shared__ int32_t lwin[256];             // window, (N-1) x W <= 255
   __shared__ int32_t tail[32];
   __shared__ int32_t lkey[256], lslot[256], llen[256];
+  __shared__ int32_t ltok[256], lamax[256];  // the block's tokens and row argmax
   __shared__ int32_t llist[POOL_LDS_INTS];
   const int lane = threadIdx.x;
   const int n1 = N - 1;
   const int nwin = n1 * W;
-  const int nc = st->n_cand;
-  const int a0 = amax[0];
+  const int T = 1 + (W + G) * n1;
   const int per = G * n1;  // ints per key list
   const bool staged = G > 0 && W > 0 && W * per <= POOL_LDS_INTS;
+  // every global read that does not depend on another goes out first
+  for (int i = lane; i < T; i += 64) {
+    ltok[i] = tokens[i];
+    lamax[i] = amax[i];
+  }
   for (int i = lane; i < nwin; i += 64) lwin[i] = win[i];
-  for (int j = lane; j < W; j += 64) ynew[j] = amax[1 + (n1 - 1) * W + j];
+  const int nc = st->n_cand;
+  __syncthreads();
+  const int a0 = lamax[0];
+  for (int j = lane; j < W; j += 64) ynew[j] = lamax[1 + (n1 - 1) * W + j];
   // per-candidate accepted length, reduced to (max k, lowest g)
   int bk = -1, bg = 0x7fffffff;
   for (int g = lane; g < nc; g += 64) {
     const int base = 1 + nwin + g * n1;  // row (g, 1)
     int k = 0;
     while (k < n1) {
-      const int pred = k == 0 ? a0 : amax[base + k - 1];
-      if (tokens[base + k] != pred) break;
+      const int pred = k == 0 ? a0 : lamax[base + k - 1];
+      if (ltok[base + k] != pred) break;
       k++;
     }
     if (k > bk || (k == bk && g < bg)) { bk = k; bg = g; }
@@ -358,10 +377,16 @@ __global__ __launch_bounds__(64) void k_verify(DevState* st, const int32_t* __re
   }
   __syncthreads();
   if (staged) {
+    // lists are read whole (entries past the length are never used), so
+    // the lengths and the lists load together
     for (int j = lane; j < W; j += 64) {
       const int key = lwin[j];
       lkey[j] = key;
       llen[j] = pool_len[key];
+    }
+    for (int idx = lane; idx < W * per; idx += 64) {
+      const int j = idx / per, rem = idx - j * per;
+      llist[idx] = pool[(size_t)lwin[j] * per + rem];
     }
     __syncthreads();
     for (int j = lane; j < W; j += 64) {
@@ -370,18 +395,14 @@ __global__ __launch_bounds__(64) void k_verify(DevState* st, const int32_t* __re
         if (lkey[q] == lkey[j]) { sl = q; break; }
       lslot[j] = sl;
     }
-    for (int idx = lane; idx < W * per; idx += 64) {
-      const int j = idx / per, rem = idx - j * per;
-      if (rem < llen[j] * n1) llist[idx] = pool[(size_t)lkey[j] * per + rem];
-    }
     __syncthreads();
   }
   if (lane == 0) {
     const int k = nc > 0 ? bk : 0;
     const int gs = nc > 0 ? bg : -1;
     const int base = 1 + nwin + (gs < 0 ? 0 : gs) * n1;
-    for (int i = 0; i < k; i++) res->tokens[i] = tokens[base + i];
-    const int bonus = k == 0 ? a0 : amax[base + k - 1];
+    for (int i = 0; i < k; i++) res->tokens[i] = ltok[base + i];
+    const int bonus = k == 0 ? a0 : lamax[base + k - 1];
     res->tokens[k] = bonus;
     for (int i = k + 1; i < 32; i++) res->tokens[i] = 0;
     res->n_emitted = k + 1;
