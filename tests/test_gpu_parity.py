@@ -25,6 +25,8 @@ FP32 = [
     lasynth.get_config("tiny", name="tiny_lookahead_only", W=4, G=0),
     lasynth.get_config("tiny", name="tiny_gqa_n5", n_heads=4, n_kv_heads=2, N=5, W=3, G=4),
     lasynth.get_config("tiny", name="tiny_plain", W=0, G=0),
+    # the largest step the kernels take: 1 + (26 + 25) * 5 = 256 rows
+    lasynth.get_config("tiny", name="tiny_t256", N=6, W=26, G=25, gen_tokens=48),
 ]
 
 
@@ -34,12 +36,12 @@ def test_fp32_lockstep(cfg):
     p = lasynth.make_prompt(cfg)
     win = lasynth.make_init_window(cfg, p) if cfg.W else None
     log(f"[fp32 lockstep] {cfg.name} T={cfg.T}")
-    ls = Lockstep(cfg, w, 256, logit_tol=1e-4, tie_margin=2e-4)
+    ls = Lockstep(cfg, w, 512, logit_tol=1e-4, tie_margin=2e-4)
     toks = ls.run(p, win, M=cfg.gen_tokens)
     ls.compare_kv(1e-4)
     log(f"  steps={len(ls.steps)} max|dlogit|={ls.max_diff:.2e} ties={ls.ties}")
     # and the output is plain greedy decoding
-    assert toks[:cfg.gen_tokens] == oracle.Oracle(cfg, w, 256).greedy(p, cfg.gen_tokens) or ls.ties
+    assert toks[:cfg.gen_tokens] == oracle.Oracle(cfg, w, 512).greedy(p, cfg.gen_tokens) or ls.ties
 
 
 BF16 = [
@@ -60,6 +62,11 @@ BF16 = [
     lasynth.get_config("7b", name="bf16_w20_t161", n_layers=2, d_model=256, n_heads=2,
                        n_kv_heads=2, d_ffn=704, vocab=1024, prompt_len=300, W=20, G=20,
                        span_len=8, n_spans=2),
+    # the largest step: 256 rows (W26 N6 G25); 16-token-tile GEMMs, a
+    # 300-token prompt prefilled as a full 256-row chunk plus a ragged 44
+    lasynth.get_config("7b", name="bf16_max_t256", n_layers=1, d_model=256, n_heads=2,
+                       n_kv_heads=2, d_ffn=704, vocab=1024, prompt_len=300, N=6, W=26, G=25,
+                       span_len=8, n_spans=2),
     # plain one-token decode
     lasynth.get_config("7b", name="bf16_plain", n_layers=2, d_model=512, n_heads=4,
                        n_kv_heads=4, d_ffn=1408, vocab=2048, prompt_len=64,
@@ -73,7 +80,7 @@ def test_bf16_lockstep(cfg):
     p = lasynth.make_prompt(cfg)
     win = lasynth.make_init_window(cfg, p) if cfg.W else None
     log(f"[bf16 lockstep] {cfg.name} T={cfg.T}")
-    ls = Lockstep(cfg, w, 512, logit_tol=2e-2)
+    ls = Lockstep(cfg, w, 1024, logit_tol=2e-2)
     ls.run(p, win, n_steps=10)
     ls.compare_kv(3e-2)
     log(f"  steps={len(ls.steps)} max|dlogit|={ls.max_diff:.2e} ties={ls.ties}")
@@ -117,3 +124,31 @@ def test_prompt_ngram_seeding(cfg):
     for _ in range(8):
         ls.step()
     log(f"  {cfg.name} seeded: steps={len(ls.steps)} max|dlogit|={ls.max_diff:.2e} ties={ls.ties}")
+
+
+@pytest.mark.parametrize("cfg", [FP32[0], BF16[0]], ids=lambda c: c.name)
+def test_step_past_capacity_is_refused(cfg):
+    """A step whose rows would not fit in max_ctx is refused with
+    LA_ERR_OUT_OF_CAPACITY before anything is launched: the steps up to the
+    limit agree with the oracle, and the refused step leaves the cache
+    length, current token, window and pool as they were."""
+    import lookahead_decoding_la_amd as la
+    w = lasynth.make_weights(cfg)
+    p = lasynth.make_prompt(cfg)
+    win = lasynth.make_init_window(cfg, p)
+    tol = 1e-4 if cfg.dtype == "f32" else 2e-2
+    max_ctx = len(p) + cfg.T + 40
+    ls = Lockstep(cfg, w, max_ctx, logit_tol=tol, tie_margin=2e-4 if cfg.dtype == "f32" else 0.05)
+    ls.prefill(p, win)
+    while ls.orc.kv_len + cfg.T <= max_ctx:
+        ls.step()
+    before = (ls.dev.debug_state(), ls.dev.debug_window(), ls.dev.debug_pool())
+    for _ in range(2):
+        with pytest.raises(la.LaError) as e:
+            ls.dev.step()
+        assert e.value.status == la.LA_ERR_OUT_OF_CAPACITY
+    after = (ls.dev.debug_state(), ls.dev.debug_window(), ls.dev.debug_pool())
+    assert before[0] == after[0] == (ls.orc.kv_len, ls.orc.current)
+    assert np.array_equal(before[1], after[1])
+    assert np.array_equal(before[2][0], after[2][0]) and np.array_equal(before[2][1], after[2][1])
+    log(f"  {cfg.name}: {len(ls.steps)} steps before the capacity limit (kv {ls.orc.kv_len})")
