@@ -59,12 +59,21 @@ typedef struct {
   int32_t G;        /* verification size = candidates per step = pool cap per key */
   int32_t max_ctx;  /* KV capacity in tokens (prompt + generated + one step's rows) */
   int32_t dtype;    /* la_dtype of weights, activations and KV cache */
+  int32_t batch;    /* B independent sequences stepped together (0 reads as 1);
+                       each has its own KV cache, window, pool and current
+                       token, and a step forwards B blocks of rows at once */
 } la_config;
 /* Supported shapes.  LA_BF16: head_dim 128, d_model % 128 == 0 and
  * <= 8192, d_ffn % 64 == 0, vocab % 128 == 0.  LA_F32 (small models): head_dim even and
  * <= 256, d_model, d_ffn and vocab even, max_ctx <= 16384.  Both:
- * n_heads % n_kv_heads == 0 and 1 + (W + G)(N - 1) <= 256.  W = G = 0 gives
- * the plain one-token greedy decode step. */
+ * n_heads % n_kv_heads == 0 and B (1 + (W + G)(N - 1)) <= 256 (B = batch).
+ * W = G = 0 gives the plain one-token greedy decode step.
+ *
+ * Batch.  Sequence b's rows are rows b*T .. b*T + T - 1 of a step (T = rows
+ * per sequence, la_step_rows); every sequence attends only to its own cache
+ * and block, so each sequence decodes exactly as it would alone.  Arrays
+ * that the calls below describe "per sequence" are laid out sequence by
+ * sequence (sequence 0 first). */
 
 /* Result of one step (host struct). */
 typedef struct {
@@ -102,7 +111,7 @@ la_status la_create(const la_config *cfg, const void *const *weights,
                     void *workspace, size_t workspace_bytes, void *hip_stream,
                     la_ctx **out);
 
-/* Prefill: empty the cache and the pool, run the prompt (host int32
+/* Prefill sequence 0: empty its cache and pool, run the prompt (host int32
  * [n_prompt], ids < vocab) causally in chunks, install the initial window
  * (host int32 [(N-1)*W], level 1 first, then level 2, ...; required when
  * W > 0, ignored otherwise) and return the first generated token (the
@@ -112,10 +121,17 @@ la_status la_create(const la_config *cfg, const void *const *weights,
  * max_ctx), LA_ERR_STATE (poisoned), LA_ERR_HIP. */
 la_status la_prefill(la_ctx *c, const int32_t *prompt, int32_t n_prompt,
                      const int32_t *init_window, int32_t *first_token);
+/* The same for sequence seq (0 <= seq < batch); la_prefill is seq 0.  Only
+ * that sequence's cache, pool, window and state are reset.
+ * Errors: as la_prefill, and LA_ERR_INVALID_ARG for seq out of range. */
+la_status la_prefill_seq(la_ctx *c, int32_t seq, const int32_t *prompt, int32_t n_prompt,
+                         const int32_t *init_window, int32_t *first_token);
 
-/* One lookahead step (blocks until the result is on the host, *out).
- * Errors: LA_ERR_STATE (before prefill or poisoned), LA_ERR_OUT_OF_CAPACITY
- * (kv_len + step rows > max_ctx), LA_ERR_INVALID_ARG (out NULL), LA_ERR_HIP. */
+/* One lookahead step of every sequence (blocks until the results are on the
+ * host): out is host la_step_result [batch], one per sequence.
+ * Errors: LA_ERR_STATE (a sequence not prefilled, or poisoned),
+ * LA_ERR_OUT_OF_CAPACITY (some sequence's kv_len + step rows > max_ctx; no
+ * sequence steps), LA_ERR_INVALID_ARG (out NULL), LA_ERR_HIP. */
 la_status la_step(la_ctx *c, la_step_result *out);
 
 /* Seed the n-gram pool with every N-gram of a token sequence (host int32
@@ -129,6 +145,9 @@ la_status la_step(la_ctx *c, la_step_result *out);
  * Errors: LA_ERR_INVALID_ARG, LA_ERR_STATE (before prefill or poisoned),
  * LA_ERR_HIP. */
 la_status la_seed_pool(la_ctx *c, const int32_t *seq, int32_t n);
+/* The same for the pool of sequence s (0 <= s < batch); la_seed_pool is
+ * s = 0.  Errors: as la_seed_pool, LA_ERR_INVALID_ARG for s out of range. */
+la_status la_seed_pool_seq(la_ctx *c, int32_t s, const int32_t *seq, int32_t n);
 
 /* Destroy a context (NULL is fine).  Waits for the context's queued work. */
 la_status la_destroy(la_ctx *c);
@@ -136,7 +155,7 @@ la_status la_destroy(la_ctx *c);
 const char *la_status_string(la_status s);
 const char *la_last_error(const la_ctx *c);
 
-/* Rows forwarded per step: 1 + (W + G)(N - 1). */
+/* Rows forwarded per step and sequence: 1 + (W + G)(N - 1). */
 int32_t la_step_rows(const la_ctx *c);
 
 /* ---- profiling ----------------------------------------------------------
@@ -145,7 +164,8 @@ int32_t la_step_rows(const la_ctx *c);
  * on the context's stream before and after every kernel launch.  ms[k]
  * (host float [LA_PROF_CLASSES]) receives the summed event time of kernel
  * class k and launches[k] (host int32) the number of launches.  The event
- * pairs add small gaps, so the step itself runs slower than la_step. */
+ * pairs add small gaps, so the step itself runs slower than la_step.  out:
+ * host la_step_result [batch] as for la_step. */
 enum {
   LA_PROF_QKV = 0,    /* fused QKV projection */
   LA_PROF_ATTN = 1,   /* masked attention (+ split merge) */
@@ -175,24 +195,28 @@ la_status la_profile_kernel(la_ctx *c, int32_t klass, int32_t reps,
 
 /* ---- inspection (tests, debugging); each synchronizes the stream ------- */
 
-/* Logits of the last step's rows, host float [rows][vocab]; n = element
- * count of the buffer (must be >= rows * vocab). */
+/* Logits of the last step's rows, host float [batch * rows][vocab]; n =
+ * element count of the buffer (must be >= batch * rows * vocab). */
 la_status la_debug_logits(la_ctx *c, float *host, size_t n);
-/* Tokens and per-row argmax of the last step, host int32 [rows] each (either
- * may be NULL). */
+/* Tokens and per-row argmax of the last step, host int32 [batch * rows]
+ * each (either may be NULL). */
 la_status la_debug_block(la_ctx *c, int32_t *tokens, int32_t *amax);
-/* Current window, host int32 [(N-1)*W] (level 1 first). */
+/* Current windows, host int32 [batch][(N-1)*W] (level 1 first). */
 la_status la_debug_window(la_ctx *c, int32_t *win);
-/* Pool: host int32 len [vocab] and tails [vocab][G][N-1] (oldest first). */
+/* Pools: host int32 len [batch][vocab] and tails [batch][vocab][G][N-1]
+ * (oldest first). */
 la_status la_debug_pool(la_ctx *c, int32_t *len, int32_t *tails);
-/* Insert one n-gram tail (host int32 [N-1]) under key, with the pool's
- * policy (tests plant candidates with it). */
+/* Insert one n-gram tail (host int32 [N-1]) under key into sequence 0's
+ * pool, with the pool's policy (tests plant candidates with it);
+ * la_debug_pool_insert_seq does it for sequence s. */
 la_status la_debug_pool_insert(la_ctx *c, int32_t key, const int32_t *tail);
+la_status la_debug_pool_insert_seq(la_ctx *c, int32_t s, int32_t key, const int32_t *tail);
 /* Cached K and V of positions pos0..pos0+n-1 of one layer as host float
- * [n_kv_heads][n][head_dim] each. */
+ * [batch][n_kv_heads][n][head_dim] each. */
 la_status la_debug_kv(la_ctx *c, int32_t layer, int32_t pos0, int32_t n,
                       float *k, float *v);
-/* Committed length and current token. */
+/* Committed length and current token of each sequence, host int32 [batch]
+ * each (either may be NULL). */
 la_status la_debug_state(la_ctx *c, int32_t *kv_len, int32_t *current);
 
 /* ---- one layer's masked attention on its own ---------------------------

@@ -29,7 +29,8 @@ EXPORTS = [
     "la_debug_block", "la_debug_window", "la_debug_pool",
     "la_debug_pool_insert", "la_debug_kv", "la_debug_state",
     "la_attention_workspace_bytes", "la_attention", "la_profile_step",
-    "la_profile_kernel", "la_seed_pool",
+    "la_profile_kernel", "la_seed_pool", "la_prefill_seq", "la_seed_pool_seq",
+    "la_debug_pool_insert_seq",
 ]
 
 PROF_CLASSES = ["qkv", "attention", "o_proj", "gate_up", "down", "lm_head",
@@ -43,7 +44,7 @@ class LaConfig(C.Structure):
                 ("vocab", C.c_int32), ("rope_theta", C.c_float),
                 ("rms_eps", C.c_float), ("W", C.c_int32), ("N", C.c_int32),
                 ("G", C.c_int32), ("max_ctx", C.c_int32),
-                ("dtype", C.c_int32)]
+                ("dtype", C.c_int32), ("batch", C.c_int32)]
 
 
 class LaStepResult(C.Structure):
@@ -94,6 +95,9 @@ def lib():
             "la_profile_step": (C.c_int, [P, pf, pi, C.POINTER(LaStepResult)]),
             "la_profile_kernel": (C.c_int, [P, I32, I32, pf]),
             "la_seed_pool": (C.c_int, [P, pi, I32]),
+            "la_prefill_seq": (C.c_int, [P, I32, pi, I32, pi, pi]),
+            "la_seed_pool_seq": (C.c_int, [P, I32, pi, I32]),
+            "la_debug_pool_insert_seq": (C.c_int, [P, I32, I32, pi]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -108,17 +112,24 @@ def _i32(a):
     return a, a.ctypes.data_as(C.POINTER(C.c_int32))
 
 
-def make_config(cfg, max_ctx: int) -> LaConfig:
+def make_config(cfg, max_ctx: int, batch: int = 1) -> LaConfig:
     """la_config from an object with the model fields (e.g. a lasynth config)."""
     return LaConfig(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.n_kv_heads,
                     cfg.head_dim, cfg.d_ffn, cfg.vocab, cfg.rope_theta,
                     cfg.rms_eps, cfg.W, cfg.N, cfg.G, max_ctx,
-                    LA_BF16 if cfg.dtype == "bf16" else LA_F32)
+                    LA_BF16 if cfg.dtype == "bf16" else LA_F32, batch)
 
 
-def workspace_bytes(cfg, max_ctx: int) -> int:
-    c = make_config(cfg, max_ctx)
+def workspace_bytes(cfg, max_ctx: int, batch: int = 1) -> int:
+    c = make_config(cfg, max_ctx, batch)
     return int(lib().la_workspace_bytes(C.byref(c)))
+
+
+def _result(r) -> dict:
+    n = int(r.n_emitted)
+    return dict(n_emitted=n, tokens=[int(x) for x in r.tokens[:n]],
+                accepted=int(r.accepted), winner=int(r.winner),
+                n_candidates=int(r.n_candidates), kv_len=int(r.kv_len))
 
 
 def upload_weights(weights, device="cuda"):
@@ -137,13 +148,19 @@ def upload_weights(weights, device="cuda"):
 
 
 class LookaheadDecoder:
-    """One decoding context (la_create ... la_destroy)."""
+    """One decoding context (la_create ... la_destroy) of `batch` sequences.
 
-    def __init__(self, cfg, dev_weights, max_ctx: int, stream=None):
+    With batch == 1 every call speaks of the one sequence (step() returns a
+    dict, the inspection calls arrays without a sequence axis); with batch >
+    1 step() returns one dict per sequence and the inspection calls add a
+    leading sequence axis."""
+
+    def __init__(self, cfg, dev_weights, max_ctx: int, stream=None, batch: int = 1):
         import torch
         self.cfg = cfg
         self.max_ctx = max_ctx
-        self._c = make_config(cfg, max_ctx)
+        self.B = int(batch)
+        self._c = make_config(cfg, max_ctx, self.B)
         L = lib()
         n = int(L.la_workspace_bytes(C.byref(self._c)))
         if n == 0:
@@ -181,42 +198,41 @@ class LookaheadDecoder:
         except Exception:
             pass
 
-    def prefill(self, prompt, init_window=None) -> int:
+    def prefill(self, prompt, init_window=None, seq: int = 0) -> int:
+        """Prefill sequence seq; returns its first generated token."""
         pa, pp = _i32(prompt)
         wp = None
         if init_window is not None:
             wa, wp = _i32(init_window)
         first = C.c_int32()
-        self._check(lib().la_prefill(self._h, pp, len(pa), wp, C.byref(first)),
-                    "la_prefill")
+        self._check(lib().la_prefill_seq(self._h, int(seq), pp, len(pa), wp, C.byref(first)),
+                    "la_prefill_seq")
         return int(first.value)
 
-    def step(self) -> dict:
-        r = LaStepResult()
-        self._check(lib().la_step(self._h, C.byref(r)), "la_step")
-        n = int(r.n_emitted)
-        return dict(n_emitted=n, tokens=[int(x) for x in r.tokens[:n]],
-                    accepted=int(r.accepted), winner=int(r.winner),
-                    n_candidates=int(r.n_candidates), kv_len=int(r.kv_len))
+    def _squeeze(self, out):
+        return out[0] if self.B == 1 else out
+
+    def step(self):
+        r = (LaStepResult * self.B)()
+        self._check(lib().la_step(self._h, r), "la_step")
+        return self._squeeze([_result(x) for x in r])
 
     def profile_step(self):
         """One step with per-launch HIP event timing: (result, {class: (ms, launches)})."""
-        r = LaStepResult()
+        r = (LaStepResult * self.B)()
         ms = (C.c_float * len(PROF_CLASSES))()
         n = (C.c_int32 * len(PROF_CLASSES))()
-        self._check(lib().la_profile_step(self._h, ms, n, C.byref(r)), "la_profile_step")
-        k = int(r.n_emitted)
-        res = dict(n_emitted=k, tokens=[int(x) for x in r.tokens[:k]],
-                   accepted=int(r.accepted), winner=int(r.winner),
-                   n_candidates=int(r.n_candidates), kv_len=int(r.kv_len))
+        self._check(lib().la_profile_step(self._h, ms, n, r), "la_profile_step")
+        res = self._squeeze([_result(x) for x in r])
         return res, {c: (float(ms[i]), int(n[i])) for i, c in enumerate(PROF_CLASSES)}
 
-    def seed_pool(self, seq) -> None:
-        """Insert every N-gram of seq (e.g. the prompt) into the pool, in
-        position order; call after prefill."""
-        a = np.ascontiguousarray(np.asarray(seq, dtype=np.int32))
-        self._check(lib().la_seed_pool(self._h, a.ctypes.data_as(C.POINTER(C.c_int32)), len(a)),
-                    "la_seed_pool")
+    def seed_pool(self, tokens, seq: int = 0) -> None:
+        """Insert every N-gram of tokens (e.g. the prompt) into sequence
+        seq's pool, in position order; call after that sequence's prefill."""
+        a = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        self._check(lib().la_seed_pool_seq(self._h, int(seq),
+                                           a.ctypes.data_as(C.POINTER(C.c_int32)), len(a)),
+                    "la_seed_pool_seq")
 
     def profile_kernel(self, klass: str, reps: int = 32) -> float:
         """Mean microseconds per launch of one kernel class (layer 0's), from
@@ -227,6 +243,8 @@ class LookaheadDecoder:
         return float(us.value)
 
     def generate(self, prompt, init_window, M: int):
+        if self.B != 1:
+            raise ValueError("generate() drives a single-sequence decoder")
         out = [self.prefill(prompt, init_window)]
         steps = []
         while len(out) < M:
@@ -237,50 +255,58 @@ class LookaheadDecoder:
 
     # -- inspection -------------------------------------------------------
     def debug_logits(self) -> np.ndarray:
-        a = np.zeros((self.T, self.cfg.vocab), np.float32)
+        """[batch * T][vocab]: sequence b's rows are b*T .. b*T + T - 1."""
+        a = np.zeros((self.B * self.T, self.cfg.vocab), np.float32)
         self._check(lib().la_debug_logits(self._h, a.ctypes.data_as(C.POINTER(C.c_float)),
                                           a.size), "la_debug_logits")
         return a
 
     def debug_block(self):
-        t = np.zeros(self.T, np.int32)
-        a = np.zeros(self.T, np.int32)
+        t = np.zeros(self.B * self.T, np.int32)
+        a = np.zeros(self.B * self.T, np.int32)
         self._check(lib().la_debug_block(self._h, _i32(t)[1], _i32(a)[1]), "la_debug_block")
         return t, a
 
     def debug_window(self) -> np.ndarray:
-        w = np.zeros((self.cfg.N - 1, self.cfg.W), np.int32)
+        w = np.zeros((self.B, self.cfg.N - 1, self.cfg.W), np.int32)
         if self.cfg.W:
-            self._check(lib().la_debug_window(self._h, _i32(w)[1]), "la_debug_window")
-        return w
+            self._check(lib().la_debug_window(self._h, w.ctypes.data_as(C.POINTER(C.c_int32))),
+                        "la_debug_window")
+        return self._squeeze(w)
 
     def debug_pool(self):
         c = self.cfg
-        ln = np.zeros(c.vocab, np.int32)
-        tl = np.zeros((c.vocab, max(c.G, 1), c.N - 1), np.int32)
-        self._check(lib().la_debug_pool(self._h, _i32(ln)[1],
-                                        tl.ctypes.data_as(C.POINTER(C.c_int32))),
+        pi = C.POINTER(C.c_int32)
+        ln = np.zeros((self.B, c.vocab), np.int32)
+        tl = np.zeros((self.B, c.vocab, max(c.G, 1), c.N - 1), np.int32)
+        self._check(lib().la_debug_pool(self._h, ln.ctypes.data_as(pi), tl.ctypes.data_as(pi)),
                     "la_debug_pool")
-        return ln, tl[:, :c.G]
+        if self.B == 1:
+            return ln[0], tl[0, :, :c.G]
+        return ln, tl[:, :, :c.G]
 
-    def debug_pool_insert(self, key: int, tail) -> None:
+    def debug_pool_insert(self, key: int, tail, seq: int = 0) -> None:
         ta, tp = _i32(tail)
-        self._check(lib().la_debug_pool_insert(self._h, int(key), tp), "la_debug_pool_insert")
+        self._check(lib().la_debug_pool_insert_seq(self._h, int(seq), int(key), tp),
+                    "la_debug_pool_insert_seq")
 
     def debug_kv(self, layer: int, pos0: int, n: int):
         c = self.cfg
-        k = np.zeros((c.n_kv_heads, n, c.head_dim), np.float32)
+        k = np.zeros((self.B, c.n_kv_heads, n, c.head_dim), np.float32)
         v = np.zeros_like(k)
         pf = C.POINTER(C.c_float)
         self._check(lib().la_debug_kv(self._h, layer, pos0, n, k.ctypes.data_as(pf),
                                       v.ctypes.data_as(pf)), "la_debug_kv")
-        return k, v
+        return self._squeeze(k), self._squeeze(v)
 
     def debug_state(self):
-        L = C.c_int32()
-        cur = C.c_int32()
-        self._check(lib().la_debug_state(self._h, C.byref(L), C.byref(cur)), "la_debug_state")
-        return int(L.value), int(cur.value)
+        """(kv_len, current token), per sequence when batch > 1."""
+        pi = C.POINTER(C.c_int32)
+        L = np.zeros(self.B, np.int32)
+        cur = np.zeros(self.B, np.int32)
+        self._check(lib().la_debug_state(self._h, L.ctypes.data_as(pi), cur.ctypes.data_as(pi)),
+                    "la_debug_state")
+        return self._squeeze([(int(a), int(b)) for a, b in zip(L, cur)])
 
 
 def attention(q, k_cache, vt_cache, out, n_heads, n_kv_heads, prefix_len, W, N, G,

@@ -73,15 +73,16 @@ struct Prof {
 
 struct la_ctx {
   la_config cfg;
-  int T = 0, MR = 0, bf16 = 0, elem = 4, ctx_stride = 0;
+  int T = 0, B = 1, MR = 0, bf16 = 0, elem = 4, ctx_stride = 0;
   int qdim = 0, kvdim = 0, qkv_rows = 0;
   hipStream_t stream = nullptr;
-  bool poisoned = false, prefilled = false, use_graph = true;
+  bool poisoned = false, use_graph = true;
   std::string err;
-  int kv_len_host = 0;
-  // device carve-up
-  DevState* st = nullptr;
-  DevResult* res_dev = nullptr;
+  std::vector<int> kv_len_host;  // per sequence
+  std::vector<char> prefilled;   // per sequence
+  // device carve-up (per-sequence arrays: sequence 0 first)
+  DevState* st = nullptr;        // [B]
+  DevResult* res_dev = nullptr;  // [B]
   float *x = nullptr, *logits = nullptr, *rope_cos = nullptr, *rope_sin = nullptr;
   float *gpart = nullptr, *attn_po = nullptr, *attn_pml = nullptr;
   float* ssq = nullptr;  // bf16: per-row partial sums of squares (deferred RMSNorm)
@@ -91,17 +92,19 @@ struct la_ctx {
   uint16_t *xnf = nullptr, *of = nullptr, *af = nullptr;  // bf16: fragment layout
   int MTT = 0;
   int32_t *tokens = nullptr, *relpos = nullptr, *amax = nullptr, *prompt_buf = nullptr;
-  int32_t *win = nullptr, *pool_len = nullptr, *pool = nullptr;
+  int32_t *win = nullptr, *pool_len = nullptr, *pool = nullptr;  // [B][...]
+  size_t pool_seq = 0;        // pool ints per sequence (V * G * (N-1))
   int32_t* tail_buf = nullptr;
-  void *kcache = nullptr, *vtcache = nullptr;
-  size_t kv_layer_elems = 0;  // elements of one layer's K (or V^T) cache
+  void *kcache = nullptr, *vtcache = nullptr;  // [layer][B][Hkv][...]
+  size_t kv_layer_elems = 0;  // elements of one layer's K (or V^T) cache, all sequences
+  size_t kv_seq = 0;          // of them per sequence
   // weights
   const void *emb = nullptr, *final_norm = nullptr, *lm = nullptr;
   std::vector<Layer> layers;
   GemmPlan p_qkv{1, 1}, p_o{1, 1}, p_gu{1, 1}, p_d{1, 1}, p_lm{1, 1};
   int attn_splits = 1;
   // host
-  DevResult* res_host = nullptr;  // pinned
+  DevResult* res_host = nullptr;  // pinned [B]
   int32_t* pin = nullptr;         // pinned staging
   size_t pin_count = 0;
   hipGraph_t graph = nullptr;
@@ -139,8 +142,10 @@ la_status check_config(const la_config* cfg, std::string* why) {
   if (c.W < 0 || c.G < 0) return bad("W and G must be >= 0");
   if (!(c.rms_eps > 0.f) || !(c.rope_theta > 0.f)) return bad("rms_eps and rope_theta must be > 0");
   if (c.dtype != LA_F32 && c.dtype != LA_BF16) return bad("dtype must be LA_F32 or LA_BF16");
+  if (c.batch < 0) return bad("batch must be >= 0 (0 reads as 1)");
+  const long B = c.batch > 0 ? c.batch : 1;
   long T = 1 + (long)(c.W + c.G) * (c.N - 1);
-  if (T > MAX_ROWS) return uns("1 + (W+G)(N-1) must be <= 256");
+  if (T * B > MAX_ROWS) return uns("batch * (1 + (W+G)(N-1)) must be <= 256");
   if (c.max_ctx < T + 1) return bad("max_ctx must exceed the step's rows");
   if (c.head_dim % 2) return bad("head_dim must be even");
   if (c.dtype == LA_BF16) {
@@ -161,21 +166,24 @@ size_t carve(la_ctx* c, void* base) {
   const la_config& g = c->cfg;
   Carver cv(base);
   const int d = g.d_model, V = g.vocab, F = g.d_ffn, dh = g.head_dim;
-  c->st = cv.take<DevState>(1);
-  c->res_dev = cv.take<DevResult>(1);
+  const int B = c->B, n1 = g.N - 1;
+  c->st = cv.take<DevState>(B);
+  c->res_dev = cv.take<DevResult>(B);
   c->tail_buf = cv.take<int32_t>(32);
   c->tokens = cv.take<int32_t>(c->MR);
   c->relpos = cv.take<int32_t>(c->MR);
   c->amax = cv.take<int32_t>(c->MR);
   c->prompt_buf = cv.take<int32_t>(c->MR);
-  c->win = cv.take<int32_t>((size_t)std::max(1, (g.N - 1) * g.W));
-  c->pool_len = cv.take<int32_t>(V);
-  c->pool = cv.take<int32_t>((size_t)V * std::max(1, g.G) * (g.N - 1));
+  c->win = cv.take<int32_t>((size_t)B * std::max(1, n1 * g.W));
+  c->pool_len = cv.take<int32_t>((size_t)B * V);
+  c->pool_seq = (size_t)V * g.G * n1;
+  c->pool = cv.take<int32_t>((size_t)B * V * std::max(1, g.G) * n1);
   c->x = cv.take<float>((size_t)c->MR * d);
   c->logits = cv.take<float>((size_t)c->MR * V);
   c->rope_cos = cv.take<float>((size_t)c->ctx_stride * (dh / 2));
   c->rope_sin = cv.take<float>((size_t)c->ctx_stride * (dh / 2));
-  c->kv_layer_elems = (size_t)g.n_kv_heads * c->ctx_stride * dh;
+  c->kv_seq = (size_t)g.n_kv_heads * c->ctx_stride * dh;
+  c->kv_layer_elems = c->kv_seq * B;
   c->kcache = cv.take<char>(c->kv_layer_elems * g.n_layers * c->elem);
   c->vtcache = cv.take<char>(c->kv_layer_elems * g.n_layers * c->elem);
   c->qb = cv.take<char>((size_t)c->MR * c->qdim * c->elem);
@@ -194,8 +202,10 @@ size_t carve(la_ctx* c, void* base) {
     gp = std::max(gp, (size_t)c->p_o.ksplit * c->MR * d);
     gp = std::max(gp, (size_t)c->p_d.ksplit * c->MR * d);
     c->gpart = cv.take<float>(gp);
-    c->attn_splits = attn_bf16_splits(g.n_heads, c->T, c->ctx_stride);
-    size_t rows16 = (size_t)g.n_heads * c->attn_splits * c->MR;
+    c->attn_splits = attn_bf16_splits(g.n_heads * B, c->T, c->ctx_stride);
+    // partials [seq][H][splits][rows16]: B blocks of T rows, or one prefill chunk
+    const size_t rows_all = std::max((size_t)B * ((c->T + 15) & ~15), (size_t)c->MR);
+    size_t rows16 = (size_t)g.n_heads * c->attn_splits * rows_all;
     c->attn_po = cv.take<float>(rows16 * dh);
     c->attn_pml = cv.take<float>(rows16 * 2);
     c->ssq = cv.take<float>((size_t)c->MR * SSQ_STRIDE);
@@ -223,7 +233,8 @@ size_t carve(la_ctx* c, void* base) {
 void init_dims(la_ctx* c, const la_config* cfg) {
   c->cfg = *cfg;
   c->T = 1 + (cfg->W + cfg->G) * (cfg->N - 1);
-  c->MR = std::max((int)align_up(c->T, 64), 128);
+  c->B = cfg->batch > 0 ? cfg->batch : 1;
+  c->MR = std::max((int)align_up((size_t)c->T * c->B, 64), 128);
   c->bf16 = cfg->dtype == LA_BF16;
   c->elem = c->bf16 ? 2 : 4;
   c->ctx_stride = (int)align_up(cfg->max_ctx, 64);
@@ -232,14 +243,33 @@ void init_dims(la_ctx* c, const la_config* cfg) {
   c->qkv_rows = c->qdim + 2 * c->kvdim;
 }
 
-void* layer_k(la_ctx* c, int l) { return (char*)c->kcache + (size_t)l * c->kv_layer_elems * c->elem; }
-void* layer_v(la_ctx* c, int l) { return (char*)c->vtcache + (size_t)l * c->kv_layer_elems * c->elem; }
+// One layer's K (or V^T) cache from sequence seq on.
+void* layer_k(la_ctx* c, int l, int seq = 0) {
+  return (char*)c->kcache + ((size_t)l * c->kv_layer_elems + seq * c->kv_seq) * c->elem;
+}
+void* layer_v(la_ctx* c, int l, int seq = 0) {
+  return (char*)c->vtcache + ((size_t)l * c->kv_layer_elems + seq * c->kv_seq) * c->elem;
+}
 
-EpiArgs base_epi(la_ctx* c, int M) {
+// The rows of one forward pass: row t is block row t % rps of sequence
+// seq0 + t / rps.  A step forwards every sequence's block (rps = T); a
+// prefill chunk, rows of one sequence's prompt.
+struct Pass {
+  int M;       // rows
+  int mode;    // MODE_STEP / MODE_CAUSAL
+  int seq0, nseq, rps;
+  int rows;    // rows per sequence
+};
+Pass step_pass(const la_ctx* c) { return Pass{c->B * c->T, MODE_STEP, 0, c->B, c->T, c->T}; }
+Pass prefill_pass(const la_ctx* c, int seq, int m) { return Pass{m, MODE_CAUSAL, seq, 1, c->MR, m}; }
+
+EpiArgs base_epi(la_ctx* c, const Pass& p) {
   EpiArgs ea;
   memset(&ea, 0, sizeof(ea));
-  ea.M = M;
-  ea.st = c->st;
+  ea.M = p.M;
+  ea.st = c->st + p.seq0;
+  ea.rps = p.rps;
+  ea.kv_seq = c->kv_seq;
   ea.relpos = c->relpos;
   ea.rope_cos = c->rope_cos;
   ea.rope_sin = c->rope_sin;
@@ -250,18 +280,21 @@ EpiArgs base_epi(la_ctx* c, int M) {
   return ea;
 }
 
-AttnArgs attn_args(la_ctx* c, int l, int M, int mode) {
+AttnArgs attn_args(la_ctx* c, int l, const Pass& p) {
   const la_config& g = c->cfg;
   AttnArgs aa;
   memset(&aa, 0, sizeof(aa));
   aa.q = c->qb;
-  aa.k_cache = layer_k(c, l);
-  aa.vt_cache = layer_v(c, l);
+  aa.k_cache = layer_k(c, l, p.seq0);
+  aa.vt_cache = layer_v(c, l, p.seq0);
   aa.out = c->bf16 ? (void*)c->of : c->xn;
   aa.out_mtt = c->bf16 ? c->MTT : 0;
-  aa.st = c->st;
-  aa.M = M;
-  aa.mode = mode;
+  aa.st = c->st + p.seq0;
+  aa.M = p.rows;
+  aa.rps = p.rps;
+  aa.nseq = p.nseq;
+  aa.kv_seq = c->kv_seq;
+  aa.mode = p.mode;
   aa.H = g.n_heads;
   aa.Hkv = g.n_kv_heads;
   aa.dh = g.head_dim;
@@ -276,17 +309,17 @@ AttnArgs attn_args(la_ctx* c, int l, int M, int mode) {
 
 // The decoder over the assembled rows.  bf16: x holds their embeddings and
 // xnf the first layer's normalized input; f32: x only.
-void enqueue_layers(la_ctx* c, int M, int mode, hipStream_t s, Prof* pf = nullptr) {
+void enqueue_layers(la_ctx* c, const Pass& p, hipStream_t s, Prof* pf = nullptr) {
 #define P_BEGIN(k) if (pf) pf->begin(k)
 #define P_END() if (pf) pf->end()
   const la_config& g = c->cfg;
-  const int d = g.d_model, F = g.d_ffn;
+  const int d = g.d_model, F = g.d_ffn, M = p.M;
   for (int l = 0; l < g.n_layers; l++) {
     const Layer& L = c->layers[l];
-    EpiArgs ea = base_epi(c, M);
+    EpiArgs ea = base_epi(c, p);
     ea.out_act = c->qb;
-    ea.k_cache = layer_k(c, l);
-    ea.vt_cache = layer_v(c, l);
+    ea.k_cache = layer_k(c, l, p.seq0);
+    ea.vt_cache = layer_v(c, l, p.seq0);
     ea.ssq = c->ssq;
     ea.rope_rows = c->rope_rows;
     ea.ssn = c->ssn;
@@ -303,7 +336,7 @@ void enqueue_layers(la_ctx* c, int M, int mode, hipStream_t s, Prof* pf = nullpt
       launch_red_qkv(c->gpart, c->p_qkv.ksplit, c->qkv_rows, M, ea, s);
       P_END();
       P_BEGIN(LA_PROF_ATTN);
-      launch_attn_bf16(attn_args(c, l, M, mode), s);
+      launch_attn_bf16(attn_args(c, l, p), s);
       P_END();
       P_BEGIN(LA_PROF_O);
       launch_gemm_bf16(c->of, c->MTT, (const uint16_t*)L.wo, c->qdim, d, M, c->p_o, c->gpart, s);
@@ -336,9 +369,9 @@ void enqueue_layers(la_ctx* c, int M, int mode, hipStream_t s, Prof* pf = nullpt
                       c->qkv_rows, M, ea, s);
       P_END();
       P_BEGIN(LA_PROF_ATTN);
-      launch_attn_f32(attn_args(c, l, M, mode), s);
+      launch_attn_f32(attn_args(c, l, p), s);
       P_END();
-      ea = base_epi(c, M);
+      ea = base_epi(c, p);
       ea.out_f32 = c->x;
       ea.ld_out = d;
       P_BEGIN(LA_PROF_O);
@@ -348,14 +381,14 @@ void enqueue_layers(la_ctx* c, int M, int mode, hipStream_t s, Prof* pf = nullpt
       P_BEGIN(LA_PROF_REDUCE);
       launch_rmsnorm(c->x, L.fnorm, M, d, g.rms_eps, 0, c->xn, s);
       P_END();
-      ea = base_epi(c, M);
+      ea = base_epi(c, p);
       ea.out_act = c->ffa;
       ea.ld_out = F;
       P_BEGIN(LA_PROF_GATEUP);
       launch_gemm_f32(EPI_SWIGLU, (const float*)c->xn, (const float*)L.wg, (const float*)L.wu, d,
                       F, M, ea, s);
       P_END();
-      ea = base_epi(c, M);
+      ea = base_epi(c, p);
       ea.out_f32 = c->x;
       ea.ld_out = d;
       P_BEGIN(LA_PROF_DOWN);
@@ -378,7 +411,7 @@ void enqueue_head(la_ctx* c, int M, hipStream_t s, Prof* pf = nullptr) {
     P_BEGIN(LA_PROF_REDUCE);
     launch_rmsnorm(c->x, c->final_norm, M, g.d_model, g.rms_eps, 0, c->xn, s);
     P_END();
-    EpiArgs ea = base_epi(c, M);
+    EpiArgs ea = base_epi(c, Pass{M, MODE_STEP, 0, 1, M, M});
     ea.out_f32 = c->logits;
     ea.ld_out = g.vocab;
     P_BEGIN(LA_PROF_LMHEAD);
@@ -393,23 +426,25 @@ void enqueue_head(la_ctx* c, int M, hipStream_t s, Prof* pf = nullptr) {
 
 void enqueue_step(la_ctx* c, hipStream_t s, Prof* pf = nullptr) {
   const la_config& g = c->cfg;
+  const Pass p = step_pass(c);
   P_BEGIN(LA_PROF_OTHER);
-  launch_assemble(MODE_STEP, c->st, c->win, c->pool_len, c->pool, nullptr, c->T, g.W, g.N, g.G,
-                  c->tokens, c->relpos, c->st, c->emb, g.d_model, c->bf16, c->x,
+  launch_assemble(MODE_STEP, c->st, c->win, c->pool_len, c->pool, nullptr, p.M, c->T, g.vocab,
+                  g.W, g.N, g.G, c->tokens, c->relpos, c->st, c->emb, g.d_model, c->bf16, c->x,
                   (const uint16_t*)c->layers[0].anorm, g.rms_eps, c->xnf, c->MTT, c->ssq,
                   c->rope_cos, c->rope_sin, c->rope_rows, s);
   P_END();
-  enqueue_layers(c, c->T, MODE_STEP, s, pf);
-  enqueue_head(c, c->T, s, pf);
+  enqueue_layers(c, p, s, pf);
+  enqueue_head(c, p.M, s, pf);
   P_BEGIN(LA_PROF_OTHER);
-  launch_verify(c->st, c->tokens, c->amax, c->win, c->pool_len, c->pool, g.W, g.N, g.G,
-                c->res_dev, s);
+  launch_verify(c->st, c->tokens, c->amax, c->win, c->pool_len, c->pool, c->B, g.vocab, g.W,
+                g.N, g.G, c->res_dev, s);
   P_END();
   P_BEGIN(LA_PROF_OTHER);
-  launch_kv_compact(c->st, g.n_layers, g.n_kv_heads, g.head_dim, c->ctx_stride, g.W, g.N,
+  launch_kv_compact(c->st, c->B, g.n_layers, g.n_kv_heads, g.head_dim, c->ctx_stride, g.W, g.N,
                     c->elem, c->kcache, c->vtcache, s);
   P_END();
-  (void)hipMemcpyAsync(c->res_host, c->res_dev, sizeof(DevResult), hipMemcpyDeviceToHost, s);
+  (void)hipMemcpyAsync(c->res_host, c->res_dev, sizeof(DevResult) * c->B, hipMemcpyDeviceToHost,
+                       s);
 }
 #undef P_BEGIN
 #undef P_END
@@ -418,6 +453,23 @@ la_status check_usable(la_ctx* c) {
   if (!c) return LA_ERR_INVALID_ARG;
   if (c->poisoned) return fail(c, LA_ERR_STATE, "context poisoned by an earlier HIP failure: " + c->err);
   return LA_OK;
+}
+
+// Every sequence prefilled and room for one more step in each.
+la_status check_steppable(la_ctx* c, const char* what) {
+  for (int b = 0; b < c->B; b++)
+    if (!c->prefilled[b])
+      return fail(c, LA_ERR_STATE, std::string(what) + " before every sequence was prefilled");
+  for (int b = 0; b < c->B; b++)
+    if ((long)c->kv_len_host[b] + c->T > c->cfg.max_ctx)
+      return fail(c, LA_ERR_OUT_OF_CAPACITY, "kv_len + step rows exceed max_ctx");
+  return LA_OK;
+}
+
+void take_results(la_ctx* c, la_step_result* out) {
+  static_assert(sizeof(DevResult) == sizeof(la_step_result), "result layout");
+  memcpy(out, c->res_host, sizeof(*out) * c->B);
+  for (int b = 0; b < c->B; b++) c->kv_len_host[b] = out[b].kv_len;
 }
 
 }  // namespace
@@ -476,9 +528,11 @@ la_status la_create(const la_config* cfg, const void* const* weights, void* work
 
   // pinned host buffers
   c->pin_count = std::max<size_t>(c->MR, (size_t)std::max(1, (g.N - 1) * g.W)) + 64;
-  LA_HIP(c, hipHostMalloc((void**)&c->res_host, sizeof(DevResult), hipHostMallocDefault));
+  LA_HIP(c, hipHostMalloc((void**)&c->res_host, sizeof(DevResult) * c->B, hipHostMallocDefault));
   LA_HIP(c, hipHostMalloc((void**)&c->pin, c->pin_count * sizeof(int32_t), hipHostMallocDefault));
-  memset(c->res_host, 0, sizeof(DevResult));
+  memset(c->res_host, 0, sizeof(DevResult) * c->B);
+  c->kv_len_host.assign(c->B, 0);
+  c->prefilled.assign(c->B, 0);
 
   // clear state, caches and activations (fill kernels: finite padding rows)
   launch_fill_u32(workspace, 0, need / 4, s);
@@ -550,9 +604,15 @@ la_status la_create(const la_config* cfg, const void* const* weights, void* work
 
 la_status la_prefill(la_ctx* c, const int32_t* prompt, int32_t n_prompt, const int32_t* init_window,
                      int32_t* first_token) {
+  return la_prefill_seq(c, 0, prompt, n_prompt, init_window, first_token);
+}
+
+la_status la_prefill_seq(la_ctx* c, int32_t seq, const int32_t* prompt, int32_t n_prompt,
+                         const int32_t* init_window, int32_t* first_token) {
   la_status us = check_usable(c);
   if (us != LA_OK) return us;
   const la_config& g = c->cfg;
+  if (seq < 0 || seq >= c->B) return fail(c, LA_ERR_INVALID_ARG, "seq out of range");
   if (!prompt || n_prompt < 1 || !first_token) return fail(c, LA_ERR_INVALID_ARG, "prompt/first_token");
   if (g.W > 0 && !init_window) return fail(c, LA_ERR_INVALID_ARG, "init_window required when W > 0");
   for (int i = 0; i < n_prompt; i++)
@@ -562,12 +622,14 @@ la_status la_prefill(la_ctx* c, const int32_t* prompt, int32_t n_prompt, const i
     if (init_window[i] < 0 || init_window[i] >= g.vocab) return fail(c, LA_ERR_INVALID_ARG, "window token out of range");
   if ((long)n_prompt + c->T > g.max_ctx) return fail(c, LA_ERR_OUT_OF_CAPACITY, "prompt + step rows exceed max_ctx");
   hipStream_t s = c->stream;
-  c->prefilled = false;
-  launch_fill_u32(c->st, 0, sizeof(DevState) / 4, s);
-  launch_fill_u32(c->pool_len, 0, (size_t)g.vocab, s);
+  DevState* sst = c->st + seq;
+  c->prefilled[seq] = 0;
+  launch_fill_u32(sst, 0, sizeof(DevState) / 4, s);
+  launch_fill_u32(c->pool_len + (size_t)seq * g.vocab, 0, (size_t)g.vocab, s);
   if (nwin > 0) {
     memcpy(c->pin, init_window, sizeof(int32_t) * nwin);
-    LA_HIP(c, hipMemcpyAsync(c->win, c->pin, sizeof(int32_t) * nwin, hipMemcpyHostToDevice, s));
+    LA_HIP(c, hipMemcpyAsync(c->win + (size_t)seq * nwin, c->pin, sizeof(int32_t) * nwin,
+                             hipMemcpyHostToDevice, s));
     LA_HIP(c, hipStreamSynchronize(s));
   }
   for (int p0 = 0; p0 < n_prompt; p0 += c->MR) {
@@ -575,31 +637,31 @@ la_status la_prefill(la_ctx* c, const int32_t* prompt, int32_t n_prompt, const i
     const bool last = p0 + m == n_prompt;
     memcpy(c->pin, prompt + p0, sizeof(int32_t) * m);
     LA_HIP(c, hipMemcpyAsync(c->prompt_buf, c->pin, sizeof(int32_t) * m, hipMemcpyHostToDevice, s));
-    launch_assemble(MODE_CAUSAL, c->st, c->win, c->pool_len, c->pool, c->prompt_buf, m, g.W, g.N,
-                    g.G, c->tokens, c->relpos, c->st, c->emb, g.d_model, c->bf16, c->x,
+    launch_assemble(MODE_CAUSAL, sst, nullptr, nullptr, nullptr, c->prompt_buf, m, m, g.vocab,
+                    g.W, g.N, g.G, c->tokens, c->relpos, sst, c->emb, g.d_model, c->bf16, c->x,
                     (const uint16_t*)c->layers[0].anorm, g.rms_eps, c->xnf, c->MTT, c->ssq,
-                  c->rope_cos, c->rope_sin, c->rope_rows, s);
-    enqueue_layers(c, m, MODE_CAUSAL, s);
+                    c->rope_cos, c->rope_sin, c->rope_rows, s);
+    enqueue_layers(c, prefill_pass(c, seq, m), s);
     if (last) enqueue_head(c, m, s);
-    launch_advance(c->st, m, c->amax, last ? 1 : 0, s);
+    launch_advance(sst, m, c->amax, last ? 1 : 0, s);
     LA_HIP(c, hipGetLastError());
     LA_HIP(c, hipStreamSynchronize(s));
   }
   DevState hs;
-  LA_HIP(c, hipMemcpy(&hs, c->st, sizeof(hs), hipMemcpyDeviceToHost));
-  c->kv_len_host = hs.L;
+  LA_HIP(c, hipMemcpy(&hs, sst, sizeof(hs), hipMemcpyDeviceToHost));
+  c->kv_len_host[seq] = hs.L;
   *first_token = hs.cur;
-  c->prefilled = true;
+  c->prefilled[seq] = 1;
   return LA_OK;
 }
+
 
 la_status la_step(la_ctx* c, la_step_result* out) {
   la_status us = check_usable(c);
   if (us != LA_OK) return us;
   if (!out) return fail(c, LA_ERR_INVALID_ARG, "out is NULL");
-  if (!c->prefilled) return fail(c, LA_ERR_STATE, "la_step before la_prefill");
-  if ((long)c->kv_len_host + c->T > c->cfg.max_ctx)
-    return fail(c, LA_ERR_OUT_OF_CAPACITY, "kv_len + step rows exceed max_ctx");
+  us = check_steppable(c, "la_step");
+  if (us != LA_OK) return us;
   if (c->use_graph) {
     LA_HIP(c, hipGraphLaunch(c->gexec, c->stream));
   } else {
@@ -607,9 +669,7 @@ la_status la_step(la_ctx* c, la_step_result* out) {
     LA_HIP(c, hipGetLastError());
   }
   LA_HIP(c, hipStreamSynchronize(c->stream));
-  static_assert(sizeof(DevResult) == sizeof(la_step_result), "result layout");
-  memcpy(out, c->res_host, sizeof(*out));
-  c->kv_len_host = out->kv_len;
+  take_results(c, out);
   return LA_OK;
 }
 
@@ -617,9 +677,8 @@ la_status la_profile_step(la_ctx* c, float* ms, int32_t* launches, la_step_resul
   la_status us = check_usable(c);
   if (us != LA_OK) return us;
   if (!out || !ms || !launches) return fail(c, LA_ERR_INVALID_ARG, "NULL output");
-  if (!c->prefilled) return fail(c, LA_ERR_STATE, "la_profile_step before la_prefill");
-  if ((long)c->kv_len_host + c->T > c->cfg.max_ctx)
-    return fail(c, LA_ERR_OUT_OF_CAPACITY, "kv_len + step rows exceed max_ctx");
+  us = check_steppable(c, "la_profile_step");
+  if (us != LA_OK) return us;
   LA_HIP(c, hipStreamSynchronize(c->stream));
   Prof pf;
   pf.pool = &c->events;
@@ -637,8 +696,7 @@ la_status la_profile_step(la_ctx* c, float* ms, int32_t* launches, la_step_resul
     ms[pf.cat[i]] += t;
     launches[pf.cat[i]] += 1;
   }
-  memcpy(out, c->res_host, sizeof(*out));
-  c->kv_len_host = out->kv_len;
+  take_results(c, out);
   return LA_OK;
 }
 
@@ -647,13 +705,15 @@ la_status la_profile_kernel(la_ctx* c, int32_t klass, int32_t reps, float* us_pe
   if (us != LA_OK) return us;
   if (!us_per_launch || reps < 1 || reps > 100000)
     return fail(c, LA_ERR_INVALID_ARG, "reps must be in 1..100000 and the output non-NULL");
-  if (!c->prefilled) return fail(c, LA_ERR_STATE, "la_profile_kernel before la_prefill");
+  for (int b = 0; b < c->B; b++)
+    if (!c->prefilled[b]) return fail(c, LA_ERR_STATE, "la_profile_kernel before la_prefill");
   if (!c->bf16) return fail(c, LA_ERR_UNSUPPORTED, "la_profile_kernel needs the bf16 kernels");
   if (klass != LA_PROF_QKV && klass != LA_PROF_ATTN && klass != LA_PROF_O &&
       klass != LA_PROF_GATEUP && klass != LA_PROF_DOWN)
     return fail(c, LA_ERR_INVALID_ARG, "klass must be QKV, ATTN, O, GATEUP or DOWN");
   const la_config& g = c->cfg;
-  const int d = g.d_model, F = g.d_ffn, M = c->T;
+  const Pass p = step_pass(c);
+  const int d = g.d_model, F = g.d_ffn, M = p.M;
   const hipStream_t s = c->stream;
   // launch i runs layer i % n_layers, so the weights streamed differ from
   // one launch to the next (no help from the last-level cache)
@@ -665,7 +725,7 @@ la_status la_profile_kernel(la_ctx* c, int32_t klass, int32_t reps, float* us_pe
                          c->gpart, s);
         break;
       case LA_PROF_ATTN:
-        launch_attn_bf16(attn_args(c, l, M, MODE_STEP), s);
+        launch_attn_bf16(attn_args(c, l, p), s);
         break;
       case LA_PROF_O:
         launch_gemm_bf16(c->of, c->MTT, (const uint16_t*)L.wo, c->qdim, d, M, c->p_o, c->gpart, s);
@@ -711,7 +771,7 @@ la_status la_destroy(la_ctx* c) {
 la_status la_debug_logits(la_ctx* c, float* host, size_t n) {
   la_status us = check_usable(c);
   if (us != LA_OK) return us;
-  size_t need = (size_t)c->T * c->cfg.vocab;
+  size_t need = (size_t)c->B * c->T * c->cfg.vocab;
   if (!host || n < need) return fail(c, LA_ERR_INVALID_ARG, "logits buffer too small");
   LA_HIP(c, hipStreamSynchronize(c->stream));
   LA_HIP(c, hipMemcpy(host, c->logits, need * sizeof(float), hipMemcpyDeviceToHost));
@@ -722,8 +782,9 @@ la_status la_debug_block(la_ctx* c, int32_t* tokens, int32_t* amax) {
   la_status us = check_usable(c);
   if (us != LA_OK) return us;
   LA_HIP(c, hipStreamSynchronize(c->stream));
-  if (tokens) LA_HIP(c, hipMemcpy(tokens, c->tokens, sizeof(int32_t) * c->T, hipMemcpyDeviceToHost));
-  if (amax) LA_HIP(c, hipMemcpy(amax, c->amax, sizeof(int32_t) * c->T, hipMemcpyDeviceToHost));
+  const size_t rows = (size_t)c->B * c->T;
+  if (tokens) LA_HIP(c, hipMemcpy(tokens, c->tokens, sizeof(int32_t) * rows, hipMemcpyDeviceToHost));
+  if (amax) LA_HIP(c, hipMemcpy(amax, c->amax, sizeof(int32_t) * rows, hipMemcpyDeviceToHost));
   return LA_OK;
 }
 
@@ -734,7 +795,7 @@ la_status la_debug_window(la_ctx* c, int32_t* win) {
   if (n == 0) return LA_OK;
   if (!win) return fail(c, LA_ERR_INVALID_ARG, "win is NULL");
   LA_HIP(c, hipStreamSynchronize(c->stream));
-  LA_HIP(c, hipMemcpy(win, c->win, sizeof(int32_t) * n, hipMemcpyDeviceToHost));
+  LA_HIP(c, hipMemcpy(win, c->win, sizeof(int32_t) * n * c->B, hipMemcpyDeviceToHost));
   return LA_OK;
 }
 
@@ -743,21 +804,26 @@ la_status la_debug_pool(la_ctx* c, int32_t* len, int32_t* tails) {
   if (us != LA_OK) return us;
   const la_config& g = c->cfg;
   LA_HIP(c, hipStreamSynchronize(c->stream));
-  if (len) LA_HIP(c, hipMemcpy(len, c->pool_len, sizeof(int32_t) * g.vocab, hipMemcpyDeviceToHost));
+  if (len)
+    LA_HIP(c, hipMemcpy(len, c->pool_len, sizeof(int32_t) * g.vocab * c->B, hipMemcpyDeviceToHost));
   if (tails && g.G > 0)
-    LA_HIP(c, hipMemcpy(tails, c->pool, sizeof(int32_t) * (size_t)g.vocab * g.G * (g.N - 1),
-                        hipMemcpyDeviceToHost));
+    LA_HIP(c, hipMemcpy(tails, c->pool, sizeof(int32_t) * c->pool_seq * c->B, hipMemcpyDeviceToHost));
   return LA_OK;
 }
 
 la_status la_seed_pool(la_ctx* c, const int32_t* seq, int32_t n) {
+  return la_seed_pool_seq(c, 0, seq, n);
+}
+
+la_status la_seed_pool_seq(la_ctx* c, int32_t sq, const int32_t* seq, int32_t n) {
   la_status us = check_usable(c);
   if (us != LA_OK) return us;
   const la_config& g = c->cfg;
+  if (sq < 0 || sq >= c->B) return fail(c, LA_ERR_INVALID_ARG, "sequence index out of range");
   if (n < 0 || (n > 0 && !seq)) return fail(c, LA_ERR_INVALID_ARG, "seq/n");
   for (int i = 0; i < n; i++)
     if (seq[i] < 0 || seq[i] >= g.vocab) return fail(c, LA_ERR_INVALID_ARG, "token out of range");
-  if (!c->prefilled) return fail(c, LA_ERR_STATE, "la_seed_pool before la_prefill");
+  if (!c->prefilled[sq]) return fail(c, LA_ERR_STATE, "la_seed_pool before la_prefill");
   const int n1 = g.N - 1;
   if (g.G == 0 || n <= n1) return LA_OK;
   LA_HIP(c, hipStreamSynchronize(c->stream));
@@ -767,7 +833,8 @@ la_status la_seed_pool(la_ctx* c, const int32_t* seq, int32_t n) {
     memcpy(c->pin, seq + p0, sizeof(int32_t) * m);
     LA_HIP(c, hipMemcpyAsync(c->prompt_buf, c->pin, sizeof(int32_t) * m, hipMemcpyHostToDevice,
                              c->stream));
-    launch_seed_pool(c->prompt_buf, m, c->pool_len, c->pool, g.N, g.G, c->stream);
+    launch_seed_pool(c->prompt_buf, m, c->pool_len + (size_t)sq * g.vocab, c->pool + sq * c->pool_seq,
+                     g.N, g.G, c->stream);
     LA_HIP(c, hipGetLastError());
     LA_HIP(c, hipStreamSynchronize(c->stream));
   }
@@ -775,9 +842,14 @@ la_status la_seed_pool(la_ctx* c, const int32_t* seq, int32_t n) {
 }
 
 la_status la_debug_pool_insert(la_ctx* c, int32_t key, const int32_t* tail) {
+  return la_debug_pool_insert_seq(c, 0, key, tail);
+}
+
+la_status la_debug_pool_insert_seq(la_ctx* c, int32_t sq, int32_t key, const int32_t* tail) {
   la_status us = check_usable(c);
   if (us != LA_OK) return us;
   const la_config& g = c->cfg;
+  if (sq < 0 || sq >= c->B) return fail(c, LA_ERR_INVALID_ARG, "sequence index out of range");
   if (!tail || key < 0 || key >= g.vocab) return fail(c, LA_ERR_INVALID_ARG, "key/tail");
   for (int i = 0; i < g.N - 1; i++)
     if (tail[i] < 0 || tail[i] >= g.vocab) return fail(c, LA_ERR_INVALID_ARG, "tail token out of range");
@@ -785,7 +857,8 @@ la_status la_debug_pool_insert(la_ctx* c, int32_t key, const int32_t* tail) {
   memcpy(c->pin, tail, sizeof(int32_t) * (g.N - 1));
   LA_HIP(c, hipMemcpyAsync(c->tail_buf, c->pin, sizeof(int32_t) * (g.N - 1), hipMemcpyHostToDevice,
                            c->stream));
-  launch_pool_insert(c->st, key, c->tail_buf, c->pool_len, c->pool, g.N, g.G, c->stream);
+  launch_pool_insert(c->st + sq, key, c->tail_buf, c->pool_len + (size_t)sq * g.vocab,
+                     c->pool + sq * c->pool_seq, g.N, g.G, c->stream);
   LA_HIP(c, hipGetLastError());
   LA_HIP(c, hipStreamSynchronize(c->stream));
   return LA_OK;
@@ -800,7 +873,8 @@ la_status la_debug_kv(la_ctx* c, int32_t layer, int32_t pos0, int32_t n, float* 
   LA_HIP(c, hipStreamSynchronize(c->stream));
   const int dh = g.head_dim, Hkv = g.n_kv_heads, es = c->elem;
   std::vector<char> kb((size_t)n * dh * es), vb((size_t)dh * n * es);
-  for (int h = 0; h < Hkv; h++) {
+  // sequence b's kv head hk is head b * Hkv + hk of the layer's cache
+  for (int h = 0; h < Hkv * c->B; h++) {
     const char* ks = (const char*)layer_k(c, layer) + (((size_t)h * c->ctx_stride + pos0) * dh) * es;
     LA_HIP(c, hipMemcpy(kb.data(), ks, kb.size(), hipMemcpyDeviceToHost));
     const char* vs = (const char*)layer_v(c, layer) + ((size_t)h * dh * c->ctx_stride + pos0) * es;
@@ -825,11 +899,13 @@ la_status la_debug_kv(la_ctx* c, int32_t layer, int32_t pos0, int32_t n, float* 
 la_status la_debug_state(la_ctx* c, int32_t* kv_len, int32_t* current) {
   la_status us = check_usable(c);
   if (us != LA_OK) return us;
-  DevState hs;
+  std::vector<DevState> hs(c->B);
   LA_HIP(c, hipStreamSynchronize(c->stream));
-  LA_HIP(c, hipMemcpy(&hs, c->st, sizeof(hs), hipMemcpyDeviceToHost));
-  if (kv_len) *kv_len = hs.L;
-  if (current) *current = hs.cur;
+  LA_HIP(c, hipMemcpy(hs.data(), c->st, sizeof(DevState) * c->B, hipMemcpyDeviceToHost));
+  for (int b = 0; b < c->B; b++) {
+    if (kv_len) kv_len[b] = hs[b].L;
+    if (current) current[b] = hs[b].cur;
+  }
   return LA_OK;
 }
 
@@ -871,6 +947,9 @@ la_status la_attention(const void* q, const void* k_cache, const void* vt_cache,
   aa.st = nullptr;
   aa.L_host = prefix_len;
   aa.M = (int)T;
+  aa.rps = (int)T;
+  aa.nseq = 1;
+  aa.kv_seq = 0;
   aa.mode = MODE_STEP;
   aa.H = n_heads;
   aa.Hkv = n_kv_heads;

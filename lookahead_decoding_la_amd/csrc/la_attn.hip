@@ -5,8 +5,9 @@
 // one forward pass; the method works with FlashAttention-style kernels).
 //
 // bf16 kernel (gfx950, head_dim 128):
-//   - grid = heads x KV splits (flash-decoding style split of the key range
-//     so short contexts still fill the CUs); one workgroup holds every query
+//   - grid = heads x KV splits x sequences (flash-decoding style split of
+//     the key range so short contexts still fill the CUs; each sequence of a
+//     batch attends to its own cache only); one workgroup holds every query
 //     row of its head (up to 128 rows with 8 waves: 4 row pairs x 2 key
 //     halves; up to 256 rows: 8 row pairs), so each K/V chunk is read from
 //     HBM once per head;
@@ -149,10 +150,11 @@ __global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
                 "key-part exchange fits in the ring");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[NBUF * CH_BYTES + QROWS * 256];
 
-  const int h = blockIdx.x, sp = blockIdx.y;
+  const int h = blockIdx.x, sp = blockIdx.y, sq = blockIdx.z;  // head, key split, sequence
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c16 = l & 15;
   const int rp = w % NRP, kp = w / NRP;
-  const int L = a.st ? a.st->L : a.L_host;
+  const int L = a.st ? a.st[sq].L : a.L_host;
+  const int r0 = sq * a.rps;  // the sequence's first row in q and out
   const int M = a.M;
   const int kvh = (h * a.Hkv) / a.H;
   const int ctx = L + M;
@@ -164,8 +166,8 @@ __global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
   const float sl2 = LOG2E / sqrtf((float)A_DH);
   const bool causal = a.mode == MODE_CAUSAL;
 
-  const uint16_t* kc = (const uint16_t*)a.k_cache + (size_t)kvh * a.ctx_stride * A_DH;
-  const uint16_t* vc = (const uint16_t*)a.vt_cache + (size_t)kvh * A_DH * a.ctx_stride;
+  const uint16_t* kc = (const uint16_t*)a.k_cache + sq * a.kv_seq + (size_t)kvh * a.ctx_stride * A_DH;
+  const uint16_t* vc = (const uint16_t*)a.vt_cache + sq * a.kv_seq + (size_t)kvh * A_DH * a.ctx_stride;
 
   // Row masks of this wave's two tiles (padding tokens take a valid row).
   // They are computed, not loaded: an ordinary global load in flight next
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
   for (int q = 0; q < QPT; q++) {
     const int j = w + q * NW;  // 1 KiB = 4 rows
     const int t = 4 * j + (l >> 4), sq = l & 15;
-    const uint16_t* gq = (const uint16_t*)a.q + (size_t)min(t, M - 1) * (a.H * A_DH) + h * A_DH +
+    const uint16_t* gq = (const uint16_t*)a.q + (size_t)(r0 + min(t, M - 1)) * (a.H * A_DH) + h * A_DH +
                          ((sq ^ (t & 15)) * 8);
     __builtin_amdgcn_global_load_lds((const void*)gq,
                                      (__attribute__((address_space(3))) void*)(qb + j * 1024), 16,
@@ -399,18 +401,18 @@ __global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
 #pragma unroll
       for (int dt = 0; dt < 8; dt++) {
         const int k = h * A_DH + dt * 16 + 4 * g;
-        const size_t o0 = a.out_mtt ? frag_index(t, k, a.out_mtt) : (size_t)t * (a.H * A_DH) + k;
+        const size_t o0 = a.out_mtt ? frag_index(r0 + t, k, a.out_mtt) : (size_t)(r0 + t) * (a.H * A_DH) + k;
         uint2 pk;
         pk.x = (uint32_t)f2bf(o[u][dt][0] * inv) | ((uint32_t)f2bf(o[u][dt][1] * inv) << 16);
         pk.y = (uint32_t)f2bf(o[u][dt][2] * inv) | ((uint32_t)f2bf(o[u][dt][3] * inv) << 16);
         *(uint2*)&out[o0] = pk;
       }
     } else {
-      float* po = a.part_o + (((size_t)h * a.splits + sp) * rows16 + t) * A_DH;
+      float* po = a.part_o + ((((size_t)sq * a.H + h) * a.splits + sp) * rows16 + t) * A_DH;
 #pragma unroll
       for (int dt = 0; dt < 8; dt++) *(f32x4*)&po[dt * 16 + 4 * g] = o[u][dt];
       if (g == 0) {
-        float* pm = a.part_ml + (((size_t)h * a.splits + sp) * rows16 + t) * 2;
+        float* pm = a.part_ml + ((((size_t)sq * a.H + h) * a.splits + sp) * rows16 + t) * 2;
         pm[0] = m_run[u];
         pm[1] = lsum[u];
       }
@@ -419,12 +421,14 @@ __global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
 }
 
 // Combine the splits of each (row, head) with log-sum-exp weights
-// 2^(m_s - m*).  A workgroup covers 8 rows of one head; a thread, 4 dims.
-// All splits' (m, l, O) are loaded up front (one round trip; splits <= 16).
+// 2^(m_s - m*).  A workgroup covers 8 rows of one head of one sequence
+// (grid z); a thread, 4 dims.  All splits' (m, l, O) are loaded up front
+// (one round trip; splits <= 16).
 constexpr int A_MAX_SPLITS = 16;
 
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const int h = blockIdx.y, t = blockIdx.x * 8 + (threadIdx.x >> 5), i = (threadIdx.x & 31) * 4;
+  const int sq = blockIdx.z;
   if (t >= a.M) return;
   const int rows16 = (a.M + 15) & ~15;
   float m[A_MAX_SPLITS], l[A_MAX_SPLITS];
@@ -432,7 +436,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 #pragma unroll
   for (int s = 0; s < A_MAX_SPLITS; s++) {
     if (s < a.splits) {
-      const size_t b = ((size_t)h * a.splits + s) * rows16 + t;
+      const size_t b = (((size_t)sq * a.H + h) * a.splits + s) * rows16 + t;
       const float2 ml = *(const float2*)&a.part_ml[b * 2];
       m[s] = ml.x;
       l[s] = ml.y;
@@ -455,7 +459,8 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   }
   const float inv = 1.f / den;
   const int k = h * A_DH + i;
-  const size_t oi = a.out_mtt ? frag_index(t, k, a.out_mtt) : (size_t)t * (a.H * A_DH) + k;
+  const int tg = sq * a.rps + t;
+  const size_t oi = a.out_mtt ? frag_index(tg, k, a.out_mtt) : (size_t)tg * (a.H * A_DH) + k;
   uint2 pk;
   pk.x = (uint32_t)f2bf(num[0] * inv) | ((uint32_t)f2bf(num[1] * inv) << 16);
   pk.y = (uint32_t)f2bf(num[2] * inv) | ((uint32_t)f2bf(num[3] * inv) << 16);
@@ -483,13 +488,13 @@ size_t attn_bf16_partial_floats(int H, int M, int splits, int dh) {
 }
 
 void launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
-  dim3 grid(a.H, a.splits);
+  dim3 grid(a.H, a.splits, a.nseq);
   if (a.M <= 128)
     hipLaunchKernelGGL((k_attn_bf16<4, 2, A_NBUF>), grid, dim3(512), 0, s, a);
   else
     hipLaunchKernelGGL((k_attn_bf16<8, 1, 2>), grid, dim3(512), 0, s, a);
   if (a.splits > 1)
-    hipLaunchKernelGGL(k_attn_merge, dim3((a.M + 7) / 8, a.H), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_attn_merge, dim3((a.M + 7) / 8, a.H, a.nseq), dim3(256), 0, s, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -498,14 +503,15 @@ void launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
 
 __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
   extern __shared__ float sc[];
-  const int t = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const int L = a.st ? a.st->L : a.L_host;
+  const int t = blockIdx.x, h = blockIdx.y, sq = blockIdx.z, tid = threadIdx.x;
+  const int L = a.st ? a.st[sq].L : a.L_host;
   const int M = a.M, dh = a.dh;
   const int kvh = (h * a.Hkv) / a.H;
   const int ctx = L + M;
-  const float* q = (const float*)a.q + (size_t)t * a.H * dh + (size_t)h * dh;
-  const float* kc = (const float*)a.k_cache + (size_t)kvh * a.ctx_stride * dh;
-  const float* vc = (const float*)a.vt_cache + (size_t)kvh * dh * a.ctx_stride;
+  const int tg = sq * a.rps + t;  // row in q and out
+  const float* q = (const float*)a.q + (size_t)tg * a.H * dh + (size_t)h * dh;
+  const float* kc = (const float*)a.k_cache + sq * a.kv_seq + (size_t)kvh * a.ctx_stride * dh;
+  const float* vc = (const float*)a.vt_cache + sq * a.kv_seq + (size_t)kvh * dh * a.ctx_stride;
   const RowDesc rd = row_desc(t, a.W, a.N);
   const float scale = 1.f / sqrtf((float)dh);
   float mx = -INFINITY;
@@ -529,7 +535,7 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
   }
   for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
   __syncthreads();
-  float* out = (float*)a.out + (size_t)t * a.H * dh + (size_t)h * dh;
+  float* out = (float*)a.out + (size_t)tg * a.H * dh + (size_t)h * dh;
   for (int i = tid; i < dh; i += 64) {
     const float* v = vc + (size_t)i * a.ctx_stride;
     float acc = 0.f;
@@ -539,7 +545,8 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
 }
 
 void launch_attn_f32(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_attn_f32, dim3(a.M, a.H), dim3(64), sizeof(float) * a.ctx_stride, s, a);
+  hipLaunchKernelGGL(k_attn_f32, dim3(a.M, a.H, a.nseq), dim3(64), sizeof(float) * a.ctx_stride, s,
+                     a);
 }
 
 }  // namespace la

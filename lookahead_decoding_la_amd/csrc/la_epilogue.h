@@ -31,13 +31,15 @@ __device__ inline void store_act<float>(void* base, size_t idx, float v) {
 __device__ inline float silu(float g) { return g / (1.0f + expf(-g)); }
 
 // Fused-QKV epilogue for the adjacent output columns (n, n+1), n even, of
-// row t: q and k are rotated by angle pos * theta^(-2i/dh) (i = pair index
-// within the head) at absolute position L + relpos[t] and stored; v goes
-// to the transposed V cache.  Block row t's key/value sit at cache
-// position L + t.
+// row t (block row tl = t % rps of sequence b = t / rps): q and k are
+// rotated by angle pos * theta^(-2i/dh) (i = pair index within the head)
+// at absolute position L_b + relpos[t] and stored; v goes to the
+// transposed V cache.  The block row's key/value sit at cache position
+// L_b + tl of its sequence.
 template <typename ACT>
 __device__ inline void qkv_pair(const EpiArgs& ea, int t, int n, float v0, float v1) {
-  const int L = ea.st->L;
+  const int b = t / ea.rps, tl = t - b * ea.rps;
+  const int L = ea.st[b].L;
   const int dh = ea.dh;
   if (n < ea.qdim + ea.kvdim) {
     const int di = (n < ea.qdim ? n : n - ea.qdim) % dh;
@@ -51,13 +53,13 @@ __device__ inline void qkv_pair(const EpiArgs& ea, int t, int n, float v0, float
       store_act<ACT>(ea.out_act, o + 1, r1);
     } else {
       const int hk = (n - ea.qdim) / dh;
-      const size_t o = ((size_t)hk * ea.max_ctx + L + t) * dh + di;
+      const size_t o = b * ea.kv_seq + ((size_t)hk * ea.max_ctx + L + tl) * dh + di;
       store_act<ACT>(ea.k_cache, o, r0);
       store_act<ACT>(ea.k_cache, o + 1, r1);
     }
   } else {
     const int vv = n - ea.qdim - ea.kvdim, hk = vv / dh, di = vv % dh;
-    const size_t o = ((size_t)hk * dh + di) * ea.max_ctx + L + t;
+    const size_t o = b * ea.kv_seq + ((size_t)hk * dh + di) * ea.max_ctx + L + tl;
     store_act<ACT>(ea.vt_cache, o, v0);
     store_act<ACT>(ea.vt_cache, o + ea.max_ctx, v1);
   }

@@ -402,9 +402,11 @@ __global__ __launch_bounds__(256) void k_red_qkv(const float* __restrict__ P, in
   const int tl = tid >> 3, c0 = (tid & 7) * 16;
   const int t = blockIdx.y * RQ_TOK + tl;
   const int n0 = cb * 128 + c0;
-  const int L = ea.st->L;
   const bool is_v = cb * 128 >= ea.qdim + ea.kvdim;
   const int tc = min(t, M - 1);  // rows past M repeat a valid row, never stored
+  // block row tq of sequence b (its state and caches)
+  const int b = tc / ea.rps, tq = tc - b * ea.rps;
+  const int L = ea.st[b].L;
   float v[16];
   {
     const float* pr = P + (size_t)tc * N + n0;
@@ -445,7 +447,7 @@ __global__ __launch_bounds__(256) void k_red_qkv(const float* __restrict__ P, in
         dst = (uint16_t*)ea.out_act + (size_t)t * ea.qdim + n0;
       } else {
         const int hk = (n0 - ea.qdim) >> 7;
-        dst = (uint16_t*)ea.k_cache + ((size_t)hk * ea.max_ctx + L + t) * 128 + c0;
+        dst = (uint16_t*)ea.k_cache + b * ea.kv_seq + ((size_t)hk * ea.max_ctx + L + tq) * 128 + c0;
       }
       uint4 a, b;
       a.x = o[0] | ((uint32_t)o[1] << 16); a.y = o[2] | ((uint32_t)o[3] << 16);
@@ -461,12 +463,15 @@ __global__ __launch_bounds__(256) void k_red_qkv(const float* __restrict__ P, in
   for (int e = 0; e < 16; e++) vt[tl][c0 + e] = v[e];
   __syncthreads();
   // V^T[hk][d][L + t]: lane = token, so one store instruction writes
-  // contiguous positions of two dimension rows
+  // contiguous positions of two dimension rows (of one sequence, unless
+  // the 32 tokens straddle two)
   const int hk = (cb * 128 - ea.qdim - ea.kvdim) >> 7;
   const int tt = tid & 31, dg = tid >> 5;
   const int tw = blockIdx.y * RQ_TOK + tt;
   if (tw < M) {
-    uint16_t* base = (uint16_t*)ea.vt_cache + (size_t)hk * 128 * ea.max_ctx + L + tw;
+    const int bw = tw / ea.rps, tlw = tw - bw * ea.rps;
+    uint16_t* base = (uint16_t*)ea.vt_cache + bw * ea.kv_seq + (size_t)hk * 128 * ea.max_ctx +
+                     ea.st[bw].L + tlw;
 #pragma unroll
     for (int e = 0; e < 16; e++) {
       const int d = dg * 16 + e;

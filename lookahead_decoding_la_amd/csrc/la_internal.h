@@ -137,14 +137,20 @@ struct ModelDims {
 // GEMM epilogues.
 enum { EPI_LOGITS = 0, EPI_RESID = 1, EPI_QKV = 2, EPI_SWIGLU = 3 };
 
+// Batched rows: row t belongs to sequence t / rps (relative to the state
+// and cache pointers, which point at the first sequence the launch covers)
+// and is that sequence's block row t % rps.  Sequence b's caches start
+// b * kv_seq elements after the pointers.
 struct EpiArgs {
   int M;                 // valid rows
   float* out_f32;        // LOGITS: [M][N]; RESID: residual [M][N], added to
   void* out_act;         // SWIGLU: [M][ffn] activation; QKV: q [M][H*dh]
-  void* k_cache;         // QKV: [Hkv][max_ctx][dh] of this layer
-  void* vt_cache;        // QKV: [Hkv][dh][max_ctx] of this layer
-  const DevState* st;    // QKV: committed length L
+  void* k_cache;         // QKV: [seq][Hkv][max_ctx][dh] of this layer
+  void* vt_cache;        // QKV: [seq][Hkv][dh][max_ctx] of this layer
+  const DevState* st;    // QKV: committed length L, one state per sequence
   const int32_t* relpos; // QKV: relative position of each row
+  int rps;               // QKV: rows per sequence
+  size_t kv_seq;         // QKV: cache elements per sequence (Hkv*max_ctx*dh)
   const float* rope_cos; // [max_ctx][dh/2]
   const float* rope_sin;
   int qdim, kvdim, dh, max_ctx, ld_out;
@@ -209,19 +215,23 @@ void launch_gemm_f32(int epi, const float* X, const float* W, const float* W2,
                      int K, int N, int M, const EpiArgs& ea, hipStream_t s);
 
 // masked attention over the cache + block
+// Batched: sequence b (grid z) owns rows b*rps .. b*rps + M - 1 of q and
+// out, state st[b] and the caches b * kv_seq elements on.
 struct AttnArgs {
   const void* q;       // [rows][H*dh] (bf16 or f32)
-  const void* k_cache; // [Hkv][ctx_stride][dh]
-  const void* vt_cache;// [Hkv][dh][ctx_stride]
+  const void* k_cache; // [seq][Hkv][ctx_stride][dh]
+  const void* vt_cache;// [seq][Hkv][dh][ctx_stride]
   void* out;           // f32: [rows][H*dh]; bf16: fragment layout, MTT tiles
   int out_mtt;
-  const DevState* st;  // committed length L (device), or NULL: use L_host
+  const DevState* st;  // committed length L (device, per sequence), or NULL: use L_host
   int L_host;
-  int M;               // rows in the block (valid + padded candidate rows)
+  int M;               // rows of one sequence's block
+  int rps, nseq;       // row stride between sequences, sequences
+  size_t kv_seq;       // cache elements per sequence
   int mode;            // MODE_STEP / MODE_CAUSAL
   int H, Hkv, dh, ctx_stride, W, N;
-  float* part_o;       // split-KV partials [H][splits][rows16][dh]
-  float* part_ml;      // [H][splits][rows16][2]
+  float* part_o;       // split-KV partials [seq][H][splits][rows16][dh]
+  float* part_ml;      // [seq][H][splits][rows16][2]
   int splits;
 };
 void launch_attn_bf16(const AttnArgs& a, hipStream_t s);
@@ -233,9 +243,12 @@ void launch_attn_f32(const AttnArgs& a, hipStream_t s);
 void launch_fill_u32(void* p, uint32_t v, size_t n, hipStream_t s);
 // Also writes the first layer's normalized input: bf16 -> fragment layout
 // (xnf, MTT tiles, norm weight nw); f32 -> nothing (a separate RMSNorm).
+// Step mode: M = nseq * T rows, sequence b's state st[b], window
+// win + b*(N-1)*W and pool pool_len + b*V, pool + b*V*G*(N-1).  Causal
+// mode: one sequence (st, the prompt rows).
 void launch_assemble(int mode, const DevState* st, const int32_t* win,
                      const int32_t* pool_len, const int32_t* pool,
-                     const int32_t* prompt, int M, int W, int N, int G,
+                     const int32_t* prompt, int M, int T, int V, int W, int N, int G,
                      int32_t* tokens, int32_t* relpos, DevState* st_w,
                      const void* emb, int d, int bf16, float* x,
                      const uint16_t* nw, float eps, uint16_t* xnf, int MTT,
@@ -245,10 +258,12 @@ void launch_rmsnorm(const float* x, const void* w, int M, int d, float eps,
                     int bf16, void* out, hipStream_t s);
 void launch_argmax(const float* logits, int M, int V, int32_t* amax,
                    hipStream_t s);
+// one workgroup per sequence (rows b*T.., window, pool and result b)
 void launch_verify(DevState* st, const int32_t* tokens, const int32_t* amax,
-                   int32_t* win, int32_t* pool_len, int32_t* pool, int W,
+                   int32_t* win, int32_t* pool_len, int32_t* pool, int nseq, int V, int W,
                    int N, int G, DevResult* res, hipStream_t s);
-void launch_kv_compact(const DevState* st, int n_layers, int Hkv, int dh,
+// caches [layer][nseq][Hkv][...]
+void launch_kv_compact(const DevState* st, int nseq, int n_layers, int Hkv, int dh,
                        int max_ctx, int W, int N, int elem, void* k_cache,
                        void* vt_cache, hipStream_t s);
 void launch_advance(DevState* st, int M, const int32_t* amax, int set_cur,

@@ -34,11 +34,13 @@ void launch_fill_u32(void* p, uint32_t v, size_t n, hipStream_t s) {
 //   token (oldest entry first), or token 0 for an empty slot (such rows are
 //   isolated by the mask and never committed);
 //   causal mode: row r = prompt[r] at relative position r.
+// In step mode row r is block row r % T of sequence r / T, which has its own
+// state, window and pool.
 
 __global__ void k_assemble(int mode, const DevState* __restrict__ st,
                            const int32_t* __restrict__ win, const int32_t* __restrict__ pool_len,
                            const int32_t* __restrict__ pool, const int32_t* __restrict__ prompt,
-                           int W, int N, int G, int32_t* tokens, int32_t* relpos,
+                           int T, int V, int W, int N, int G, int32_t* tokens, int32_t* relpos,
                            DevState* st_w, const void* __restrict__ emb, int d, int bf16,
                            float* __restrict__ x, const uint16_t* __restrict__ nw, float eps,
                            uint16_t* __restrict__ xnf, int MTT, float* __restrict__ ssq,
@@ -47,16 +49,21 @@ __global__ void k_assemble(int mode, const DevState* __restrict__ st,
   __shared__ float sh[4];
   const int r = blockIdx.x;
   int tok, rp;
+  const DevState* sr = st;  // the row's sequence
   if (mode == MODE_STEP) {
-    const int cur = st->cur;
-    int nc = G > 0 ? pool_len[cur] : 0;
+    const int b = r / T, rl = r - b * T;
+    sr = st + b;
+    const int32_t* wb = win + (size_t)b * (N - 1) * W;
+    const int32_t* pb = pool + (size_t)b * V * G * (N - 1);
+    const int cur = sr->cur;
+    int nc = G > 0 ? pool_len[(size_t)b * V + cur] : 0;
     nc = nc < G ? nc : G;
-    const RowDesc rd = row_desc(r, W, N);
+    const RowDesc rd = row_desc(rl, W, N);
     rp = row_relpos(rd);
     if (rd.kind == 0) tok = cur;
-    else if (rd.kind == 1) tok = win[(rd.a - 1) * W + rd.b];
-    else tok = rd.a < nc ? pool[((size_t)cur * G + rd.a) * (N - 1) + (rd.b - 1)] : 0;
-    if (r == 0 && threadIdx.x == 0) st_w->n_cand = nc;
+    else if (rd.kind == 1) tok = wb[(rd.a - 1) * W + rd.b];
+    else tok = rd.a < nc ? pb[((size_t)cur * G + rd.a) * (N - 1) + (rd.b - 1)] : 0;
+    if (rl == 0 && threadIdx.x == 0) st_w[b].n_cand = nc;
   } else {
     tok = prompt[r];
     rp = r;
@@ -70,7 +77,7 @@ __global__ void k_assemble(int mode, const DevState* __restrict__ st,
     // this row's rotary factors (head_dim 128: 64 pairs), gathered once per
     // block for every layer's QKV reduce
     if (threadIdx.x < 128) {
-      const size_t pos = (size_t)(st->L + rp);
+      const size_t pos = (size_t)(sr->L + rp);
       const int i = threadIdx.x & 63;
       rope_rows[r * 128 + threadIdx.x] =
           threadIdx.x < 64 ? rope_cos[pos * 64 + i] : rope_sin[pos * 64 + i];
@@ -134,14 +141,14 @@ __global__ void k_assemble(int mode, const DevState* __restrict__ st,
 
 void launch_assemble(int mode, const DevState* st, const int32_t* win,
                      const int32_t* pool_len, const int32_t* pool, const int32_t* prompt,
-                     int M, int W, int N, int G, int32_t* tokens, int32_t* relpos,
+                     int M, int T, int V, int W, int N, int G, int32_t* tokens, int32_t* relpos,
                      DevState* st_w, const void* emb, int d, int bf16, float* x,
                      const uint16_t* nw, float eps, uint16_t* xnf, int MTT, float* ssq,
                      const float* rope_cos, const float* rope_sin, float* rope_rows,
                      hipStream_t s) {
   hipLaunchKernelGGL(k_assemble, dim3(M), dim3(256), 0, s, mode, st, win, pool_len, pool,
-                     prompt, W, N, G, tokens, relpos, st_w, emb, d, bf16, x, nw, eps, xnf, MTT,
-                     ssq, rope_cos, rope_sin, rope_rows);
+                     prompt, T, V, W, N, G, tokens, relpos, st_w, emb, d, bf16, x, nw, eps, xnf,
+                     MTT, ssq, rope_cos, rope_sin, rope_rows);
 }
 
 // ---------------------------------------------------------------------------
@@ -333,10 +340,11 @@ __device__ inline int pool_insert_list(int32_t* lst, int len, int n1, int G, con
   return len;
 }
 
+// One workgroup per sequence of the batch (its rows, window, pool, result).
 __global__ __launch_bounds__(64) void k_verify(DevState* st, const int32_t* __restrict__ tokens,
                                                const int32_t* __restrict__ amax, int32_t* win,
-                                               int32_t* pool_len, int32_t* pool, int W, int N,
-                                               int G, DevResult* res) {
+                                               int32_t* pool_len, int32_t* pool, int V, int W,
+                                               int N, int G, DevResult* res) {
   __shared__ int32_t ynew[256];
   __shared__ int32_t lwin[256];             // window, (N-1) x W <= 255
   __shared__ int32_t tail[32];
@@ -349,6 +357,16 @@ __global__ __launch_bounds__(64) void k_verify(DevState* st, const int32_t* __re
   const int T = 1 + (W + G) * n1;
   const int per = G * n1;  // ints per key list
   const bool staged = G > 0 && W > 0 && W * per <= POOL_LDS_INTS;
+  {
+    const int b = blockIdx.x;
+    st += b;
+    tokens += (size_t)b * T;
+    amax += (size_t)b * T;
+    win += (size_t)b * nwin;
+    pool_len += (size_t)b * V;
+    pool += (size_t)b * V * per;
+    res += b;
+  }
   // every global read that does not depend on another goes out first
   for (int i = lane; i < T; i += 64) {
     ltok[i] = tokens[i];
@@ -445,27 +463,30 @@ __global__ __launch_bounds__(64) void k_verify(DevState* st, const int32_t* __re
 }
 
 void launch_verify(DevState* st, const int32_t* tokens, const int32_t* amax, int32_t* win,
-                   int32_t* pool_len, int32_t* pool, int W, int N, int G, DevResult* res,
-                   hipStream_t s) {
-  hipLaunchKernelGGL(k_verify, dim3(1), dim3(64), 0, s, st, tokens, amax, win, pool_len, pool,
-                     W, N, G, res);
+                   int32_t* pool_len, int32_t* pool, int nseq, int V, int W, int N, int G,
+                   DevResult* res, hipStream_t s) {
+  hipLaunchKernelGGL(k_verify, dim3(nseq), dim3(64), 0, s, st, tokens, amax, win, pool_len, pool,
+                     V, W, N, G, res);
 }
 
 // ---------------------------------------------------------------------------
 // KV compaction: the accepted candidate rows (g*, 1..k), written at
 // L_old + row by the QKV epilogue, move to L_old + 1 .. L_old + k.  Row 0 is
 // already at L_old.  Sources never overlap other rows' destinations.
+// Grid (layer, kv head, sequence); caches [layer][sequence][kv head][...].
 
 template <typename E>
-__global__ void k_kv_compact(const DevState* __restrict__ st, int Hkv, int dh, int max_ctx,
-                             int W, int N, E* kc, E* vtc) {
+__global__ void k_kv_compact(const DevState* __restrict__ st, int nseq, int Hkv, int dh,
+                             int max_ctx, int W, int N, E* kc, E* vtc) {
+  const int layer = blockIdx.x, hk = blockIdx.y, sq = blockIdx.z;
+  st += sq;
   const int k = st->k;
   if (k == 0) return;
-  const int layer = blockIdx.x, hk = blockIdx.y;
   const int g = st->winner, L0 = st->L_old;
   const int src0 = L0 + 1 + (N - 1) * W + g * (N - 1);  // row (g, 1)
-  E* kb = kc + ((size_t)layer * Hkv + hk) * max_ctx * dh;
-  E* vb = vtc + ((size_t)layer * Hkv + hk) * dh * max_ctx;
+  const size_t head = ((size_t)layer * nseq + sq) * Hkv + hk;
+  E* kb = kc + head * max_ctx * dh;
+  E* vb = vtc + head * dh * max_ctx;
   for (int e = threadIdx.x; e < k * dh; e += blockDim.x) {
     const int i = e / dh, di = e % dh;
     kb[(size_t)(L0 + 1 + i) * dh + di] = kb[(size_t)(src0 + i) * dh + di];
@@ -473,15 +494,15 @@ __global__ void k_kv_compact(const DevState* __restrict__ st, int Hkv, int dh, i
   }
 }
 
-void launch_kv_compact(const DevState* st, int n_layers, int Hkv, int dh, int max_ctx, int W,
-                       int N, int elem, void* k_cache, void* vt_cache, hipStream_t s) {
-  dim3 grid(n_layers, Hkv);
+void launch_kv_compact(const DevState* st, int nseq, int n_layers, int Hkv, int dh, int max_ctx,
+                       int W, int N, int elem, void* k_cache, void* vt_cache, hipStream_t s) {
+  dim3 grid(n_layers, Hkv, nseq);
   if (elem == 2)
-    hipLaunchKernelGGL(k_kv_compact<uint16_t>, grid, dim3(256), 0, s, st, Hkv, dh, max_ctx, W, N,
-                       (uint16_t*)k_cache, (uint16_t*)vt_cache);
+    hipLaunchKernelGGL(k_kv_compact<uint16_t>, grid, dim3(256), 0, s, st, nseq, Hkv, dh, max_ctx,
+                       W, N, (uint16_t*)k_cache, (uint16_t*)vt_cache);
   else
-    hipLaunchKernelGGL(k_kv_compact<uint32_t>, grid, dim3(256), 0, s, st, Hkv, dh, max_ctx, W, N,
-                       (uint32_t*)k_cache, (uint32_t*)vt_cache);
+    hipLaunchKernelGGL(k_kv_compact<uint32_t>, grid, dim3(256), 0, s, st, nseq, Hkv, dh, max_ctx,
+                       W, N, (uint32_t*)k_cache, (uint32_t*)vt_cache);
 }
 
 // ---------------------------------------------------------------------------

@@ -59,19 +59,30 @@ class Lockstep:
             assert np.array_equal(lg_tails[key][:lo_len[key]], lo_tails[key][:lo_len[key]])
 
     def step(self):
-        cfg = self.cfg
         rg = self.dev.step()
         lg_g = self.dev.debug_logits()
         tok_g, amax_g = self.dev.debug_block()
-        tok_o, valid, nc = self.orc.block_tokens()
+        win_g = self.dev.debug_window() if self.cfg.W else None
+        pool_g = self.dev.debug_pool() if self.cfg.G else None
+        self._compare(self.orc, rg, lg_g, tok_g, amax_g, win_g, pool_g,
+                      self.dev.debug_state())
+        self.steps.append(rg)
+        return rg
+
+    def _compare(self, orc, rg, lg_g, tok_g, amax_g, win_g, pool_g, state_g):
+        """One sequence's step on the device (its rows' logits, tokens and
+        argmax, result, window, pool, state) against the oracle stepping the
+        same block from its own state."""
+        cfg = self.cfg
+        tok_o, valid, nc = orc.block_tokens()
         v = valid.astype(bool)
         assert nc == rg["n_candidates"], (nc, rg)
         assert np.array_equal(tok_g[v], tok_o[v])
-        lg_o = self.orc.forward_block(tok_o, valid, keep=True)
+        lg_o = orc.forward_block(tok_o, valid, keep=True)
         d = float(np.max(np.abs(lg_g[v].astype(np.float64) - lg_o[v])))
         self.max_diff = max(self.max_diff, d)
         assert d <= self.tol, f"logit diff {d} > {self.tol} at step {len(self.steps)}"
-        amax_o = self.orc.block_argmax()
+        amax_o = orc.block_argmax()
         for r in np.nonzero(v)[0]:
             if amax_g[r] != amax_o[r]:
                 m = margin(lg_o[r])
@@ -80,19 +91,17 @@ class Lockstep:
                     f"{amax_o[r]}, oracle margin {m}")
                 self.ties += 1
                 amax_o[r] = amax_g[r]
-        ro = self.orc.commit(amax_o)
+        ro = orc.commit(amax_o)
         assert ro == rg, (ro, rg)
         if cfg.W:
-            assert np.array_equal(self.dev.debug_window(), self.orc.window())
+            assert np.array_equal(win_g, orc.window())
         if cfg.G:
-            lg_len, lg_tails = self.dev.debug_pool()
-            lo_len, lo_tails = self.orc.pool()
+            lg_len, lg_tails = pool_g
+            lo_len, lo_tails = orc.pool()
             assert np.array_equal(lg_len, lo_len)
             mask = np.arange(cfg.G)[None, :] < lo_len[:, None]
             assert np.array_equal(lg_tails[mask], lo_tails[mask])
-        assert self.dev.debug_state() == (self.orc.kv_len, self.orc.current)
-        self.steps.append(rg)
-        return rg
+        assert state_g == (orc.kv_len, orc.current)
 
     def run(self, prompt, win, n_steps=None, M=None):
         out = [self.prefill(prompt, win)]
@@ -107,3 +116,59 @@ class Lockstep:
             ko, vo = self.orc.kv(layer, 0, L)
             assert np.max(np.abs(kg - ko)) <= tol
             assert np.max(np.abs(vg - vo)) <= tol
+
+
+class BatchLockstep(Lockstep):
+    """B sequences stepped together by one HIP context (one forward pass of
+    B blocks), each compared with an oracle of its own: a batched step is B
+    independent single-sequence steps."""
+
+    def __init__(self, cfg, weights, max_ctx, B, logit_tol, tie_margin=0.05):
+        self.cfg = cfg
+        self.B = B
+        self.tol = logit_tol
+        self.tie = tie_margin
+        self.dev = la.LookaheadDecoder(cfg, la.upload_weights(weights), max_ctx, batch=B)
+        self.orcs = [oracle.Oracle(cfg, weights, max_ctx) for _ in range(B)]
+        self.ties = 0
+        self.max_diff = 0.0
+        self.steps = []
+
+    def prefill(self, prompts, wins):
+        return [self.prefill_one(b, prompts[b], wins[b]) for b in range(self.B)]
+
+    def prefill_one(self, b, prompt, win):
+        """(Re)start sequence b alone, on the device and in its oracle."""
+        fg = self.dev.prefill(prompt, win, seq=b)
+        fo, lg = self.orcs[b].prefill(prompt, win, logits=True)
+        if fg != fo:
+            m = margin(lg[-1])
+            assert m <= self.tie, f"seq {b} prefill token {fg} vs oracle {fo}, margin {m}"
+            self.ties += 1
+            self.orcs[b].set_current(fg)
+        return fg
+
+    def step(self):
+        cfg, T = self.cfg, self.dev.T
+        rgs = self.dev.step()
+        lg_g = self.dev.debug_logits()
+        tok_g, amax_g = self.dev.debug_block()
+        win_g = self.dev.debug_window() if cfg.W else None
+        pool_g = self.dev.debug_pool() if cfg.G else None
+        states = self.dev.debug_state()
+        for b in range(self.B):
+            rows = slice(b * T, (b + 1) * T)
+            self._compare(self.orcs[b], rgs[b], lg_g[rows], tok_g[rows], amax_g[rows],
+                          win_g[b] if cfg.W else None,
+                          (pool_g[0][b], pool_g[1][b]) if cfg.G else None, states[b])
+        self.steps.append(rgs)
+        return rgs
+
+    def compare_kv(self, tol):
+        for b, orc in enumerate(self.orcs):
+            L = orc.kv_len
+            for layer in range(self.cfg.n_layers):
+                kg, vg = self.dev.debug_kv(layer, 0, L)
+                ko, vo = orc.kv(layer, 0, L)
+                assert np.max(np.abs(kg[b] - ko)) <= tol
+                assert np.max(np.abs(vg[b] - vo)) <= tol
