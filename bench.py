@@ -186,6 +186,58 @@ def sweep(cfg, dev_w, prompt, steps, warmup):
     return rows
 
 
+# (W, N, G, batches) of the batch sweep: rows per step = B * (1 + (W+G)(N-1))
+BATCH_SWEEP = [(15, 5, 15, (1, 2)), (7, 5, 7, (1, 2, 4)), (5, 3, 5, (1, 2, 4, 8, 12)),
+               (0, 5, 0, (1, 4, 16, 64, 128, 256))]
+
+
+def batch_sweep(cfg, dev_w, steps, warmup, prompt_len=128):
+    """Aggregate throughput as the batch grows: B sequences (their own
+    prompts and windows) stepped together by one context, for several step
+    shapes, up to 256 rows per forward pass.  Reports tokens/s summed over
+    the sequences, the step time, and the GEMM time and throughput (event-
+    timed step), i.e. where more rows stop being free."""
+    import lookahead_decoding_la_amd as la
+    import torch
+    out = []
+    for W, N, G, batches in BATCH_SWEEP:
+        c = cfg.with_(W=W, N=N, G=G, prompt_len=prompt_len)
+        for B in batches:
+            max_ctx = prompt_len + (warmup + steps + 2) * N + c.T + 64
+            dec = la.LookaheadDecoder(c, dev_w, max_ctx, batch=B)
+            for b in range(B):
+                p = lasynth.make_prompt(c, seed=b)
+                dec.prefill(p, lasynth.make_init_window(c, p, seed=b) if W else None, seq=b)
+            res = []
+            for _ in range(warmup):
+                dec.step()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                r = dec.step()
+                res.extend(r if B > 1 else [r])
+            torch.cuda.synchronize()
+            sec = time.perf_counter() - t0
+            _, prof = dec.profile_step()
+            dec.close()
+            tok = sum(x["n_emitted"] for x in res)
+            gemm_ms = sum(prof[k][0] for k in ("qkv", "o_proj", "gate_up", "down", "lm_head"))
+            fl = linear_flops(c, B * c.T)
+            r = {"W": W, "N": N, "G": G, "B": B, "rows": B * c.T,
+                 "ms_per_step": round(sec / steps * 1e3, 4),
+                 "tokens_per_step": round(tok / steps, 3),
+                 "tokens_per_s": round(tok / sec, 1),
+                 "kernel_ms_event_timed": {k: round(v[0], 4) for k, v in prof.items()},
+                 "gemm_ms_event_timed": round(gemm_ms, 4),
+                 "gemm_tflops": round(fl / (gemm_ms * 1e-3) / 1e12, 1),
+                 "step_weight_tbps": round(streamed_weight_bytes(c) / (sec / steps) / 1e12, 3)}
+            log(f"batch W={W:2d} N={N} G={G:2d} B={B:3d} rows={B * c.T:3d}: "
+                f"{r['ms_per_step']:.3f} ms/step, {r['tokens_per_step']:.2f} tok/step, "
+                f"{r['tokens_per_s']:.0f} tok/s, GEMMs {gemm_ms:.3f} ms ({r['gemm_tflops']} TFLOP/s)")
+            out.append(r)
+    return out
+
+
 def sweep_counters(run_dir):
     """MFMA busy fraction of the GEMM dispatches of each sweep setting, from
     a rocprofv3 run of `--sweep` with SQ_VALU_MFMA_BUSY_CYCLES and
@@ -267,6 +319,8 @@ def main():
     ap.add_argument("--sweep-counters", metavar="DIR",
                     help="MFMA busy fraction per sweep setting from a rocprofv3 counter run "
                          "of --sweep; prints one JSON line")
+    ap.add_argument("--batch-sweep", action="store_true",
+                    help="throughput vs batch size (sequences per step) and step shape")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only the copy kernel used to calibrate HBM counters")
     ap.add_argument("--write-traffic", nargs=4, metavar="DIR",
@@ -303,6 +357,11 @@ def main():
     if args.sweep:
         out = {"metric": "lookahead step ms vs W = G (N = %d)" % cfg.N, "config": cfg.name,
                "sweep": sweep(cfg, dev_w, prompt, args.steps, args.warmup)}
+        print(json.dumps(out), flush=True)
+        return
+    if args.batch_sweep:
+        out = {"metric": "tokens/s vs sequences per step", "config": cfg.name,
+               "batch_sweep": batch_sweep(cfg, dev_w, args.steps, args.warmup)}
         print(json.dumps(out), flush=True)
         return
     n_prof = 3
@@ -362,7 +421,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profiles(f"gate_up_{cfg.name}"),
-                "kernel": "k_gemm_bf16 (fused gate/up + SwiGLU)",
+                "kernel": "k_gemm_dma<8, 2, 1> (fused gate/up + SwiGLU)",
                 "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_s * 1e6, 2),
                 "avg_launch_us_step_events": round(gu_step * 1e3, 2)}
     dec.close()

@@ -489,7 +489,12 @@ size_t attn_bf16_partial_floats(int H, int M, int splits, int dh) {
 
 void launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.H, a.splits, a.nseq);
-  if (a.M <= 128)
+  // up to 32 rows (plain decode, small steps): 2 waves and a 2-chunk ring,
+  // 72 KiB of LDS, so two workgroups share a CU; up to 128 rows: 8 waves
+  // (4 row pairs x 2 key halves); up to 256: 8 row pairs
+  if (a.M <= 32)
+    hipLaunchKernelGGL((k_attn_bf16<1, 2, 2>), grid, dim3(128), 0, s, a);
+  else if (a.M <= 128)
     hipLaunchKernelGGL((k_attn_bf16<4, 2, A_NBUF>), grid, dim3(512), 0, s, a);
   else
     hipLaunchKernelGGL((k_attn_bf16<8, 1, 2>), grid, dim3(512), 0, s, a);
