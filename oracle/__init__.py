@@ -86,6 +86,12 @@ def lib():
             "orc_row_pos": (I, [C.POINTER(_Cfg), I]),
             "orc_visible": (I, [C.POINTER(_Cfg), I, I]),
             "orc_attention": (None, [C.POINTER(_Cfg), I, P, P, P, I, I32, D]),
+            "orc_philox4x32_10": (None, [C.POINTER(C.c_uint32), C.POINTER(C.c_uint32),
+                                         C.POINTER(C.c_uint32)]),
+            "orc_uniform": (C.c_double, [C.c_uint64, C.c_int64]),
+            "orc_sample_logits": (I, [D, I, C.c_double, I, C.c_double, C.c_double, D]),
+            "orc_block_select": (I, [P, I32, D]),
+            "orc_set_sampling": (I, [P, C.c_double, I, C.c_double, C.c_uint64]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -128,6 +134,30 @@ def row_pos(cfg, r: int) -> int:
 def visible(cfg, r: int, s: int) -> bool:
     c = make_cfg(cfg, 1)
     return bool(lib().orc_visible(C.byref(c), r, s))
+
+
+def philox4x32_10(ctr, key):
+    """Philox4x32-10 of a 4-word counter and a 2-word key (4 words out)."""
+    c = (C.c_uint32 * 4)(*[int(x) & 0xFFFFFFFF for x in ctr])
+    k = (C.c_uint32 * 2)(*[int(x) & 0xFFFFFFFF for x in key])
+    o = (C.c_uint32 * 4)()
+    lib().orc_philox4x32_10(c, k, o)
+    return [int(x) for x in o]
+
+
+def uniform(seed: int, pos: int) -> float:
+    """The uniform that draws the token at sequence position pos."""
+    return float(lib().orc_uniform(int(seed) & (2**64 - 1), int(pos)))
+
+
+def sample_logits(logits, temperature: float, top_k: int = 0, top_p: float = 1.0,
+                  u: float = 0.5):
+    """One draw from a row of logits: (token, margin); see the C source."""
+    lg = np.ascontiguousarray(logits, dtype=np.float64)
+    m = C.c_double()
+    t = lib().orc_sample_logits(_f64p(lg), lg.size, float(temperature), int(top_k),
+                                float(top_p), float(u), C.byref(m))
+    return int(t), float(m.value)
 
 
 def attention(cfg, L, q, k, v, bf16: bool, valid=None):
@@ -258,6 +288,23 @@ class Oracle:
         if lib().orc_block_argmax(self._h, _i32(a)[1]):
             raise RuntimeError("no block forwarded")
         return a
+
+    def block_select(self):
+        """Per-row decisions of the kept block (argmax for lookahead rows;
+        draws for the current-token and candidate rows when sampling) and
+        the draws' margins (NaN where no draw)."""
+        a = np.zeros(self.T, np.int32)
+        m = np.zeros(self.T, np.float64)
+        if lib().orc_block_select(self._h, _i32(a)[1], _f64p(m)):
+            raise RuntimeError("no block forwarded")
+        return a, m
+
+    def set_sampling(self, temperature: float, top_k: int = 0, top_p: float = 1.0,
+                     seed: int = 0) -> None:
+        """Draw the emitted tokens (temperature > 0) instead of the argmax."""
+        if lib().orc_set_sampling(self._h, float(temperature), int(top_k), float(top_p),
+                                  int(seed) & (2**64 - 1)):
+            raise ValueError("bad sampling parameters")
 
     def commit(self, amax=None) -> dict:
         r = _Res()

@@ -80,6 +80,10 @@ typedef struct orc {
   int32_t *btok, *bvalid;
   double *blk_k, *blk_v; /* [layer][T][kvdim] */
   double *logits;        /* [T][vocab] */
+  /* sampling (temperature 0: greedy) */
+  double temperature, top_p;
+  int32_t top_k;
+  uint64_t seed;
 } orc;
 
 /* ------------------------------------------------------------------------ */
@@ -336,6 +340,136 @@ static int argmax_f32(const double *lg, int V) {
 }
 
 /* ------------------------------------------------------------------------ */
+/* sampling (the pages say the method supports several
+ * sampling schemes but give no algorithm, so all of this is a reading)     */
+
+/* Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and
+ * Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC'11): ten rounds;
+ * each multiplies words 0 and 2 by two fixed 32-bit constants, keeps the
+ * low halves and mixes the high halves with words 1 and 3 and the key;
+ * the key advances by two Weyl increments between rounds. */
+void orc_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4]) {
+  uint32_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+  uint32_t k0 = key_in[0], k1 = key_in[1];
+  for (int r = 0; r < 10; r++) {
+    uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    uint32_t n1 = (uint32_t)p1;
+    uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    uint32_t n3 = (uint32_t)p0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* The uniform that draws the token at absolute sequence position pos
+ * (prompt tokens at 0..P-1, the first generated token at P): Philox with
+ * counter (pos low, pos high, 0, 0) and key (seed low, seed high); the top
+ * 24 bits of word 0 scaled by 2^-24, so u in [0, 1) is exact in fp32.
+ * Keying by position, not by step, makes a sampled lookahead run draw
+ * every token with the same uniform as plain sampled decoding. */
+double orc_uniform(uint64_t seed, int64_t pos) {
+  uint32_t ctr[4] = {(uint32_t)pos, (uint32_t)((uint64_t)pos >> 32), 0u, 0u};
+  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  orc_philox4x32_10(ctr, key, out);
+  return (double)(out[0] >> 8) * (1.0 / 16777216.0);
+}
+
+typedef struct { double z; int32_t i; } orc_zi;
+
+/* logit descending, lower token id first on equal logits */
+static int zi_cmp(const void *pa, const void *pb) {
+  const orc_zi *a = pa, *b = pb;
+  if (a->z != b->z) return a->z > b->z ? -1 : 1;
+  return a->i < b->i ? -1 : (a->i > b->i);
+}
+
+/*
+ * One draw from a row of logits (reading):
+ *   1. order the tokens by logit, descending, lower id first on ties;
+ *   2. keep the first top_k of them (all when top_k is 0 or >= V);
+ *   3. weights w = exp((z - z_max) / temperature) over the kept tokens;
+ *      with top_p < 1 keep the shortest prefix whose weight sum reaches
+ *      top_p times the kept total (at least one token);
+ *   4. return the first kept token whose running weight sum exceeds
+ *      u times the remaining total.
+ * The decision takes the logits rounded to fp32 (as the argmax does) and
+ * computes in double.  *margin (may be NULL) receives how far the draw is
+ * from changing: the smallest of the distance from u to the ends of the
+ * drawn token's interval and from the top-p cut to the running sums beside
+ * it (fractions of the totals), and the logit gap at the top-k cut over
+ * the temperature.  A logit error e moves each of these by about 2e/T at
+ * most.
+ */
+int orc_sample_logits(const double *lg, int V, double temperature, int top_k, double top_p,
+                      double u, double *margin) {
+  orc_zi *a = malloc(sizeof(orc_zi) * (size_t)V);
+  for (int j = 0; j < V; j++) {
+    a[j].z = (double)(float)lg[j];
+    a[j].i = j;
+  }
+  qsort(a, (size_t)V, sizeof(orc_zi), zi_cmp);
+  int n = (top_k > 0 && top_k < V) ? top_k : V;
+  double mg = INFINITY;
+  if (n < V) mg = (a[n - 1].z - a[n].z) / temperature;
+  double *w = malloc(sizeof(double) * (size_t)n);
+  double tot = 0.0;
+  for (int j = 0; j < n; j++) {
+    w[j] = exp((a[j].z - a[0].z) / temperature);
+    tot += w[j];
+  }
+  if (top_p < 1.0) {
+    const double cut = top_p * tot;
+    double run = 0.0;
+    int m = n;
+    for (int j = 0; j < n; j++) {
+      const double prev = run;
+      run += w[j];
+      if (run >= cut) {
+        m = j + 1;
+        double d = fmin(cut - prev, run - cut) / tot;
+        if (j == 0) d = (run - cut) / tot;  /* one token is always kept */
+        mg = fmin(mg, d);
+        break;
+      }
+    }
+    n = m;
+  }
+  double z2 = 0.0;
+  for (int j = 0; j < n; j++) z2 += w[j];
+  const double target = u * z2;
+  double run = 0.0;
+  int pick = n - 1;
+  for (int j = 0; j < n; j++) {
+    if (run + w[j] > target) {
+      pick = j;
+      break;
+    }
+    run += w[j];
+  }
+  mg = fmin(mg, fmin(target - run, run + w[pick] - target) / z2);
+  if (margin) *margin = mg;
+  const int tok = a[pick].i;
+  free(a);
+  free(w);
+  return tok;
+}
+
+/* The decision for a row whose output is the token at position pos:
+ * greedy argmax, or a draw with that position's uniform. */
+static int decide(const orc *o, const double *lg, int64_t pos, double *margin) {
+  if (o->temperature > 0.0)
+    return orc_sample_logits(lg, o->c.vocab, o->temperature, o->top_k, o->top_p,
+                             orc_uniform(o->seed, pos), margin);
+  if (margin) *margin = NAN;
+  return argmax_f32(lg, o->c.vocab);
+}
+
+/* ------------------------------------------------------------------------ */
 /* block layout and mask (reading of the Summary's 2D window + verification
  * branch in one pass)                                                      */
 
@@ -421,6 +555,7 @@ orc *orc_create(const orc_config *cfg, const void *const *weights) {
       c->G < 0 || c->max_ctx < 1)
     return NULL;
   orc *o = calloc(1, sizeof(orc));
+  if (o) o->top_p = 1.0; /* greedy until orc_set_sampling */
   o->c = *cfg;
   o->T = 1 + (c->W + c->G) * (c->N - 1);
   o->kvdim = c->n_kv_heads * c->head_dim;
@@ -499,7 +634,8 @@ int orc_extend(orc *o, const int32_t *seq, int n, double *logits_all) {
   forward(o, n, seq, pos, vis, bk, bv, lg, want);
   for (int r = 0; r < n; r++) commit_row(o, bk, bv, n, r, o->L + r);
   o->L += n;
-  int nxt = argmax_f32(lg + (size_t)(n - 1) * c->vocab, c->vocab);
+  /* the next token sits at position L: argmax, or a draw (sampling set) */
+  int nxt = decide(o, lg + (size_t)(n - 1) * c->vocab, o->L, NULL);
   if (!logits_all) free(lg);
   free(pos); free(vis); free(want); free(bk); free(bv);
   return nxt;
@@ -626,10 +762,45 @@ int orc_block_argmax(const orc *o, int32_t *amax) {
   return 0;
 }
 
+/* The decision of every valid row of the kept block: lookahead rows take
+ * the argmax (they only propose n-grams; reading); the current-token row
+ * and the candidate rows, whose outputs are the tokens verification emits,
+ * take decide() for their output position, L + relative position + 1.
+ * margin[T] (may be NULL) receives the draws' margins (NaN for argmax). */
+int orc_block_select(const orc *o, int32_t *sel, double *margin) {
+  if (!o->has_block) return -1;
+  for (int r = 0; r < o->T; r++) {
+    double m = NAN;
+    int k, a, b;
+    row_kind(&o->c, r, &k, &a, &b);
+    const double *lg = o->logits + (size_t)r * o->c.vocab;
+    if (!o->bvalid[r]) sel[r] = -1;
+    else if (k == 1) sel[r] = argmax_f32(lg, o->c.vocab);
+    else sel[r] = decide(o, lg, (int64_t)o->L + orc_row_pos(&o->c, r) + 1, &m);
+    if (margin) margin[r] = m;
+  }
+  return 0;
+}
+
+/* Sampling for the tokens this context emits from now on (temperature 0:
+ * greedy; top_k 0: no cut; top_p 1: no cut).  Returns -1 for bad values. */
+int orc_set_sampling(orc *o, double temperature, int top_k, double top_p, uint64_t seed) {
+  if (!(temperature >= 0.0) || top_k < 0 || !(top_p > 0.0 && top_p <= 1.0)) return -1;
+  o->temperature = temperature;
+  o->top_k = top_k;
+  o->top_p = top_p;
+  o->seed = seed;
+  return 0;
+}
+
 /*
- * Finish the step for the kept block, given the per-row argmax decisions
- * amax[T] (NULL: take the oracle's own).
- *   Verification (greedy): candidate g is accepted for k_g tokens, the
+ * Finish the step for the kept block, given the per-row decisions amax[T]
+ * (NULL: take the oracle's own, orc_block_select: argmax when greedy, the
+ * draws when sampling).
+ *   Verification (greedy; with sampling the same rule on the draws, so a
+ *   candidate token is accepted exactly when it equals the token drawn at
+ *   its position, which keeps every emitted token a draw from the model's
+ *   distribution given the tokens before it): candidate g is accepted for k_g tokens, the
  *   longest prefix with cand[g][0] == argmax(row 0) and cand[g][i] ==
  *   argmax(row (g, i)) for 1 <= i < k_g; the winner g* is the lowest g with
  *   the largest k_g.  Emit cand[g*][0..k-1] and then the next greedy token
@@ -647,7 +818,7 @@ int orc_commit(orc *o, const int32_t *amax_in, orc_result *res) {
   int T = o->T, n1 = c->N - 1, W = c->W;
   int32_t *amax = malloc(sizeof(int32_t) * T);
   if (amax_in) memcpy(amax, amax_in, sizeof(int32_t) * T);
-  else orc_block_argmax(o, amax);
+  else orc_block_select(o, amax, NULL);
   int nc = 0;
   for (int g = 0; g < c->G; g++) nc += o->bvalid[row_cand(c, g, 1)] != 0;
   int a0 = amax[0];
@@ -708,8 +879,9 @@ int orc_step(orc *o, orc_result *res, double *logits_out) {
   return rc;
 }
 
-/* Plain greedy decoding: after orc_prefill, each call appends the current
- * token (one row at position L) and returns the next greedy token. */
+/* Plain one-token decoding: after orc_prefill, each call appends the
+ * current token (one row at position L) and returns the next token (the
+ * argmax, or the draw at its position when sampling is set). */
 int orc_greedy_next(orc *o, double *logits_out) {
   int t = orc_extend(o, &o->cur, 1, logits_out);
   if (t < 0) return -1;
