@@ -149,6 +149,28 @@ la_status la_seed_pool(la_ctx *c, const int32_t *seq, int32_t n);
  * s = 0.  Errors: as la_seed_pool, LA_ERR_INVALID_ARG for s out of range. */
 la_status la_seed_pool_seq(la_ctx *c, int32_t s, const int32_t *seq, int32_t n);
 
+/* Sampling for sequence seq (0 <= seq < batch), from the next decision on
+ * (a prefill's first token included); kept across la_prefill_seq.
+ * temperature 0 (the state after la_create) selects the argmax (greedy
+ * decoding); temperature > 0 draws every emitted token: the tokens ordered
+ * by logit (descending, lower id first on ties), cut to the first top_k
+ * (0: no cut), weighted by exp((logit - max) / temperature), cut to the
+ * shortest prefix holding top_p (in (0, 1], 1: no cut) of the weight, and
+ * the first token whose running weight exceeds u times the total is drawn.
+ * u for the token at sequence position n (the prompt holds positions
+ * 0..n_prompt-1) is the top 24 bits of word 0 of Philox4x32-10 with counter
+ * (n low, n high, 0, 0) and key (seed low, seed high), times 2^-24.  A
+ * candidate token is accepted when it equals the draw at its position, so
+ * the output is exactly that of plain sampled decoding with the same seed
+ * (the method's pages: sampling is supported and the output distribution
+ * is unchanged; the scheme itself is this library's reading).  The
+ * lookahead window keeps taking the argmax.  Needs vocab <= 32768 when
+ * temperature > 0.
+ * Errors: LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED (vocab), LA_ERR_STATE,
+ * LA_ERR_HIP. */
+la_status la_set_sampling(la_ctx *c, int32_t seq, float temperature, int32_t top_k,
+                          float top_p, uint64_t seed);
+
 /* Destroy a context (NULL is fine).  Waits for the context's queued work. */
 la_status la_destroy(la_ctx *c);
 
@@ -175,7 +197,7 @@ enum {
   LA_PROF_LMHEAD = 5, /* LM head (logits) */
   LA_PROF_REDUCE = 6, /* split-K sums with fused epilogues (RoPE + KV write,
                          residual + RMSNorm) and RMSNorm kernels */
-  LA_PROF_OTHER = 7,  /* assembly, argmax, verification, KV compaction */
+  LA_PROF_OTHER = 7,  /* assembly, token selection, verification, KV compaction */
   LA_PROF_CLASSES = 8
 };
 la_status la_profile_step(la_ctx *c, float *ms, int32_t *launches,
@@ -198,7 +220,8 @@ la_status la_profile_kernel(la_ctx *c, int32_t klass, int32_t reps,
 /* Logits of the last step's rows, host float [batch * rows][vocab]; n =
  * element count of the buffer (must be >= batch * rows * vocab). */
 la_status la_debug_logits(la_ctx *c, float *host, size_t n);
-/* Tokens and per-row argmax of the last step, host int32 [batch * rows]
+/* Tokens and per-row decisions (argmax, or draw when sampling) of the last
+ * step, host int32 [batch * rows]
  * each (either may be NULL). */
 la_status la_debug_block(la_ctx *c, int32_t *tokens, int32_t *amax);
 /* Current windows, host int32 [batch][(N-1)*W] (level 1 first). */
@@ -244,6 +267,19 @@ la_status la_attention(const void *q, const void *k_cache,
                        int32_t prefix_len, int32_t ctx_stride, int32_t W,
                        int32_t N, int32_t G, void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/* ---- one draw per row on its own ---------------------------------------
+ * The draw la_set_sampling describes (temperature > 0), for rows of
+ * logits: out[r] = the token drawn from logits[r] with the uniform of
+ * sequence position positions[r].  Queued on the hipStream_t stream (NULL:
+ * the null stream), not waited for.
+ *   logits     DEVICE float [rows][vocab], vocab <= 32768
+ *   positions  DEVICE int64 [rows]
+ *   out        DEVICE int32 [rows]
+ * Errors: LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED (vocab), LA_ERR_HIP. */
+la_status la_sample(const float *logits, int32_t rows, int32_t vocab, float temperature,
+                    int32_t top_k, float top_p, uint64_t seed, const int64_t *positions,
+                    int32_t *out, void *stream);
 
 #ifdef __cplusplus
 }

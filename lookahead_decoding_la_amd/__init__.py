@@ -30,7 +30,7 @@ EXPORTS = [
     "la_debug_pool_insert", "la_debug_kv", "la_debug_state",
     "la_attention_workspace_bytes", "la_attention", "la_profile_step",
     "la_profile_kernel", "la_seed_pool", "la_prefill_seq", "la_seed_pool_seq",
-    "la_debug_pool_insert_seq",
+    "la_debug_pool_insert_seq", "la_set_sampling", "la_sample",
 ]
 
 PROF_CLASSES = ["qkv", "attention", "o_proj", "gate_up", "down", "lm_head",
@@ -98,6 +98,9 @@ def lib():
             "la_prefill_seq": (C.c_int, [P, I32, pi, I32, pi, pi]),
             "la_seed_pool_seq": (C.c_int, [P, I32, pi, I32]),
             "la_debug_pool_insert_seq": (C.c_int, [P, I32, I32, pi]),
+            "la_set_sampling": (C.c_int, [P, I32, C.c_float, I32, C.c_float, C.c_uint64]),
+            "la_sample": (C.c_int, [P, I32, I32, C.c_float, I32, C.c_float, C.c_uint64, P, P,
+                                    P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -226,6 +229,14 @@ class LookaheadDecoder:
         res = self._squeeze([_result(x) for x in r])
         return res, {c: (float(ms[i]), int(n[i])) for i, c in enumerate(PROF_CLASSES)}
 
+    def set_sampling(self, temperature: float, top_k: int = 0, top_p: float = 1.0,
+                     seed: int = 0, seq: int = 0) -> None:
+        """Draw sequence seq's tokens (temperature > 0) instead of taking the
+        argmax; temperature 0 returns to greedy decoding (la_set_sampling)."""
+        self._check(lib().la_set_sampling(self._h, int(seq), float(temperature), int(top_k),
+                                          float(top_p), int(seed) & (2**64 - 1)),
+                    "la_set_sampling")
+
     def seed_pool(self, tokens, seq: int = 0) -> None:
         """Insert every N-gram of tokens (e.g. the prompt) into sequence
         seq's pool, in position order; call after that sequence's prefill."""
@@ -307,6 +318,22 @@ class LookaheadDecoder:
         self._check(lib().la_debug_state(self._h, L.ctypes.data_as(pi), cur.ctypes.data_as(pi)),
                     "la_debug_state")
         return self._squeeze([(int(a), int(b)) for a, b in zip(L, cur)])
+
+
+def sample(logits, temperature, top_k, top_p, seed, positions, out=None, stream=None):
+    """One draw per row of device logits [rows][vocab] (fp32) with the
+    uniform of positions[r] (device int64); returns out (device int32)."""
+    import torch
+    rows, vocab = int(logits.shape[0]), int(logits.shape[1])
+    if out is None:
+        out = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    s = stream if stream is not None else torch.cuda.current_stream()
+    st = lib().la_sample(logits.data_ptr(), rows, vocab, float(temperature), int(top_k),
+                         float(top_p), int(seed) & (2**64 - 1), positions.data_ptr(),
+                         out.data_ptr(), s.cuda_stream)
+    if st != LA_OK:
+        raise LaError(st, "la_sample: " + lib().la_status_string(st).decode())
+    return out
 
 
 def attention(q, k_cache, vt_cache, out, n_heads, n_kv_heads, prefix_len, W, N, G,

@@ -83,6 +83,7 @@ struct la_ctx {
   // device carve-up (per-sequence arrays: sequence 0 first)
   DevState* st = nullptr;        // [B]
   DevResult* res_dev = nullptr;  // [B]
+  SampleParams* sparams = nullptr;  // [B]; zeros: argmax
   float *x = nullptr, *logits = nullptr, *rope_cos = nullptr, *rope_sin = nullptr;
   float *gpart = nullptr, *attn_po = nullptr, *attn_pml = nullptr;
   float* ssq = nullptr;  // bf16: per-row partial sums of squares (deferred RMSNorm)
@@ -169,6 +170,7 @@ size_t carve(la_ctx* c, void* base) {
   const int B = c->B, n1 = g.N - 1;
   c->st = cv.take<DevState>(B);
   c->res_dev = cv.take<DevResult>(B);
+  c->sparams = cv.take<SampleParams>(B);
   c->tail_buf = cv.take<int32_t>(32);
   c->tokens = cv.take<int32_t>(c->MR);
   c->relpos = cv.take<int32_t>(c->MR);
@@ -399,8 +401,9 @@ void enqueue_layers(la_ctx* c, const Pass& p, hipStream_t s, Prof* pf = nullptr)
   }
 }
 
-void enqueue_head(la_ctx* c, int M, hipStream_t s, Prof* pf = nullptr) {
+void enqueue_head(la_ctx* c, const Pass& p, hipStream_t s, Prof* pf = nullptr) {
   const la_config& g = c->cfg;
+  const int M = p.M;
   if (c->bf16) {
     // xnf already holds the final-norm'd rows
     P_BEGIN(LA_PROF_LMHEAD);
@@ -419,8 +422,10 @@ void enqueue_head(la_ctx* c, int M, hipStream_t s, Prof* pf = nullptr) {
                     g.vocab, M, ea, s);
     P_END();
   }
+  // each row's token: the argmax, or the draw the sequence's sampling asks for
   P_BEGIN(LA_PROF_OTHER);
-  launch_argmax(c->logits, M, g.vocab, c->amax, s);
+  launch_select(c->logits, M, g.vocab, c->T, p.mode, g.W, g.N, c->st + p.seq0, c->relpos,
+                c->sparams + p.seq0, c->amax, s);
   P_END();
 }
 
@@ -434,7 +439,7 @@ void enqueue_step(la_ctx* c, hipStream_t s, Prof* pf = nullptr) {
                   c->rope_cos, c->rope_sin, c->rope_rows, s);
   P_END();
   enqueue_layers(c, p, s, pf);
-  enqueue_head(c, p.M, s, pf);
+  enqueue_head(c, p, s, pf);
   P_BEGIN(LA_PROF_OTHER);
   launch_verify(c->st, c->tokens, c->amax, c->win, c->pool_len, c->pool, c->B, g.vocab, g.W,
                 g.N, g.G, c->res_dev, s);
@@ -641,8 +646,9 @@ la_status la_prefill_seq(la_ctx* c, int32_t seq, const int32_t* prompt, int32_t 
                     g.W, g.N, g.G, c->tokens, c->relpos, sst, c->emb, g.d_model, c->bf16, c->x,
                     (const uint16_t*)c->layers[0].anorm, g.rms_eps, c->xnf, c->MTT, c->ssq,
                     c->rope_cos, c->rope_sin, c->rope_rows, s);
-    enqueue_layers(c, prefill_pass(c, seq, m), s);
-    if (last) enqueue_head(c, m, s);
+    const Pass pp = prefill_pass(c, seq, m);
+    enqueue_layers(c, pp, s);
+    if (last) enqueue_head(c, pp, s);
     launch_advance(sst, m, c->amax, last ? 1 : 0, s);
     LA_HIP(c, hipGetLastError());
     LA_HIP(c, hipStreamSynchronize(s));
@@ -753,6 +759,28 @@ la_status la_profile_kernel(la_ctx* c, int32_t klass, int32_t reps, float* us_pe
   float ms = 0.f;
   LA_HIP(c, hipEventElapsedTime(&ms, c->events[0], c->events[1]));
   *us_per_launch = ms * 1e3f / reps;
+  return LA_OK;
+}
+
+la_status la_set_sampling(la_ctx* c, int32_t seq, float temperature, int32_t top_k, float top_p,
+                          uint64_t seed) {
+  la_status us = check_usable(c);
+  if (us != LA_OK) return us;
+  if (seq < 0 || seq >= c->B) return fail(c, LA_ERR_INVALID_ARG, "seq out of range");
+  if (!(temperature >= 0.f) || !std::isfinite(temperature) || top_k < 0 ||
+      !(top_p > 0.f && top_p <= 1.f))
+    return fail(c, LA_ERR_INVALID_ARG, "temperature >= 0, top_k >= 0, 0 < top_p <= 1");
+  if (temperature > 0.f && c->cfg.vocab > SAMPLE_MAX_VOCAB)
+    return fail(c, LA_ERR_UNSUPPORTED, "sampling needs vocab <= 32768");
+  SampleParams h;
+  memset(&h, 0, sizeof(h));
+  h.temperature = temperature;
+  h.top_k = top_k;
+  h.top_p = top_p;
+  h.seed_lo = (uint32_t)seed;
+  h.seed_hi = (uint32_t)(seed >> 32);
+  LA_HIP(c, hipStreamSynchronize(c->stream));
+  LA_HIP(c, hipMemcpy(c->sparams + seq, &h, sizeof(h), hipMemcpyHostToDevice));
   return LA_OK;
 }
 
@@ -958,6 +986,26 @@ la_status la_attention(const void* q, const void* k_cache, const void* vt_cache,
   aa.W = W;
   aa.N = N;
   launch_attn_bf16(aa, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+la_status la_sample(const float* logits, int32_t rows, int32_t vocab, float temperature,
+                    int32_t top_k, float top_p, uint64_t seed, const int64_t* positions,
+                    int32_t* out, void* stream) {
+  if (!logits || !positions || !out || rows < 0 || vocab < 1) return LA_ERR_INVALID_ARG;
+  if (!(temperature > 0.f) || !std::isfinite(temperature) || top_k < 0 ||
+      !(top_p > 0.f && top_p <= 1.f))
+    return LA_ERR_INVALID_ARG;
+  if (vocab > SAMPLE_MAX_VOCAB) return LA_ERR_UNSUPPORTED;
+  if (rows == 0) return LA_OK;
+  SampleParams p;
+  memset(&p, 0, sizeof(p));
+  p.temperature = temperature;
+  p.top_k = top_k;
+  p.top_p = top_p;
+  p.seed_lo = (uint32_t)seed;
+  p.seed_hi = (uint32_t)(seed >> 32);
+  launch_sample_rows(logits, rows, vocab, p, positions, out, (hipStream_t)stream);
   return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 

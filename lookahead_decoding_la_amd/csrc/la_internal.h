@@ -84,6 +84,17 @@ struct DevResult {
 // Mask modes of a forwarded block.
 enum { MODE_STEP = 0, MODE_CAUSAL = 1 };
 
+// Per-sequence token selection: temperature 0 takes the argmax; otherwise
+// the emitted tokens are draws (la_sample.hip).
+struct SampleParams {
+  float temperature;  // 0: argmax
+  float top_p;        // (0, 1], 1: no cut
+  int32_t top_k;      // 0: no cut
+  uint32_t seed_lo, seed_hi;
+  int32_t pad[3];
+};
+constexpr int SAMPLE_MAX_VOCAB = 32768;  // 1024 threads x 32 logits per row
+
 // ---------------------------------------------------------------------------
 // Block-row layout of one lookahead step ("Break the Sequential Dependency of
 // LLM Inference Using Lookahead Decoding", Summary: the lookahead branch's 2D
@@ -256,8 +267,18 @@ void launch_assemble(int mode, const DevState* st, const int32_t* win,
                      float* rope_rows, hipStream_t s);
 void launch_rmsnorm(const float* x, const void* w, int M, int d, float eps,
                     int bf16, void* out, hipStream_t s);
-void launch_argmax(const float* logits, int M, int V, int32_t* amax,
-                   hipStream_t s);
+// The decision of each row (la_sample.hip): step mode (rows b*T.., state
+// st[b], parameters sp[b]): lookahead rows and empty candidate slots take
+// the argmax, the current-token and candidate rows a draw when sampling is
+// on; causal mode (one sequence): row M-1 as the current-token row, the
+// others the argmax.  A draw for the token at position L + relpos + 1.
+void launch_select(const float* logits, int M, int V, int T, int mode, int W, int N,
+                   const DevState* st, const int32_t* relpos, const SampleParams* sp,
+                   int32_t* out, hipStream_t s);
+// Draws from rows of logits with one parameter set, row r with the uniform
+// of position positions[r].
+void launch_sample_rows(const float* logits, int rows, int V, const SampleParams& p,
+                        const int64_t* positions, int32_t* out, hipStream_t s);
 // one workgroup per sequence (rows b*T.., window, pool and result b)
 void launch_verify(DevState* st, const int32_t* tokens, const int32_t* amax,
                    int32_t* win, int32_t* pool_len, int32_t* pool, int nseq, int V, int W,

@@ -1,6 +1,6 @@
 // Small kernels of the lookahead step: block assembly + embedding gather,
-// RMSNorm, per-row argmax, greedy verification with window shift and n-gram
-// pool update, KV compaction, and fills.
+// RMSNorm, greedy verification with window shift and n-gram pool update, KV
+// compaction, and fills.  (Per-row token selection: la_sample.hip.)
 //
 // Method source: "Break the Sequential Dependency of LLM Inference Using
 // Lookahead Decoding" (summary page).  Summary: the lookahead branch keeps a
@@ -192,67 +192,6 @@ void launch_rmsnorm(const float* x, const void* w, int M, int d, float eps, int 
                     void* out, hipStream_t s) {
   if (bf16) hipLaunchKernelGGL(k_rmsnorm<uint16_t>, dim3(M), dim3(256), 0, s, x, w, d, eps, out);
   else hipLaunchKernelGGL(k_rmsnorm<float>, dim3(M), dim3(256), 0, s, x, w, d, eps, out);
-}
-
-// ---------------------------------------------------------------------------
-// Per-row argmax over the vocabulary, lowest token id on ties.
-
-__device__ inline void better(float& bv, int& bi, float v, int i) {
-  if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
-}
-
-__global__ __launch_bounds__(256) void k_argmax(const float* __restrict__ logits, int V,
-                                                int32_t* amax) {
-  __shared__ float sv[4];
-  __shared__ int si[4];
-  const int r = blockIdx.x;
-  const float* lg = logits + (size_t)r * V;
-  float bv = -INFINITY;
-  int bi = 0x7fffffff;
-  // float4 loads, 8 in flight per thread (V % 4 == 0 when vectorized)
-  if ((V & 3) == 0) {
-    const float4* l4 = (const float4*)lg;
-    const int V4 = V >> 2;
-    int i = threadIdx.x;
-    for (; i + 7 * 256 < V4; i += 8 * 256) {
-      float4 q[8];
-#pragma unroll
-      for (int u = 0; u < 8; u++) q[u] = l4[i + u * 256];
-#pragma unroll
-      for (int u = 0; u < 8; u++) {
-        const int b = (i + u * 256) * 4;
-        better(bv, bi, q[u].x, b);
-        better(bv, bi, q[u].y, b + 1);
-        better(bv, bi, q[u].z, b + 2);
-        better(bv, bi, q[u].w, b + 3);
-      }
-    }
-    for (; i < V4; i += 256) {
-      const float4 q = l4[i];
-      better(bv, bi, q.x, 4 * i);
-      better(bv, bi, q.y, 4 * i + 1);
-      better(bv, bi, q.z, 4 * i + 2);
-      better(bv, bi, q.w, 4 * i + 3);
-    }
-  } else {
-    for (int i = threadIdx.x; i < V; i += 256) better(bv, bi, lg[i], i);
-  }
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(bv, o);
-    const int oi = __shfl_xor(bi, o);
-    better(bv, bi, ov, oi);
-  }
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  if (l == 0) { sv[w] = bv; si[w] = bi; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int k = 1; k < 4; k++) better(bv, bi, sv[k], si[k]);
-    amax[r] = bi;
-  }
-}
-
-void launch_argmax(const float* logits, int M, int V, int32_t* amax, hipStream_t s) {
-  hipLaunchKernelGGL(k_argmax, dim3(M), dim3(256), 0, s, logits, V, amax);
 }
 
 // ---------------------------------------------------------------------------

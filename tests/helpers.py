@@ -23,3 +23,24 @@ def trajectory_rows(W, N, G, r):
             [la(ll, j) for ll in range(2, l + 1)]
     g, i = (r - 1 - n1 * W) // n1, 1 + (r - 1 - n1 * W) % n1
     return [0] + [cd(g, ii) for ii in range(1, i + 1)]
+
+
+def definition_probs(z, T, k, p):
+    """Probability of each token under the draw's definition, from its
+    description: tokens ordered by logit (fp32), descending, lower id first
+    on ties; the first k kept (all for k = 0); weights exp((z - z_max) / T);
+    the shortest prefix holding a fraction p of the weight kept; weights
+    renormalized over what is kept."""
+    import numpy as np
+    z = np.asarray(z, np.float32).astype(np.float64)
+    order = sorted(range(z.size), key=lambda j: (-z[j], j))
+    n = k if 0 < k < z.size else z.size
+    kept = order[:n]
+    w = np.exp((z[kept] - z[kept[0]]) / T)
+    if p < 1.0:
+        c = np.cumsum(w)
+        m = int(np.argmax(c >= p * c[-1])) + 1
+        kept, w = kept[:m], w[:m]
+    out = np.zeros(z.size)
+    out[kept] = w / w.sum()
+    return out

@@ -4,9 +4,11 @@ Each step the HIP library runs one lookahead step; the oracle forwards the
 same block from its own state and takes the same decisions.  Compared:
   - the block tokens (bit-exact);
   - the logits of every valid row (max |diff| <= logit_tol);
-  - every row's argmax: equal, or else the oracle's top-2 margin on that row
-    is <= tie_margin (an excused near-tie: the oracle adopts the HIP choice
-    and the count is reported);
+  - every row's decision: equal, or else excused: an argmax row whose
+    oracle top-2 margin is <= tie_margin, or a drawn row (sampling) whose
+    oracle draw margin is <= draw_tol (the draw sat that close to a
+    boundary, where logits within logit_tol can move it); the oracle adopts
+    the HIP choice and the count is reported;
   - the step result (accepted length, winner, emitted tokens, kv length),
     the window and the n-gram pool (bit-exact).
 """
@@ -27,23 +29,44 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def draw_tol(logit_tol, temperature):
+    """How close to a boundary a draw may sit and still flip when every
+    logit may be off by logit_tol: each weight moves by a factor of at most
+    exp(logit_tol / T), so a running sum, as a fraction of the total, moves
+    by about 2 logit_tol / T; twice that as the excuse."""
+    return 4.0 * logit_tol / temperature
+
+
 class Lockstep:
-    def __init__(self, cfg, weights, max_ctx, logit_tol, tie_margin=0.05):
+    def __init__(self, cfg, weights, max_ctx, logit_tol, tie_margin=0.05, sampling=None):
+        """sampling: (temperature, top_k, top_p, seed) for both sides, or None."""
         self.cfg = cfg
         self.tol = logit_tol
         self.tie = tie_margin
         self.dev = la.LookaheadDecoder(cfg, la.upload_weights(weights), max_ctx)
         self.orc = oracle.Oracle(cfg, weights, max_ctx)
+        self.sampling = sampling
+        if sampling:
+            self.dev.set_sampling(*sampling)
+            self.orc.set_sampling(*sampling)
         self.ties = 0
         self.max_diff = 0.0
         self.steps = []
+
+    def _first_token_excused(self, lg, n_prompt, sampling):
+        if sampling:
+            T, k, p, seed = sampling
+            m = oracle.sample_logits(lg[-1], T, k, p, oracle.uniform(seed, n_prompt))[1]
+            return m <= draw_tol(self.tol, T), m
+        m = margin(lg[-1])
+        return m <= self.tie, m
 
     def prefill(self, prompt, win):
         fg = self.dev.prefill(prompt, win)
         fo, lg = self.orc.prefill(prompt, win, logits=True)
         if fg != fo:
-            m = margin(lg[-1])
-            assert m <= self.tie, f"prefill token {fg} vs oracle {fo}, margin {m}"
+            ok, m = self._first_token_excused(lg, len(prompt), self.sampling)
+            assert ok, f"prefill token {fg} vs oracle {fo}, margin {m}"
             self.ties += 1
             self.orc.set_current(fg)
         return fg
@@ -65,11 +88,11 @@ class Lockstep:
         win_g = self.dev.debug_window() if self.cfg.W else None
         pool_g = self.dev.debug_pool() if self.cfg.G else None
         self._compare(self.orc, rg, lg_g, tok_g, amax_g, win_g, pool_g,
-                      self.dev.debug_state())
+                      self.dev.debug_state(), self.sampling)
         self.steps.append(rg)
         return rg
 
-    def _compare(self, orc, rg, lg_g, tok_g, amax_g, win_g, pool_g, state_g):
+    def _compare(self, orc, rg, lg_g, tok_g, amax_g, win_g, pool_g, state_g, sampling=None):
         """One sequence's step on the device (its rows' logits, tokens and
         argmax, result, window, pool, state) against the oracle stepping the
         same block from its own state."""
@@ -82,12 +105,15 @@ class Lockstep:
         d = float(np.max(np.abs(lg_g[v].astype(np.float64) - lg_o[v])))
         self.max_diff = max(self.max_diff, d)
         assert d <= self.tol, f"logit diff {d} > {self.tol} at step {len(self.steps)}"
-        amax_o = orc.block_argmax()
+        amax_o, dmarg = orc.block_select()
         for r in np.nonzero(v)[0]:
             if amax_g[r] != amax_o[r]:
-                m = margin(lg_o[r])
-                assert m <= self.tie, (
-                    f"step {len(self.steps)} row {r}: argmax {amax_g[r]} vs oracle "
+                if np.isnan(dmarg[r]):
+                    m, lim = margin(lg_o[r]), self.tie
+                else:
+                    m, lim = dmarg[r], draw_tol(self.tol, sampling[0])
+                assert m <= lim, (
+                    f"step {len(self.steps)} row {r}: token {amax_g[r]} vs oracle "
                     f"{amax_o[r]}, oracle margin {m}")
                 self.ties += 1
                 amax_o[r] = amax_g[r]
@@ -123,13 +149,20 @@ class BatchLockstep(Lockstep):
     B blocks), each compared with an oracle of its own: a batched step is B
     independent single-sequence steps."""
 
-    def __init__(self, cfg, weights, max_ctx, B, logit_tol, tie_margin=0.05):
+    def __init__(self, cfg, weights, max_ctx, B, logit_tol, tie_margin=0.05, sampling=None):
+        """sampling: per-sequence list of (temperature, top_k, top_p, seed)
+        or None entries (greedy), or None for an all-greedy batch."""
         self.cfg = cfg
         self.B = B
         self.tol = logit_tol
         self.tie = tie_margin
         self.dev = la.LookaheadDecoder(cfg, la.upload_weights(weights), max_ctx, batch=B)
         self.orcs = [oracle.Oracle(cfg, weights, max_ctx) for _ in range(B)]
+        self.seq_sampling = list(sampling) if sampling else [None] * B
+        for b, sp in enumerate(self.seq_sampling):
+            if sp:
+                self.dev.set_sampling(*sp, seq=b)
+                self.orcs[b].set_sampling(*sp)
         self.ties = 0
         self.max_diff = 0.0
         self.steps = []
@@ -142,8 +175,8 @@ class BatchLockstep(Lockstep):
         fg = self.dev.prefill(prompt, win, seq=b)
         fo, lg = self.orcs[b].prefill(prompt, win, logits=True)
         if fg != fo:
-            m = margin(lg[-1])
-            assert m <= self.tie, f"seq {b} prefill token {fg} vs oracle {fo}, margin {m}"
+            ok, m = self._first_token_excused(lg, len(prompt), self.seq_sampling[b])
+            assert ok, f"seq {b} prefill token {fg} vs oracle {fo}, margin {m}"
             self.ties += 1
             self.orcs[b].set_current(fg)
         return fg
@@ -160,7 +193,8 @@ class BatchLockstep(Lockstep):
             rows = slice(b * T, (b + 1) * T)
             self._compare(self.orcs[b], rgs[b], lg_g[rows], tok_g[rows], amax_g[rows],
                           win_g[b] if cfg.W else None,
-                          (pool_g[0][b], pool_g[1][b]) if cfg.G else None, states[b])
+                          (pool_g[0][b], pool_g[1][b]) if cfg.G else None, states[b],
+                          self.seq_sampling[b])
         self.steps.append(rgs)
         return rgs
 

@@ -26,6 +26,7 @@ import pytest
 
 import lasynth
 import oracle
+from helpers import definition_probs as _definition_probs
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -92,22 +93,6 @@ def test_draw_temperature():
     tot = 2.0 + math.exp(-2) + math.exp(-4)
     assert oracle.sample_logits(LG, 0.5, u=(2.0 + 0.5 * math.exp(-2)) / tot)[0] == 2
     assert oracle.sample_logits(LG, 0.5, u=(2.0 + math.exp(-2) + 0.5 * math.exp(-4)) / tot)[0] == 0
-
-
-def _definition_probs(z, T, k, p):
-    """Probabilities the definition gives each token (float64)."""
-    z = np.asarray(z, np.float32).astype(np.float64)
-    order = sorted(range(z.size), key=lambda j: (-z[j], j))
-    n = k if 0 < k < z.size else z.size
-    kept = order[:n]
-    w = np.exp((z[kept] - z[kept[0]]) / T)
-    if p < 1.0:
-        c = np.cumsum(w)
-        m = int(np.argmax(c >= p * c[-1])) + 1
-        kept, w = kept[:m], w[:m]
-    out = np.zeros(z.size)
-    out[kept] = w / w.sum()
-    return out
 
 
 SETTINGS = [(1.0, 0, 1.0), (0.7, 0, 1.0), (1.3, 10, 1.0), (1.0, 0, 0.8), (0.9, 25, 0.6)]
