@@ -364,8 +364,8 @@ def main():
                "batch_sweep": batch_sweep(cfg, dev_w, args.steps, args.warmup)}
         print(json.dumps(out), flush=True)
         return
-    n_prof = 3
-    total = args.warmup + args.steps + n_prof
+    n_prof, n_samp = 3, 16
+    total = args.warmup + args.steps + n_prof + n_samp
     max_ctx = cfg.prompt_len + (total + 2) * cfg.N + cfg.T + 64
     dec = la.LookaheadDecoder(cfg, dev_w, max_ctx)
     first = dec.prefill(prompt, win)
@@ -424,6 +424,16 @@ def main():
                 "kernel": "k_gemm_dma<8, 2, 1> (fused gate/up + SwiGLU)",
                 "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_s * 1e6, 2),
                 "avg_launch_us_step_events": round(gu_step * 1e3, 2)}
+    # the same step with sampled verification (temperature 0.8, top-k 50,
+    # top-p 0.95): the difference is the per-row draws
+    dec.set_sampling(0.8, 50, 0.95, 1)
+    torch.cuda.synchronize()
+    a = time.perf_counter()
+    for _ in range(n_samp):
+        dec.step()
+    torch.cuda.synchronize()
+    samp_ms = (time.perf_counter() - a) / n_samp * 1e3
+    log(f"sampled step (T 0.8, top-k 50, top-p 0.95): {samp_ms:.3f} ms/step")
     dec.close()
 
     plain = None
@@ -468,6 +478,8 @@ def main():
                    "rows_per_step": cfg.T, "prompt_len": cfg.prompt_len,
                    "kv_len_start": L0, "kv_len_end": L},
         "accepted_tokens_per_step": round(emitted / args.steps, 3),
+        "sampled_step_ms": {"ms_per_step": round(samp_ms, 4), "temperature": 0.8,
+                            "top_k": 50, "top_p": 0.95},
         "step_ms_p10_p50_p90": [round(float(np.percentile(per_ms, q)), 4) for q in (10, 50, 90)],
         "step_hbm_roofline": {"t_roof_ms": round(roof_s / args.steps * 1e3, 4),
                               "frac": round(roof_s / elapsed, 4),

@@ -18,34 +18,31 @@
 //     a draw from the model's distribution given the tokens before it, and
 //     a lookahead run emits what plain sampled decoding would.
 //
-// GPU design: one 1024-thread workgroup per row; the row's logits sit in
-// LDS (128 KiB, so V <= 32768) and thread t works on tokens t + 1024 i.  The order is
-// a 64-bit key per token: order-preserving bits of the fp32 logit, then the
-// complemented token id, so keys are distinct and "earlier in the order" is
-// "larger key".  A selection (the k-th key, or the key where the running
-// weight from the top passes a target) descends 4 bits at a time: per
-// level every thread bins its live tokens by the next digit (16 weight and
-// 16 count sums), a fixed-order block reduction gives the totals and every
-// thread takes the same digit; it stops when one token is left.  Sums run
-// in a fixed order, so a row's decision is the same on every run.
+// GPU design: one 1024-thread workgroup per row; thread t keeps, for the
+// tokens j = t + 1024 i (i < 32, so V <= 32768), the order key of the logit
+// (order-preserving bits of the fp32 value) and its weight in registers.
+// The draw order is by key, descending, then by token id, ascending.  A
+// selection (the k-th token in that order, or the token where the running
+// weight first reaches or exceeds a target) is a bitwise search for the
+// largest key whose running total (over tokens with key >= it) still meets
+// the target: one pass over the registers and one fixed-order block sum
+// per bit; equal keys are then told apart by a search over token ids.  Sums
+// run in a fixed order, so a row's decision is the same on every run.
 #include "la_epilogue.h"
 
 namespace la {
 
 namespace {
 
-constexpr int SEL_T = 1024;            // threads per row
+constexpr int SEL_T = 1024;  // threads per row
 constexpr int SEL_PER = SAMPLE_MAX_VOCAB / SEL_T;
 constexpr int SEL_WAVES = SEL_T / 64;
 
 struct SelShared {
-  float w[SEL_WAVES][16];
-  uint32_t c[SEL_WAVES][16];
-  float wt[16];
-  uint32_t ct[16];
-  float f[SEL_WAVES];
+  float f[2][SEL_WAVES];  // double-buffered: one barrier per block sum
+  uint32_t n[2][SEL_WAVES];
   int32_t i[SEL_WAVES];
-  unsigned long long key;
+  int32_t tok;
 };
 
 // Philox4x32-10: word 0 of the output block.
@@ -72,37 +69,80 @@ __device__ inline float uniform_at(uint32_t seed_lo, uint32_t seed_hi, long long
   return (float)(w >> 8) * (1.0f / 16777216.0f);
 }
 
-// Order key: larger = earlier in the draw order.
-__device__ inline unsigned long long order_key(float z, int j) {
-  uint32_t b = __float_as_uint(z);
-  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((unsigned long long)b << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)j);
+// Order key of a finite logit: larger logit, larger key (never 0).
+__device__ inline uint32_t order_key(float z) {
+  const uint32_t b = __float_as_uint(z);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ inline float wave_sum_f(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+// Sum over a wave in a fixed order with DPP lane moves (VALU, no LDS round
+// trip): within quads (quad_perm [1,0,3,2], [2,3,0,1]), then within rows of
+// 16 (row_ror 4, 8), so every lane holds its row's sum; the four row sums
+// are read from lanes 0, 16, 32, 48 and added in order.
+__device__ inline uint32_t row_sum_u(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);
   return v;
+}
+__device__ inline float row_sum_f(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+  return v;
+}
+__device__ inline float wave_sum_f(float v) {
+  v = row_sum_f(v);
+  return ((__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16))) +
+          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32))) +
+         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
 }
 __device__ inline uint32_t wave_sum_u(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v = row_sum_u(v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 0) +
+         (uint32_t)__builtin_amdgcn_readlane((int)v, 16) +
+         (uint32_t)__builtin_amdgcn_readlane((int)v, 32) +
+         (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
 }
 
-// Sum over the block in a fixed order (wave trees, then waves in order).
-__device__ inline float block_sum(float v, SelShared& sh) {
-  v = wave_sum_f(v);
-  if ((threadIdx.x & 63) == 0) sh.f[threadIdx.x >> 6] = v;
+// (weight, count) summed over the block in a fixed order; buf alternates
+// between calls so one barrier suffices.
+struct Pair {
+  float s;
+  uint32_t n;
+};
+__device__ inline Pair block_pair(float s, uint32_t n, SelShared& sh, int& buf) {
+  s = wave_sum_f(s);
+  n = wave_sum_u(n);
+  if ((threadIdx.x & 63) == 0) {
+    sh.f[buf][threadIdx.x >> 6] = s;
+    sh.n[buf][threadIdx.x >> 6] = n;
+  }
   __syncthreads();
-  float t = 0.f;
-  for (int q = 0; q < SEL_WAVES; q++) t += sh.f[q];
-  __syncthreads();
-  return t;
+  Pair p{0.f, 0u};
+  for (int q = 0; q < SEL_WAVES; q++) {
+    p.s += sh.f[buf][q];
+    p.n += sh.n[buf][q];
+  }
+  buf ^= 1;
+  return p;
 }
 
 // Largest logit, lowest id on ties, over the block.
-__device__ inline void block_argmax(float& bv, int& bi, SelShared& sh) {
+__device__ inline int block_argmax(const float (&z)[SEL_PER], int V, float* vmax, SelShared& sh) {
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+#pragma unroll
+  for (int e = 0; e < SEL_PER; e++) {
+    const int j = threadIdx.x + e * SEL_T;
+    if (j < V && z[e] > bv) {  // j ascends per thread: the first of equal values stays
+      bv = z[e];
+      bi = j;
+    }
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float ov = __shfl_xor(bv, o);
@@ -113,169 +153,156 @@ __device__ inline void block_argmax(float& bv, int& bi, SelShared& sh) {
     }
   }
   if ((threadIdx.x & 63) == 0) {
-    sh.f[threadIdx.x >> 6] = bv;
+    sh.f[0][threadIdx.x >> 6] = bv;
     sh.i[threadIdx.x >> 6] = bi;
   }
   __syncthreads();
-  bv = sh.f[0];
+  bv = sh.f[0][0];
   bi = sh.i[0];
   for (int q = 1; q < SEL_WAVES; q++)
-    if (sh.f[q] > bv || (sh.f[q] == bv && sh.i[q] < bi)) {
-      bv = sh.f[q];
+    if (sh.f[0][q] > bv || (sh.f[0][q] == bv && sh.i[q] < bi)) {
+      bv = sh.f[0][q];
       bi = sh.i[q];
     }
   __syncthreads();
-}
-
-// Walk the live tokens (key >= lo) from the largest key down and return
-// the key of the token where the running total first reaches the target:
-// by count (weighted false: the kth token, kth >= 1), or by weight
-// (running weight >= target, or > target when strict).  If rounding leaves
-// no digit that reaches it, the walk takes the last live digit.
-__device__ unsigned long long descend(const float* zl, float zmax, float invT, int V,
-                                      unsigned long long lo, bool weighted, uint32_t kth,
-                                      float target, bool strict, SelShared& sh) {
-  const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
-  unsigned long long prefix = 0ull, mask = 0ull;
-  float acc = 0.f;
-  uint32_t cacc = 0;
-  for (int shift = 60; shift >= 0; shift -= 4) {
-    float hw[16];
-    uint32_t hc[16];
-#pragma unroll
-    for (int d = 0; d < 16; d++) {
-      hw[d] = 0.f;
-      hc[d] = 0u;
-    }
-#pragma unroll 2
-    for (int e = 0; e < SEL_PER; e++) {
-      const int j = tid + e * SEL_T;
-      if (j >= V) break;
-      const float ze = zl[j];
-      const unsigned long long K = order_key(ze, j);
-      if (K < lo || (K & mask) != prefix) continue;
-      const int dg = (int)((K >> shift) & 15ull);
-      const float we = weighted ? expf((ze - zmax) * invT) : 0.f;
-#pragma unroll
-      for (int d = 0; d < 16; d++) {
-        hw[d] += dg == d ? we : 0.f;
-        hc[d] += dg == d ? 1u : 0u;
-      }
-    }
-#pragma unroll
-    for (int d = 0; d < 16; d++) {
-      hw[d] = wave_sum_f(hw[d]);
-      hc[d] = wave_sum_u(hc[d]);
-    }
-    if (ln == 0) {
-#pragma unroll
-      for (int d = 0; d < 16; d++) {
-        sh.w[wv][d] = hw[d];
-        sh.c[wv][d] = hc[d];
-      }
-    }
-    __syncthreads();
-    if (tid < 16) {
-      float s = 0.f;
-      uint32_t c = 0u;
-      for (int q = 0; q < SEL_WAVES; q++) {
-        s += sh.w[q][tid];
-        c += sh.c[q][tid];
-      }
-      sh.wt[tid] = s;
-      sh.ct[tid] = c;
-    }
-    __syncthreads();
-    // every thread takes the same digit from the same totals
-    int pick = -1, last = -1;
-    {
-      float a = acc;
-      uint32_t ca = cacc;
-      for (int d = 15; d >= 0; d--) {
-        const uint32_t c = sh.ct[d];
-        if (c == 0u) continue;
-        last = d;
-        const bool hit = weighted ? (strict ? a + sh.wt[d] > target : a + sh.wt[d] >= target)
-                                  : ca + c >= kth;
-        if (hit) {
-          pick = d;
-          break;
-        }
-        a += sh.wt[d];
-        ca += c;
-      }
-    }
-    if (pick < 0) pick = last < 0 ? 0 : last;  // (no live token cannot happen)
-    for (int d = 15; d > pick; d--) {
-      acc += sh.wt[d];
-      cacc += sh.ct[d];
-    }
-    const bool single = sh.ct[pick] == 1u;
-    prefix |= (unsigned long long)pick << shift;
-    mask |= 15ull << shift;
-    __syncthreads();  // the totals are rewritten by the next level
-    if (single) {
-      for (int e = 0; e < SEL_PER; e++) {
-        const int j = tid + e * SEL_T;
-        if (j >= V) break;
-        const unsigned long long K = order_key(zl[j], j);
-        if (K >= lo && (K & mask) == prefix) sh.key = K;
-      }
-      __syncthreads();
-      const unsigned long long k = sh.key;
-      __syncthreads();
-      return k;
-    }
-  }
-  return prefix;
-}
-
-// The row's argmax (lowest id on ties) from its copy in LDS.
-__device__ inline int row_argmax(const float* zl, int V, float* vmax, SelShared& sh) {
-  float bv = -INFINITY;
-  int bi = 0x7fffffff;
-  for (int j = threadIdx.x; j < V; j += SEL_T) {
-    const float v = zl[j];
-    if (v > bv) {  // j ascends: the first of equal values stays
-      bv = v;
-      bi = j;
-    }
-  }
-  block_argmax(bv, bi, sh);
   if (vmax) *vmax = bv;
   return bi;
 }
 
-// One row's draw; zl holds the row in LDS.
-__device__ int draw_row(const float* zl, int V, const SampleParams& p, float u, SelShared& sh) {
+// Tokens out of play carry key 0 (a real key is never 0).  A selection
+// returns (key, token) of the token in the draw order where the running
+// total over the tokens in play first meets the target: by count
+// (WEIGHTED false: the kth token) or by weight (>= target, or > target
+// when strict).  Rounding that leaves no such token gives the last token
+// in play.
+struct KeyTok {
+  uint32_t key;
+  int tok;
+};
+template <bool WEIGHTED>
+__device__ KeyTok select_token(const uint32_t (&k)[SEL_PER], const float (&w)[SEL_PER],
+                               uint32_t kth, float target, bool strict, SelShared& sh,
+                               int& buf) {
   const int tid = threadIdx.x;
-  float zmax;
-  row_argmax(zl, V, &zmax, sh);
-  const float invT = 1.f / p.temperature;  // weights exp((z - zmax) * invT), recomputed
-  unsigned long long lo = 0ull;
-  if (p.top_k > 0 && p.top_k < V)
-    lo = descend(zl, zmax, invT, V, 0ull, false, (uint32_t)p.top_k, 0.f, false, sh);
-  auto kept_sum = [&](unsigned long long lo_key) {
-    float s = 0.f;
-    for (int j = tid; j < V; j += SEL_T) {
-      const float ze = zl[j];
-      if (order_key(ze, j) >= lo_key) s += expf((ze - zmax) * invT);
-    }
-    return block_sum(s, sh);
+  auto meets = [&](float s, uint32_t n) {
+    return WEIGHTED ? (strict ? s > target : s >= target) : n >= kth;
   };
-  if (p.top_p < 1.f) {
-    const float zk = kept_sum(lo);
-    lo = descend(zl, zmax, invT, V, lo, true, 0u, p.top_p * zk, false, sh);
+  // running total of the tokens with key >= c (weights, or counts)
+  auto total_ge = [&](uint32_t c) {
+    float s = 0.f;
+    uint32_t n = 0u;
+#pragma unroll
+    for (int e = 0; e < SEL_PER; e++) {
+      if (WEIGHTED) s += k[e] >= c ? w[e] : 0.f;
+      else n += k[e] >= c ? 1u : 0u;
+    }
+    return block_pair(s, n, sh, buf);
+  };
+  // the largest key t whose running total meets the target
+  uint32_t t = 0u;
+  for (int bit = 31; bit >= 0; bit--) {
+    const uint32_t c = t | (1u << bit);
+    const Pair p = total_ge(c);
+    if (meets(p.s, p.n)) t = c;
   }
-  const float zs = kept_sum(lo);
-  const unsigned long long ks = descend(zl, zmax, invT, V, lo, true, 0u, u * zs, true, sh);
-  return (int)(0xFFFFFFFFu - (uint32_t)(ks & 0xFFFFFFFFull));
+  // the tokens at t (equal logits) go in id order
+  uint32_t ne = 0u;
+#pragma unroll
+  for (int e = 0; e < SEL_PER; e++) ne += (t != 0u && k[e] == t) ? 1u : 0u;
+  const uint32_t neq = block_pair(0.f, ne, sh, buf).n;
+  if (neq <= 1u) {
+    // one token at t; or none (rounding): the last token in play, i.e. the
+    // smallest key, highest id among equals
+    if (neq == 0u) {
+      uint32_t mk = 0xFFFFFFFFu;
+#pragma unroll
+      for (int e = 0; e < SEL_PER; e++)
+        if (k[e] != 0u) mk = min(mk, k[e]);
+      for (int o = 32; o > 0; o >>= 1) mk = min(mk, (uint32_t)__shfl_xor((int)mk, o));
+      if ((tid & 63) == 0) sh.n[buf][tid >> 6] = mk;
+      __syncthreads();
+      t = 0xFFFFFFFFu;
+      for (int q = 0; q < SEL_WAVES; q++) t = min(t, sh.n[buf][q]);
+      buf ^= 1;
+    }
+    int hi = -1;
+#pragma unroll
+    for (int e = 0; e < SEL_PER; e++)
+      if (k[e] == t) hi = tid + e * SEL_T;
+    for (int o = 32; o > 0; o >>= 1) hi = max(hi, __shfl_xor(hi, o));
+    if ((tid & 63) == 0) sh.i[tid >> 6] = hi;
+    __syncthreads();
+    int tok = -1;
+    for (int q = 0; q < SEL_WAVES; q++) tok = max(tok, sh.i[q]);
+    __syncthreads();
+    return KeyTok{t, tok};
+  }
+  // several tokens at t: the smallest id J with (total above t) + (their
+  // total up to J) meeting the target
+  const Pair above = t == 0xFFFFFFFFu ? Pair{0.f, 0u} : total_ge(t + 1u);
+  int J = 0;
+  for (int bit = 14; bit >= 0; bit--) {
+    const int c = J + (1 << bit) - 1;  // test ids <= c
+    float s = 0.f;
+    uint32_t n = 0u;
+#pragma unroll
+    for (int e = 0; e < SEL_PER; e++) {
+      const bool in = k[e] == t && tid + e * SEL_T <= c;
+      s += in ? w[e] : 0.f;
+      n += in ? 1u : 0u;
+    }
+    const Pair p = block_pair(s, n, sh, buf);
+    if (!meets(above.s + p.s, above.n + p.n)) J += 1 << bit;
+  }
+  return KeyTok{t, J};
 }
 
-// Copy a row of logits to LDS (and wait for every thread's part).
-__device__ inline void load_row(const float* __restrict__ row, int V, float* zl) {
-  for (int j = threadIdx.x; j < V; j += SEL_T) zl[j] = row[j];
-  __syncthreads();
+// Take the tokens after (key, tok) in the draw order out of play.
+__device__ inline void cut_after(uint32_t (&k)[SEL_PER], const KeyTok& kt) {
+#pragma unroll
+  for (int e = 0; e < SEL_PER; e++) {
+    const int j = threadIdx.x + e * SEL_T;
+    if (k[e] < kt.key || (k[e] == kt.key && j > kt.tok)) k[e] = 0u;
+  }
+}
+
+// One row's draw; z holds the thread's logits (tokens past V unused).
+__device__ int draw_row(const float (&z)[SEL_PER], int V, const SampleParams& p, float u,
+                        SelShared& sh) {
+  float zmax;
+  block_argmax(z, V, &zmax, sh);
+  const float invT = 1.f / p.temperature;
+  uint32_t k[SEL_PER];
+  float w[SEL_PER];
+#pragma unroll
+  for (int e = 0; e < SEL_PER; e++) {
+    const int j = threadIdx.x + e * SEL_T;
+    k[e] = j < V ? order_key(z[e]) : 0u;
+    w[e] = j < V ? expf((z[e] - zmax) * invT) : 0.f;
+  }
+  int buf = 0;
+  if (p.top_k > 0 && p.top_k < V)
+    cut_after(k, select_token<false>(k, w, (uint32_t)p.top_k, 0.f, false, sh, buf));
+  auto total = [&]() {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < SEL_PER; e++) s += k[e] != 0u ? w[e] : 0.f;
+    return block_pair(s, 0u, sh, buf).s;
+  };
+  if (p.top_p < 1.f) {
+    const float zk = total();
+    cut_after(k, select_token<true>(k, w, 0u, p.top_p * zk, false, sh, buf));
+  }
+  const float zs = total();
+  return select_token<true>(k, w, 0u, u * zs, true, sh, buf).tok;
+}
+
+__device__ inline void load_row(const float* __restrict__ row, int V, float (&z)[SEL_PER]) {
+#pragma unroll
+  for (int e = 0; e < SEL_PER; e++) {
+    const int j = threadIdx.x + e * SEL_T;
+    z[e] = j < V ? row[j] : -INFINITY;
+  }
 }
 
 __global__ __launch_bounds__(SEL_T) void k_select(const float* __restrict__ logits, int V, int M,
@@ -285,7 +312,6 @@ __global__ __launch_bounds__(SEL_T) void k_select(const float* __restrict__ logi
                                                   const SampleParams* __restrict__ sp,
                                                   int32_t* __restrict__ out) {
   __shared__ SelShared sh;
-  __shared__ float zl[SAMPLE_MAX_VOCAB];
   const int r = blockIdx.x;
   int b = 0;
   bool draw;
@@ -298,13 +324,14 @@ __global__ __launch_bounds__(SEL_T) void k_select(const float* __restrict__ logi
   }
   const SampleParams p = sp[b];
   draw = draw && p.temperature > 0.f;  // uniform over the workgroup
-  load_row(logits + (size_t)r * V, V, zl);
+  float z[SEL_PER];
+  load_row(logits + (size_t)r * V, V, z);
   int tok;
   if (draw) {
     const long long pos = (long long)st[b].L + relpos[r] + 1;
-    tok = draw_row(zl, V, p, uniform_at(p.seed_lo, p.seed_hi, pos), sh);
+    tok = draw_row(z, V, p, uniform_at(p.seed_lo, p.seed_hi, pos), sh);
   } else {
-    tok = row_argmax(zl, V, nullptr, sh);
+    tok = block_argmax(z, V, nullptr, sh);
   }
   if (threadIdx.x == 0) out[r] = tok;
 }
@@ -314,10 +341,10 @@ __global__ __launch_bounds__(SEL_T) void k_sample_rows(const float* __restrict__
                                                        const int64_t* __restrict__ positions,
                                                        int32_t* __restrict__ out) {
   __shared__ SelShared sh;
-  __shared__ float zl[SAMPLE_MAX_VOCAB];
   const int r = blockIdx.x;
-  load_row(logits + (size_t)r * V, V, zl);
-  const int tok = draw_row(zl, V, p, uniform_at(p.seed_lo, p.seed_hi, positions[r]), sh);
+  float z[SEL_PER];
+  load_row(logits + (size_t)r * V, V, z);
+  const int tok = draw_row(z, V, p, uniform_at(p.seed_lo, p.seed_hi, positions[r]), sh);
   if (threadIdx.x == 0) out[r] = tok;
 }
 

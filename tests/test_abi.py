@@ -82,3 +82,31 @@ def test_attention_argument_checks_without_gpu():
     assert lib.la_attention(one, one, one, one, 32, 32, 128, 200, 256, 15, 5, 15, one, 1 << 30, None) == la.LA_ERR_INVALID_ARG
     assert lib.la_attention(one, one, one, one, 32, 32, 128, 16, 256, 15, 5, 15, one, 8, None) == la.LA_ERR_OUT_OF_CAPACITY
     assert lib.la_attention_workspace_bytes(32, 128, 1152, 15, 5, 15) > 0
+
+
+def test_sampling_and_batch_argument_checks_without_gpu():
+    lib = la.lib()
+    one = C.c_void_p(1)
+    toks = (C.c_int32 * 4)(1, 2, 3, 4)
+    first = C.c_int32()
+    assert lib.la_set_sampling(None, 0, 0.8, 0, 1.0, 1) == la.LA_ERR_INVALID_ARG
+    assert lib.la_prefill_seq(None, 0, toks, 4, None, C.byref(first)) == la.LA_ERR_INVALID_ARG
+    assert lib.la_seed_pool_seq(None, 0, toks, 4) == la.LA_ERR_INVALID_ARG
+    assert lib.la_debug_pool_insert_seq(None, 0, 1, toks) == la.LA_ERR_INVALID_ARG
+    # la_sample validates before touching the device
+    assert lib.la_sample(None, 1, 16, 1.0, 0, 1.0, 0, one, one, None) == la.LA_ERR_INVALID_ARG
+    assert lib.la_sample(one, 1, 16, 0.0, 0, 1.0, 0, one, one, None) == la.LA_ERR_INVALID_ARG
+    assert lib.la_sample(one, 1, 16, 1.0, -1, 1.0, 0, one, one, None) == la.LA_ERR_INVALID_ARG
+    assert lib.la_sample(one, 1, 16, 1.0, 0, 0.0, 0, one, one, None) == la.LA_ERR_INVALID_ARG
+    assert lib.la_sample(one, 1, 16, 1.0, 0, 1.5, 0, one, one, None) == la.LA_ERR_INVALID_ARG
+    assert lib.la_sample(one, 1, 32769, 1.0, 0, 1.0, 0, one, one, None) == la.LA_ERR_UNSUPPORTED
+    assert lib.la_sample(one, 0, 16, 1.0, 0, 1.0, 0, one, one, None) == la.LA_OK
+
+
+def test_batch_config_limits():
+    import lasynth
+    cfg = lasynth.get_config("7b")                      # 121 rows per sequence
+    assert la.workspace_bytes(cfg, 1024, batch=2) > la.workspace_bytes(cfg, 1024, batch=1)
+    assert la.workspace_bytes(cfg, 1024, batch=3) == 0  # 363 rows > 256
+    assert la.workspace_bytes(cfg, 1024, batch=0) == la.workspace_bytes(cfg, 1024, batch=1)
+    assert la.workspace_bytes(cfg, 1024, batch=-1) == 0
