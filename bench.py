@@ -292,7 +292,23 @@ def cpu_baseline(cfg, prompt, win, n_steps=3):
         secs += time.perf_counter() - t0
         emitted += r["n_emitted"]
     log(f"cpu oracle: {n_steps} steps in {secs:.1f} s ({oracle.max_threads()} threads)")
-    del o, w
+    del o
+    # plain greedy decoding on the same oracle and weights (one row per token)
+    g = oracle.Oracle(cfg.with_(W=0, G=0), w, P + 8)
+    g.prefill(prompt[:P])
+    t0 = time.perf_counter()
+    n_plain = 3
+    for _ in range(n_plain):
+        g.greedy_next()
+    plain_s = time.perf_counter() - t0
+    del g, w
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")),
+                             "")
+    except OSError:
+        pass
     return {
         "value": emitted / secs,
         "unit": "tokens/s",
@@ -302,6 +318,9 @@ def cpu_baseline(cfg, prompt, win, n_steps=3):
                    f"model ({cfg.T} rows each, G candidates planted per step) after a "
                    f"{P}-token prompt: {secs:.1f} s, {emitted} tokens"),
         "ms_per_step": secs / n_steps * 1e3,
+        "plain_greedy_tokens_per_s": round(n_plain / plain_s, 3),
+        "nproc": os.cpu_count(),
+        "cpu_model": cpu_model,
     }
 
 
