@@ -137,6 +137,17 @@ constexpr float RESCALE_LOG2 = 8.f;
 // through LDS at the end.  Chunks go straight from HBM to LDS
 // (global_load_lds, no register staging) through a ring of NBUF buffers,
 // NBUF - 1 chunks ahead of the one being consumed.
+// Key splits used for a block over nch 64-key chunks (context + block),
+// chosen at run time from the committed length so one captured graph fits
+// every length: about three chunks per split, one split (no merge) for two
+// chunks or fewer, at most smax (the launch's grid and the partial buffers).
+// Measured at 121 rows and 32 heads: 1 split best at 2 chunks, 4 at 7-11,
+// 6 at 18, 8 at 33.
+__device__ inline int eff_splits(int nch, int smax) {
+  const int s = nch <= 2 ? 1 : (nch + 2) / 3;
+  return s < smax ? s : smax;
+}
+
 template <int NRP, int KSPL, int NBUF>
 __global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
   constexpr int NW = NRP * KSPL;
@@ -159,7 +170,9 @@ __global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
   const int kvh = (h * a.Hkv) / a.H;
   const int ctx = L + M;
   const int nch = (ctx + AKC - 1) / AKC;
-  const int cps = (nch + a.splits - 1) / a.splits;
+  const int S = eff_splits(nch, a.splits);
+  if (sp >= S) return;  // a split this length does not use (uniform; before any load)
+  const int cps = (nch + S - 1) / S;
   const int c0 = min(sp * cps, nch), c1 = min(nch, c0 + cps);
   const int nloc = c1 - c0;
   const int rows16 = (M + 15) & ~15;
@@ -394,7 +407,7 @@ __global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
     if (u == 1 && !act1) break;
     const int t = (2 * rp + u) * 16 + c16;
     if (t >= M) continue;
-    if (a.splits == 1) {
+    if (S == 1) {
       // row-major, or fragment layout (dims dt*16 + 4g + 0..3 stay adjacent)
       uint16_t* out = (uint16_t*)a.out;
       const float inv = 1.f / lsum[u];
@@ -429,13 +442,15 @@ constexpr int A_MAX_SPLITS = 16;
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const int h = blockIdx.y, t = blockIdx.x * 8 + (threadIdx.x >> 5), i = (threadIdx.x & 31) * 4;
   const int sq = blockIdx.z;
-  if (t >= a.M) return;
+  const int L = a.st ? a.st[sq].L : a.L_host;
+  const int S = eff_splits((L + a.M + AKC - 1) / AKC, a.splits);
+  if (t >= a.M || S == 1) return;  // one split wrote the output itself
   const int rows16 = (a.M + 15) & ~15;
   float m[A_MAX_SPLITS], l[A_MAX_SPLITS];
   f32x4 o[A_MAX_SPLITS];
 #pragma unroll
   for (int s = 0; s < A_MAX_SPLITS; s++) {
-    if (s < a.splits) {
+    if (s < S) {
       const size_t b = (((size_t)sq * a.H + h) * a.splits + s) * rows16 + t;
       const float2 ml = *(const float2*)&a.part_ml[b * 2];
       m[s] = ml.x;
@@ -446,12 +461,12 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   float mstar = -INFINITY;
 #pragma unroll
   for (int s = 0; s < A_MAX_SPLITS; s++)
-    if (s < a.splits) mstar = fmaxf(mstar, m[s]);
+    if (s < S) mstar = fmaxf(mstar, m[s]);
   float den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < A_MAX_SPLITS; s++) {
-    if (s < a.splits) {
+    if (s < S) {
       const float wgt = (m[s] == -INFINITY) ? 0.f : exp2f(m[s] - mstar);
       den += wgt * l[s];
       num += wgt * o[s];
@@ -469,17 +484,13 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 
 constexpr int A_NBUF = 4;  // ring depth (chunks) of the bf16 kernel
 
+// Splits the launch provides for (the grid's second dimension and the
+// partial buffers): what eff_splits asks for at the longest context.
 int attn_bf16_splits(int H, int M, int max_ctx) {
-  (void)M;
-  const int max_chunks = (max_ctx + AKC - 1) / AKC;
-  // about A_NBUF chunks per split at the largest context, and enough
-  // workgroups to spread over the CUs
-  int s = (max_chunks + A_NBUF - 1) / A_NBUF;
-  const int fill = (128 + H - 1) / H;
-  if (s < fill) s = fill;
-  if (s > max_chunks) s = max_chunks;
-  if (s > A_MAX_SPLITS) s = A_MAX_SPLITS;
-  return s < 1 ? 1 : s;
+  (void)H;
+  const int max_chunks = (max_ctx + M + AKC - 1) / AKC;
+  const int s = max_chunks <= 2 ? 1 : (max_chunks + 2) / 3;
+  return s < A_MAX_SPLITS ? s : A_MAX_SPLITS;
 }
 
 size_t attn_bf16_partial_floats(int H, int M, int splits, int dh) {

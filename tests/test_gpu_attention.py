@@ -1,8 +1,17 @@
 """One layer's masked attention kernel (la_attention) vs the oracle (GPU only).
 
 Kernel-only workload: 32 heads x 128, prefix 1024, 121 query rows (W15 N5
-G15), Q/K/V ~ N(0,1) in bf16.  Tolerance: max |diff| <= 1e-2 and relative
-Frobenius error <= 1e-2 (bf16 output rounding is 2^-9 relative).
+G15), Q/K/V ~ N(0,1) in bf16.
+
+Tolerance, from the kernel's arithmetic: the probabilities enter the PV
+product as bf16 and the output is stored as bf16, each a round-to-nearest
+with unit roundoff 2^-8 (bf16 keeps 8 significant bits), with fp32 sums
+elsewhere.  For an output element o = sum_i p_i v_i / sum_i p_i the first
+contributes at most 2^-8 * sum_i p_i |v_i| / sum_i p_i <= 2^-8 * max |v|
+(over the head's values) and the second 2^-8 * |o|, so per element
+    |got - ref| <= 2^-8 * (max |v| + |ref|) + 1e-4,
+the last term for the fp32 accumulation.  Plus a relative Frobenius error
+<= 1e-2 over the whole output.
 """
 import numpy as np
 import pytest
@@ -32,7 +41,8 @@ def _run(a):
     cfg = lasynth.get_config("tiny", n_heads=H, n_kv_heads=Hkv, head_dim=dh,
                              W=a["W"], N=a["N"], G=a["G"])
     ref = oracle.attention(cfg, L, a["q"], a["k"], a["v"], bf16=True)
-    return got, ref
+    vmax = np.abs(lasynth.bf16_bits_to_f32(a["v"])).max(axis=(1, 2))  # per KV head
+    return got, ref, vmax[(np.arange(H) * Hkv) // H]  # per query head
 
 
 CASES = [
@@ -51,9 +61,10 @@ CASES = [
 def test_attention_matches_oracle(kw):
     a = lasynth.make_attn_inputs(seed=7, **kw)
     log(f"[attention] {kw} T={a['T']}")
-    got, ref = _run(a)
+    got, ref, vmax = _run(a)
     err = np.abs(got - ref)
+    bound = 2.0**-8 * (vmax[None, :, None] + np.abs(ref)) + 1e-4
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
-    log(f"  max={err.max():.3e} rel={rel:.3e}")
-    assert err.max() <= 1e-2
+    log(f"  max={err.max():.3e} (worst fraction of the bound {np.max(err / bound):.2f}) rel={rel:.3e}")
+    assert np.all(err <= bound)
     assert rel <= 1e-2
