@@ -44,3 +44,19 @@ def definition_probs(z, T, k, p):
     out = np.zeros(z.size)
     out[kept] = w / w.sum()
     return out
+
+
+def full_depth_logit_tol(name):
+    """Logit bound of one full-depth bf16 run of workload `name` against
+    exact arithmetic: 1.5x the largest logit change that storing the seven
+    bf16 activations alone causes on the same weights (measured by
+    tests/rounding_bounds.py, recorded in tests/golden/rounding_bounds.json).
+    Two bf16 runs compared with each other are each within this bound of
+    the exact logits, so they may differ by twice it; an argmax may then
+    differ wherever the top-2 margin is within twice the comparison bound."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                        "rounding_bounds.json")
+    with open(path) as f:
+        return 1.5 * json.load(f)[name]["max_abs_dlogit"]

@@ -8,19 +8,26 @@ configuration bench.py times (121 rows per step, W15 N5 G15).
   logit tolerance, and the candidate must be accepted in full.
 - A property that holds at any size: the lookahead output equals plain
   one-token greedy decoding (here both on the GPU, 512-token prompt, 256
-  tokens); a divergence is allowed only at a near-tie (margin <= 0.05).
+  tokens).  While the two share the history, a lookahead step's
+  current-token row and the plain step at the same position compute the
+  same logits through different row layouts and summation orders: they
+  must agree within the full-depth bound below, and a divergence is allowed
+  only where the plain run's top-2 margin is within twice that bound.
 
 Logit tolerance at full depth.  The bf16 datapath stores activations in
 bf16 at seven points per layer (normed inputs of the QKV and FFN GEMMs,
 q/k/v and the KV cache, attention probabilities, attention output, SwiGLU
 output, final normed input of the LM head).  Rounding alone, with every
 other operation exact, moves the logits of this 32-layer model by up to
-0.23 (rms 0.036; fp64 emulation over 16 tokens x 32000 logits); any single
-one of the seven roundings already exceeds 2e-2 by four layers.  The 2e-2
-bound therefore applies to the shallow bf16 parity configurations
-(tests/test_gpu_parity.py); here the bound is 1.5x the emulated
-rounding-only error, and argmax decisions are excused where two logits
-that far off can swap (margin <= 2 x tolerance).
+0.181 (rms 0.034; fp64 emulation on these weights over 32 prompt tokens x
+32000 logits, tests/rounding_bounds.py); any single one of the seven
+roundings already exceeds 2e-2 by four layers.  The 2e-2 bound therefore
+applies to the shallow bf16 parity configurations
+(tests/test_gpu_parity.py); here one GPU run against the oracle is held to
+1.5x the emulated rounding-only error, with argmax decisions excused where
+two logits that far off can swap (margin <= 2 x tolerance); two GPU runs
+against each other, to twice that bound (each is within it of the exact
+logits), with decisions excused at margins up to twice the comparison bound.
 """
 import numpy as np
 import pytest
@@ -29,11 +36,12 @@ import torch
 import lasynth
 import lookahead_decoding_la_amd as la
 import oracle
+from helpers import full_depth_logit_tol
 from lockstep import log, margin
 
 pytestmark = pytest.mark.gpu
 
-LOGIT_TOL_7B = 0.35          # 1.5 x the rounding-only error of the bf16 datapath
+LOGIT_TOL_7B = full_depth_logit_tol("7b")  # 1.5 x the rounding-only error: 0.272
 TIE_MARGIN_7B = 2 * LOGIT_TOL_7B
 
 
@@ -99,18 +107,32 @@ def test_7b_lookahead_output_equals_plain_greedy(w7b):
     win = lasynth.make_init_window(cfg, prompt)
     M = cfg.gen_tokens
     dec = la.LookaheadDecoder(cfg, dev_w, 1024)
-    toks, steps = dec.generate(prompt, win, M)
+    toks = [dec.prefill(prompt, win)]
+    steps, la_logits = [], {}  # position of the token a step's row 0 predicts -> logits
+    while len(toks) < M:
+        r = dec.step()
+        la_logits[len(toks)] = dec.debug_logits()[0].copy()
+        steps.append(r)
+        toks += r["tokens"]
+    toks = toks[:M]
     dec.close()
     acc = sum(s["n_emitted"] for s in steps) / len(steps)
     log(f"[7b] lookahead: {len(steps)} steps for {M} tokens ({acc:.2f} tokens/step)")
     plain = la.LookaheadDecoder(cfg.with_(W=0, G=0), dev_w, 1024)
     ref = [plain.prefill(prompt)]
-    margins = [None]
+    margins, dmax = [None], 0.0
     while len(ref) < M:
+        n = len(ref)
         ref += plain.step()["tokens"]
-        margins.append(margin(plain.debug_logits()[0]))
+        lg = plain.debug_logits()[0]
+        margins.append(margin(lg))
+        if n in la_logits and toks[:n] == ref[:n]:
+            dmax = max(dmax, float(np.max(np.abs(la_logits[n] - lg))))
     plain.close()
     div = next((i for i in range(M) if toks[i] != ref[i]), None)
-    log(f"[7b] first divergence: {div}")
+    log(f"[7b] first divergence: {div}" +
+        (f" (plain margin {margins[div]:.3f})" if div else "") +
+        f"; max |logit difference| before it {dmax:.3f}")
+    assert dmax <= 2 * LOGIT_TOL_7B
     if div is not None:
-        assert div > 0 and margins[div] is not None and margins[div] <= 0.05, (div, margins[div])
+        assert div > 0 and margins[div] <= 4 * LOGIT_TOL_7B, (div, margins[div])

@@ -7,13 +7,13 @@ weights).  The narrow versions of these step shapes run in lockstep with the
 oracle in tests/test_gpu_parity.py; here the full models are checked
 through a property that holds at any size: lookahead decoding emits the
 tokens of plain one-token greedy decoding on the same weights (both on the
-GPU), and where they part, the plain run's top-2 logit margin at that token
-is within the near-tie bound of the 7B test (two bf16 runs whose logits
-may each be off by the full-depth rounding error can order two close
-logits differently).  Up to that point the two runs share the history, so
-a lookahead step's current-token row and the plain step at the same
-position compute the same logits through different row layouts; they must
-agree within the 7B full-depth logit bound.
+GPU).  Up to the first divergence the two runs share the history, so a
+lookahead step's current-token row and the plain step at the same position
+compute the same logits through different row layouts; each is within the
+shape's full-depth bound of the exact logits (1.5x the rounding-only error
+that tests/rounding_bounds.py measures on these weights: 0.293 for 13B,
+0.679 for 34B), so they must agree within twice it, and the divergence
+must sit where the plain run's top-2 margin is within twice that.
 """
 import numpy as np
 import pytest
@@ -21,8 +21,8 @@ import torch
 
 import lasynth
 import lookahead_decoding_la_amd as la
+from helpers import full_depth_logit_tol
 from lockstep import log, margin
-from test_gpu_7b import LOGIT_TOL_7B, TIE_MARGIN_7B
 
 pytestmark = pytest.mark.gpu
 
@@ -68,6 +68,7 @@ def test_full_size_lookahead_equals_plain_greedy(name):
     log(f"[{name}] first divergence: {div}" +
         (f" (plain margin {margins[div]:.3f})" if div else "") +
         f"; max |logit difference| before it {dmax:.3f}")
-    assert dmax <= LOGIT_TOL_7B
+    tol = full_depth_logit_tol(name)
+    assert dmax <= 2 * tol, (dmax, tol)
     if div is not None:
-        assert div > 0 and margins[div] <= TIE_MARGIN_7B, (div, margins[div])
+        assert div > 0 and margins[div] <= 4 * tol, (div, margins[div])
