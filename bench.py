@@ -17,6 +17,7 @@ result readback.  Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -195,8 +196,9 @@ def batch_sweep(cfg, dev_w, steps, warmup, prompt_len=128):
     """Aggregate throughput as the batch grows: B sequences (their own
     prompts and windows) stepped together by one context, for several step
     shapes, up to 256 rows per forward pass.  Reports tokens/s summed over
-    the sequences, the step time, and the GEMM time and throughput (event-
-    timed step), i.e. where more rows stop being free."""
+    the sequences, the step time (median of the timed steps, each timed on
+    the host around la_step), and the GEMM time and throughput (event-timed
+    step), i.e. where more rows stop being free."""
     import lookahead_decoding_la_amd as la
     import torch
     out = []
@@ -208,16 +210,20 @@ def batch_sweep(cfg, dev_w, steps, warmup, prompt_len=128):
             for b in range(B):
                 p = lasynth.make_prompt(c, seed=b)
                 dec.prefill(p, lasynth.make_init_window(c, p, seed=b) if W else None, seq=b)
-            res = []
+            res, per = [], []
             for _ in range(warmup):
                 dec.step()
             torch.cuda.synchronize()
-            t0 = time.perf_counter()
+            gc.disable()
             for _ in range(steps):
-                r = dec.step()
+                t0 = time.perf_counter()
+                r = dec.step()  # returns after the step's stream synchronizes
+                per.append(time.perf_counter() - t0)
                 res.extend(r if B > 1 else [r])
-            torch.cuda.synchronize()
-            sec = time.perf_counter() - t0
+            gc.enable()
+            # median step: a setting's first context in a process has shown
+            # occasional host-side stalls that the steps after it do not have
+            sec = float(np.median(per)) * steps
             _, prof = dec.profile_step()
             dec.close()
             tok = sum(x["n_emitted"] for x in res)

@@ -5,12 +5,13 @@
 // one forward pass; the method works with FlashAttention-style kernels).
 //
 // bf16 kernel (gfx950, head_dim 128):
-//   - grid = heads x KV splits x sequences (flash-decoding style split of
-//     the key range so short contexts still fill the CUs; each sequence of a
-//     batch attends to its own cache only); one workgroup holds every query
-//     row of its head (up to 128 rows with 8 waves: 4 row pairs x 2 key
-//     halves; up to 256 rows: 8 row pairs), so each K/V chunk is read from
-//     HBM once per head;
+//   - grid = heads x (KV splits x row groups) x sequences (flash-decoding
+//     style split of the key range so short contexts still fill the CUs;
+//     each sequence of a batch attends to its own cache only); a workgroup
+//     holds 32 NRP query rows of its head (NRP row pairs of 16-row tiles),
+//     and the row groups of one head and split read the same K/V chunks
+//     (from HBM once, then from L2: their workgroup ids differ by a
+//     multiple of the head count, so they land on the same XCD);
 //   - Q and 64-key chunks of K and V^T go straight from HBM into LDS
 //     (global_load_lds), XOR-swizzled so the MFMA operand reads are free of
 //     bank conflicts, through a ring of chunk buffers a few chunks deep;
@@ -22,6 +23,9 @@
 //     passes on are one contiguous V^T piece);
 //   - splits merge in a second kernel (log-sum-exp weights).
 // The cache stores V transposed ([kv head][dh][position]) for this reason.
+#include <algorithm>
+#include <type_traits>
+
 #include "la_epilogue.h"
 
 namespace la {
@@ -130,21 +134,25 @@ __device__ inline int score_key(int kt, int r) {
 // bf16), and the rescaling of the output accumulators is rarely needed.
 constexpr float RESCALE_LOG2 = 8.f;
 
-// One workgroup = one head x one range of 64-key chunks, all query rows.
+// One workgroup = one head x one range of 64-key chunks x 32 NRP query rows
+// (row group rg: rows 32 NRP rg ..).
 // NRP x KSPL waves: wave w owns 16-row tiles 2 rp and 2 rp + 1 (rp = w %
 // NRP), so every K / V^T fragment read from LDS feeds two MFMAs, and key
 // part kp = w / NRP of each chunk (KSPL parts); the key parts are merged
 // through LDS at the end.  Chunks go straight from HBM to LDS
 // (global_load_lds, no register staging) through a ring of NBUF buffers,
 // NBUF - 1 chunks ahead of the one being consumed.
-// Key splits used for a block over nch 64-key chunks (context + block),
-// chosen at run time from the committed length so one captured graph fits
-// every length: about three chunks per split, one split (no merge) for two
-// chunks or fewer, at most smax (the launch's grid and the partial buffers).
-// Measured at 121 rows and 32 heads: 1 split best at 2 chunks, 4 at 7-11,
-// 6 at 18, 8 at 33.
-__device__ inline int eff_splits(int nch, int smax) {
-  const int s = nch <= 2 ? 1 : (nch + 2) / 3;
+// Key splits used for M block rows over nch 64-key chunks (context +
+// block), chosen at run time from the committed length so one captured
+// graph fits every length, at most smax (the launch's grid and the partial
+// buffers).  Up to 16 rows (one-token decode) a workgroup's chunk work is
+// small next to its fixed costs: one or two chunks per split, up to 8
+// splits.  Larger blocks: about three chunks per split, and one split (no
+// merge) for two chunks or fewer.  Measured, 32 heads, in captured graphs:
+// 1 row: 6 splits best at 5 and 9 chunks, 8 at 16; 121 rows: 1 split at 2
+// chunks, 2-3 at 6, 3-4 at 11, 4 at 18.
+__host__ __device__ inline int eff_splits(int nch, int smax, int M) {
+  const int s = M <= 16 ? (nch < 8 ? nch : 8) : (nch <= 2 ? 1 : (nch + 2) / 3);
   return s < smax ? s : smax;
 }
 
@@ -161,17 +169,41 @@ __global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
                 "key-part exchange fits in the ring");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[NBUF * CH_BYTES + QROWS * 256];
 
-  const int h = blockIdx.x, sp = blockIdx.y, sq = blockIdx.z;  // head, key split, sequence
+  const int M = a.M;
+  const int RG = (M + QROWS - 1) / QROWS;  // row groups
+  const int h = blockIdx.x, sq = blockIdx.z;  // head, sequence
+  const int sp = blockIdx.y / RG, tb = (blockIdx.y % RG) * QROWS;  // key split, first row
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c16 = l & 15;
   const int rp = w % NRP, kp = w / NRP;
-  const int L = a.st ? a.st[sq].L : a.L_host;
   const int r0 = sq * a.rps;  // the sequence's first row in q and out
-  const int M = a.M;
+
+  // Q of the group's rows: local row t (0 .. QROWS - 1, row tb + t; padding
+  // rows repeat row M - 1) owns bytes [256 t, 256 t + 256) after the chunk
+  // ring; dims 8p..8p+7 sit in slot p ^ (t & 15).
+  unsigned char* qb = lds + NBUF * CH_BYTES;
+#pragma unroll
+  for (int q = 0; q < QPT; q++) {
+    const int j = w + q * NW;  // 1 KiB = 4 rows
+    const int t = 4 * j + (l >> 4), qs = l & 15;
+    const uint16_t* gq = (const uint16_t*)a.q + (size_t)(r0 + min(tb + t, M - 1)) * (a.H * A_DH) +
+                         h * A_DH + ((qs ^ (t & 15)) * 8);
+    __builtin_amdgcn_global_load_lds((const void*)gq,
+                                     (__attribute__((address_space(3))) void*)(qb + j * 1024), 16,
+                                     0, 0);
+  }
+
+  // The committed length, read while the Q loads are in flight: a scalar
+  // load (constant address space; nothing writes the state during this
+  // kernel), so waiting for it does not wait for Q.
+  const int L = a.st ? *(const __attribute__((address_space(4))) int32_t*)&a.st[sq].L : a.L_host;
   const int kvh = (h * a.Hkv) / a.H;
   const int ctx = L + M;
   const int nch = (ctx + AKC - 1) / AKC;
-  const int S = eff_splits(nch, a.splits);
-  if (sp >= S) return;  // a split this length does not use (uniform; before any load)
+  const int S = eff_splits(nch, a.splits, M);
+  if (sp >= S) {  // a split this length does not use (uniform)
+    wait_vm<0>();   // Q loads land before the LDS is released
+    return;
+  }
   const int cps = (nch + S - 1) / S;
   const int c0 = min(sp * cps, nch), c1 = min(nch, c0 + cps);
   const int nloc = c1 - c0;
@@ -190,29 +222,14 @@ __global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
   int trow[2];
 #pragma unroll
   for (int u = 0; u < 2; u++) {
-    const int t = (2 * rp + u) * 16 + c16;
+    const int t = tb + (2 * rp + u) * 16 + c16;
     trow[u] = t < M ? t : (causal ? M - 1 : 0);
 #pragma unroll
     for (int i = 0; i < 4; i++) rm[u][i] = 0ull;
     if (!causal) step_row_mask(trow[u], a.W, a.N, rm[u][0], rm[u][1], rm[u][2], rm[u][3]);
   }
-  const bool act = 2 * rp * 16 < M;  // tile 2 rp holds tokens
-  const bool act1 = (2 * rp + 1) * 16 < M;
-
-  // Q of the head: row t (0 .. QROWS - 1, padding rows repeat row M - 1)
-  // owns bytes [256 t, 256 t + 256) after the chunk ring; dims 8p..8p+7 sit
-  // in slot p ^ (t & 15).
-  unsigned char* qb = lds + NBUF * CH_BYTES;
-#pragma unroll
-  for (int q = 0; q < QPT; q++) {
-    const int j = w + q * NW;  // 1 KiB = 4 rows
-    const int t = 4 * j + (l >> 4), sq = l & 15;
-    const uint16_t* gq = (const uint16_t*)a.q + (size_t)(r0 + min(t, M - 1)) * (a.H * A_DH) + h * A_DH +
-                         ((sq ^ (t & 15)) * 8);
-    __builtin_amdgcn_global_load_lds((const void*)gq,
-                                     (__attribute__((address_space(3))) void*)(qb + j * 1024), 16,
-                                     0, 0);
-  }
+  const bool act = tb + 2 * rp * 16 < M;  // tile 2 rp holds tokens
+  const bool act1 = tb + (2 * rp + 1) * 16 < M;
 
   // Issue chunk c into ring slot b.  Instruction j of a chunk (wave-uniform
   // LDS base, 1 KiB per instruction) covers K keys 4j..4j+3 or V^T dims
@@ -274,7 +291,9 @@ __global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
     unsigned char* vb = kb + CH_K_BYTES;
     const bool full = (c + 1) * AKC <= L;  // whole chunk in the committed prefix
     const int b0 = c * AKC - L;
-    if (act) {
+    // the second tile is skipped (MFMAs, softmax) when it holds no rows
+    auto chunk = [&](auto two) {
+      constexpr bool TWO = decltype(two)::value;
       f32x4 s[2][KT];
 #pragma unroll
       for (int j = 0; j < KT; j++) {
@@ -288,12 +307,13 @@ __global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
         for (int ks = 0; ks < 4; ks++) {
           const bf16x8 kf = *(const bf16x8*)(krow + (((4 * ks + g) ^ sw) << 4));
           s[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], s[0][j], 0, 0, 0);
-          s[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][ks], s[1][j], 0, 0, 0);
+          if constexpr (TWO)
+            s[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][ks], s[1][j], 0, 0, 0);
         }
       }
       bf16x8 pf[2][KT / 2];
 #pragma unroll
-      for (int u = 0; u < 2; u++) {
+      for (int u = 0; u < (TWO ? 2 : 1); u++) {
         const uint64_t win = full ? ~0ull
                                   : chunk_window(causal, trow[u], b0, rm[u][0], rm[u][1],
                                                  rm[u][2], rm[u][3]) >> (8 * g);
@@ -360,10 +380,15 @@ __global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
             vf = __builtin_bit_cast(bf16x8, vr);
           }
           o[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[0][j2], o[0][dt], 0, 0, 0);
-          o[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[1][j2], o[1][dt], 0, 0, 0);
+          if constexpr (TWO)
+            o[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[1][j2], o[1][dt], 0, 0, 0);
         }
       }
-    }
+    };
+    if (act1)
+      chunk(std::true_type{});
+    else if (act)
+      chunk(std::false_type{});
     lds_barrier();  // slot i % NBUF is free for the next issue
   }
   wait_vm<0>();  // drain the ring's redundant loads (also before LDS reuse)
@@ -405,7 +430,7 @@ __global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
 #pragma unroll
   for (int u = 0; u < 2; u++) {
     if (u == 1 && !act1) break;
-    const int t = (2 * rp + u) * 16 + c16;
+    const int t = tb + (2 * rp + u) * 16 + c16;
     if (t >= M) continue;
     if (S == 1) {
       // row-major, or fragment layout (dims dt*16 + 4g + 0..3 stay adjacent)
@@ -442,8 +467,8 @@ constexpr int A_MAX_SPLITS = 16;
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const int h = blockIdx.y, t = blockIdx.x * 8 + (threadIdx.x >> 5), i = (threadIdx.x & 31) * 4;
   const int sq = blockIdx.z;
-  const int L = a.st ? a.st[sq].L : a.L_host;
-  const int S = eff_splits((L + a.M + AKC - 1) / AKC, a.splits);
+  const int L = a.st ? *(const __attribute__((address_space(4))) int32_t*)&a.st[sq].L : a.L_host;
+  const int S = eff_splits((L + a.M + AKC - 1) / AKC, a.splits, a.M);
   if (t >= a.M || S == 1) return;  // one split wrote the output itself
   const int rows16 = (a.M + 15) & ~15;
   float m[A_MAX_SPLITS], l[A_MAX_SPLITS];
@@ -482,15 +507,16 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   *(uint2*)&((uint16_t*)a.out)[oi] = pk;
 }
 
-constexpr int A_NBUF = 4;  // ring depth (chunks) of the bf16 kernel
-
 // Splits the launch provides for (the grid's second dimension and the
-// partial buffers): what eff_splits asks for at the longest context.
+// partial buffers): what eff_splits asks for at the longest context, capped
+// so that heads x sequences x row groups x splits stays near 1024
+// workgroups (four per CU): a large batch fills the chip without splitting
+// the keys, and every split costs a prologue and merge traffic.  H counts
+// the heads of all sequences.
 int attn_bf16_splits(int H, int M, int max_ctx) {
-  (void)H;
-  const int max_chunks = (max_ctx + M + AKC - 1) / AKC;
-  const int s = max_chunks <= 2 ? 1 : (max_chunks + 2) / 3;
-  return s < A_MAX_SPLITS ? s : A_MAX_SPLITS;
+  const int rg = M <= 128 ? (M + 31) / 32 : 1;  // row groups of the instance launch_attn_bf16 picks
+  const int cap = std::max(1, 1024 / (H * rg));
+  return eff_splits((max_ctx + M + AKC - 1) / AKC, std::min(A_MAX_SPLITS, cap), M);
 }
 
 size_t attn_bf16_partial_floats(int H, int M, int splits, int dh) {
@@ -498,17 +524,23 @@ size_t attn_bf16_partial_floats(int H, int M, int splits, int dh) {
   return (size_t)H * splits * rows16 * (dh + 2);
 }
 
+template <int NRP, int KSPL, int NBUF>
+static void launch_attn_inst(const AttnArgs& a, hipStream_t s) {
+  const int rg = (a.M + 32 * NRP - 1) / (32 * NRP);
+  hipLaunchKernelGGL((k_attn_bf16<NRP, KSPL, NBUF>), dim3(a.H, a.splits * rg, a.nseq),
+                     dim3(NRP * KSPL * 64), 0, s, a);
+}
+
 void launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
-  dim3 grid(a.H, a.splits, a.nseq);
-  // up to 32 rows (plain decode, small steps): 2 waves and a 2-chunk ring,
-  // 72 KiB of LDS, so two workgroups share a CU; up to 128 rows: 8 waves
-  // (4 row pairs x 2 key halves); up to 256: 8 row pairs
-  if (a.M <= 32)
-    hipLaunchKernelGGL((k_attn_bf16<1, 2, 2>), grid, dim3(128), 0, s, a);
-  else if (a.M <= 128)
-    hipLaunchKernelGGL((k_attn_bf16<4, 2, A_NBUF>), grid, dim3(512), 0, s, a);
+  // up to 128 rows: row groups of 32 rows, 2 waves (2 key halves) and a
+  // 2-chunk ring, 72 KiB of LDS, so two workgroups share a CU (measured at
+  // 57 and 121 rows and 0-1000 committed tokens: as fast as 64-row groups
+  // and 1-4 µs per layer faster than one 128-row workgroup per head); up to
+  // 256 rows: one workgroup of 8 row pairs per head
+  if (a.M <= 128)
+    launch_attn_inst<1, 2, 2>(a, s);
   else
-    hipLaunchKernelGGL((k_attn_bf16<8, 1, 2>), grid, dim3(512), 0, s, a);
+    launch_attn_inst<8, 1, 2>(a, s);
   if (a.splits > 1)
     hipLaunchKernelGGL(k_attn_merge, dim3((a.M + 7) / 8, a.H, a.nseq), dim3(256), 0, s, a);
 }
