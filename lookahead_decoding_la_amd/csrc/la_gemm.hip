@@ -395,9 +395,12 @@ __device__ inline uint4 pack8(const float* v) {
 // for 32 tokens, then RoPE + store q (row-major) or k (cache rows), or
 // transpose v through LDS so that the V^T cache rows (positions of one
 // dimension) are written as contiguous runs.  Thread: token tid/8, columns
-// 16*(tid%8) .. +16 of the block.
+// 16*(tid%8) .. +16 of the block.  Every load the thread needs (the KS
+// partials, the row's sums of squares, the rotary factors, the committed
+// length) is issued before the first is used: one memory round trip.
 constexpr int RQ_TOK = 32;
 
+template <int KS>
 __global__ __launch_bounds__(256) void k_red_qkv(const float* __restrict__ P, int ks, int N,
                                                  int M, EpiArgs ea) {
   __shared__ float vt[RQ_TOK][128 + 1];
@@ -410,33 +413,62 @@ __global__ __launch_bounds__(256) void k_red_qkv(const float* __restrict__ P, in
   // block row tq of sequence b (its state and caches)
   const int b = tc / ea.rps, tq = tc - b * ea.rps;
   const int L = ea.st[b].L;
-  float v[16];
-  {
-    const float* pr = P + (size_t)tc * N + n0;
+  constexpr int NZ = KS > 0 ? KS : 1;
+  float4 pz[NZ][4];
 #pragma unroll
-    for (int e = 0; e < 16; e += 4) {
-      const float4 a = *(const float4*)(pr + e);
-      v[e] = a.x; v[e + 1] = a.y; v[e + 2] = a.z; v[e + 3] = a.w;
+  for (int z = 0; z < NZ; z++)
+#pragma unroll
+    for (int e = 0; e < 4; e++) pz[z][e] = *(const float4*)(P + ((size_t)z * M + tc) * N + n0 + 4 * e);
+  static_assert(SSQ_STRIDE == 8, "sums of squares: two float4 per row");
+  const float4 q0 = *(const float4*)(ea.ssq + tc * SSQ_STRIDE);
+  const float4 q1 = *(const float4*)(ea.ssq + tc * SSQ_STRIDE + 4);
+  float4 rc0, rc1, rs0, rs1;  // rotary factors of pairs c0/2 .. c0/2 + 7
+  if (!is_v) {
+    const float* cs = ea.rope_rows + (size_t)tc * 128 + c0 / 2;
+    rc0 = *(const float4*)cs;
+    rc1 = *(const float4*)(cs + 4);
+    rs0 = *(const float4*)(cs + 64);
+    rs1 = *(const float4*)(cs + 68);
+  }
+  float v[16];
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    v[4 * e] = pz[0][e].x; v[4 * e + 1] = pz[0][e].y;
+    v[4 * e + 2] = pz[0][e].z; v[4 * e + 3] = pz[0][e].w;
+  }
+#pragma unroll
+  for (int z = 1; z < NZ; z++)
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      v[4 * e] += pz[z][e].x; v[4 * e + 1] += pz[z][e].y;
+      v[4 * e + 2] += pz[z][e].z; v[4 * e + 3] += pz[z][e].w;
     }
+  if constexpr (KS == 0) {  // any other split count: the remaining splits in order
     for (int z = 1; z < ks; z++) {
-      const float* pz = P + ((size_t)z * M + tc) * N + n0;
+      const float* pr = P + ((size_t)z * M + tc) * N + n0;
 #pragma unroll
       for (int e = 0; e < 16; e += 4) {
-        const float4 a = *(const float4*)(pz + e);
+        const float4 a = *(const float4*)(pr + e);
         v[e] += a.x; v[e + 1] += a.y; v[e + 2] += a.z; v[e + 3] += a.w;
       }
     }
   }
   {
-    // the input rows were not normalized (deferred RMSNorm)
-    const float inv = row_inv_rms(ea.ssq, ea.ssn, tc, ea.dmodel, ea.eps);
+    // the input rows were not normalized (deferred RMSNorm); chunk sums in
+    // order, as row_inv_rms adds them
+    const float qs[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      if (i < ea.ssn) sq += qs[i];
+    const float inv = 1.f / sqrtf(sq / (float)ea.dmodel + ea.eps);
 #pragma unroll
     for (int e = 0; e < 16; e++) v[e] *= inv;
   }
   if (!is_v) {
     // rotary angle of pair i (dims 2i, 2i+1 of the head) at pos
-    const float* cs = ea.rope_rows + (size_t)tc * 128 + c0 / 2;
-    const float* sn = cs + 64;
+    const float cs[8] = {rc0.x, rc0.y, rc0.z, rc0.w, rc1.x, rc1.y, rc1.z, rc1.w};
+    const float sn[8] = {rs0.x, rs0.y, rs0.z, rs0.w, rs1.x, rs1.y, rs1.z, rs1.w};
     uint16_t o[16];
 #pragma unroll
     for (int e = 0; e < 8; e++) {
@@ -497,6 +529,10 @@ __device__ inline float block_sum(float v, float* sh) {
 // residual add; the next GEMM's input bf16(x * w) in fragment layout
 // (deferred RMSNorm) and this chunk's sum of squares.  Workgroup (c, t):
 // columns c*SSQ_CHUNK .. +SSQ_CHUNK of row t, 8 per thread.
+// KS > 0: that many splits, every partial loaded before the first add (one
+// memory round trip); KS == 0: ks splits, loaded one after another.  The
+// splits are added in order either way.
+template <int KS>
 __global__ __launch_bounds__(SSQ_CHUNK / 8) void k_red_resid_scale(
     const float* __restrict__ P, int ks, int d, int M, float* __restrict__ x,
     const uint16_t* __restrict__ w, uint16_t* __restrict__ xnf, int MTT, float* __restrict__ ssq) {
@@ -509,11 +545,21 @@ __global__ __launch_bounds__(SSQ_CHUNK / 8) void k_red_resid_scale(
     const uint4 wv = *(const uint4*)(w + i);
     float v[8];
     load8(xr + i, v);
-    for (int z = 0; z < ks; z++) {
-      float p[8];
-      load8(P + ((size_t)z * M + t) * d + i, p);
+    if constexpr (KS > 0) {
+      float p[KS][8];
 #pragma unroll
-      for (int e = 0; e < 8; e++) v[e] += p[e];
+      for (int z = 0; z < KS; z++) load8(P + ((size_t)z * M + t) * d + i, p[z]);
+#pragma unroll
+      for (int z = 0; z < KS; z++)
+#pragma unroll
+        for (int e = 0; e < 8; e++) v[e] += p[z][e];
+    } else {
+      for (int z = 0; z < ks; z++) {
+        float p[8];
+        load8(P + ((size_t)z * M + t) * d + i, p);
+#pragma unroll
+        for (int e = 0; e < 8; e++) v[e] += p[e];
+      }
     }
     *(float4*)(xr + i) = make_float4(v[0], v[1], v[2], v[3]);
     *(float4*)(xr + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
@@ -608,13 +654,28 @@ __global__ __launch_bounds__(256) void k_red_swiglu(const float* __restrict__ P,
 }
 
 void launch_red_qkv(const float* P, int ks, int N, int M, const EpiArgs& ea, hipStream_t s) {
-  hipLaunchKernelGGL(k_red_qkv, dim3(N / 128, (M + RQ_TOK - 1) / RQ_TOK), dim3(256), 0, s, P, ks,
-                     N, M, ea);
+  const dim3 grid(N / 128, (M + RQ_TOK - 1) / RQ_TOK);
+  if (ks == 1) hipLaunchKernelGGL(k_red_qkv<1>, grid, dim3(256), 0, s, P, ks, N, M, ea);
+  else if (ks == 2) hipLaunchKernelGGL(k_red_qkv<2>, grid, dim3(256), 0, s, P, ks, N, M, ea);
+  else if (ks == 4) hipLaunchKernelGGL(k_red_qkv<4>, grid, dim3(256), 0, s, P, ks, N, M, ea);
+  else hipLaunchKernelGGL(k_red_qkv<0>, grid, dim3(256), 0, s, P, ks, N, M, ea);
 }
 void launch_red_resid_scale(const float* P, int ks, int d, int M, float* x, const uint16_t* w,
                             uint16_t* xnf, int MTT, float* ssq, hipStream_t s) {
-  hipLaunchKernelGGL(k_red_resid_scale, dim3((d + SSQ_CHUNK - 1) / SSQ_CHUNK, M),
-                     dim3(SSQ_CHUNK / 8), 0, s, P, ks, d, M, x, w, xnf, MTT, ssq);
+  const dim3 grid((d + SSQ_CHUNK - 1) / SSQ_CHUNK, M), block(SSQ_CHUNK / 8);
+#define LA_RED_CASE(k)                                                                              \
+  case k:                                                                                           \
+    hipLaunchKernelGGL(k_red_resid_scale<k>, grid, block, 0, s, P, ks, d, M, x, w, xnf, MTT, ssq); \
+    break;
+  switch (ks) {
+    LA_RED_CASE(1)
+    LA_RED_CASE(2)
+    LA_RED_CASE(4)
+    LA_RED_CASE(8)
+    default:
+      hipLaunchKernelGGL(k_red_resid_scale<0>, grid, block, 0, s, P, ks, d, M, x, w, xnf, MTT, ssq);
+  }
+#undef LA_RED_CASE
 }
 void launch_red_resid_norm(const float* P, int ks, int d, int M, float* x, const uint16_t* w,
                            float eps, uint16_t* xnf, int MTT, hipStream_t s) {
