@@ -507,15 +507,21 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   *(uint2*)&((uint16_t*)a.out)[oi] = pk;
 }
 
+// Row groups of the instance launch_attn_bf16 picks for M rows: 32-row
+// groups from 65 to 128 rows, one workgroup per head otherwise.
+static int attn_row_groups(int M) { return M > 64 && M <= 128 ? (M + 31) / 32 : 1; }
+
 // Splits the launch provides for (the grid's second dimension and the
 // partial buffers): what eff_splits asks for at the longest context, capped
-// so that heads x sequences x row groups x splits stays near 1024
-// workgroups (four per CU): a large batch fills the chip without splitting
-// the keys, and every split costs a prologue and merge traffic.  H counts
-// the heads of all sequences.
+// so that heads x sequences x row groups x splits stays near 512 workgroups
+// (one resident round at two per CU): more splits than that only add
+// prologues, merge traffic and a second round of workgroups (measured at 40
+// heads x 81 rows, 1100 committed tokens: 4 splits 22 us, 7 splits 27-29
+// us; at 64 heads x 57 rows, 2100 tokens: 4 splits 26 us, 8 splits 33 us),
+// and a large batch fills the chip without splitting the keys.  H counts the
+// heads of all sequences.
 int attn_bf16_splits(int H, int M, int max_ctx) {
-  const int rg = M <= 128 ? (M + 31) / 32 : 1;  // row groups of the instance launch_attn_bf16 picks
-  const int cap = std::max(1, 1024 / (H * rg));
+  const int cap = std::max(1, 512 / (H * attn_row_groups(M)));
   return eff_splits((max_ctx + M + AKC - 1) / AKC, std::min(A_MAX_SPLITS, cap), M);
 }
 
@@ -532,12 +538,18 @@ static void launch_attn_inst(const AttnArgs& a, hipStream_t s) {
 }
 
 void launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
-  // up to 128 rows: row groups of 32 rows, 2 waves (2 key halves) and a
-  // 2-chunk ring, 72 KiB of LDS, so two workgroups share a CU (measured at
-  // 57 and 121 rows and 0-1000 committed tokens: as fast as 64-row groups
-  // and 1-4 µs per layer faster than one 128-row workgroup per head); up to
-  // 256 rows: one workgroup of 8 row pairs per head
-  if (a.M <= 128)
+  // 2 key halves and a 2-chunk ring per workgroup; up to 32 rows one row
+  // pair (72 KiB of LDS, two workgroups per CU), 33-64 rows two row pairs
+  // (80 KiB), 65-128 rows row groups of 32 (measured at 121 rows and 0-1000
+  // committed tokens: 1-4 us per layer faster than one 128-row workgroup per
+  // head; at 57 rows, 64 heads and 2100 tokens one 64-row group is 3.7 us
+  // faster than two of 32); above 128 rows one workgroup of 8 row pairs per
+  // head.  attn_row_groups mirrors this choice.
+  if (a.M <= 32)
+    launch_attn_inst<1, 2, 2>(a, s);
+  else if (a.M <= 64)
+    launch_attn_inst<2, 2, 2>(a, s);
+  else if (a.M <= 128)
     launch_attn_inst<1, 2, 2>(a, s);
   else
     launch_attn_inst<8, 1, 2>(a, s);
