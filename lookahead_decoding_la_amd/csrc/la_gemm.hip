@@ -46,8 +46,8 @@ __global__ __launch_bounds__(G_NW * 64) void k_gemm_bf16(
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int wt = blockIdx.x, kz = blockIdx.y;
   const int KS = K >> 5;
-  const int ks0 = (int)((long)KS * kz / ksplit);
-  const int nst = ((int)((long)KS * (kz + 1) / ksplit) - ks0) / J;
+  const int ks0 = KS * kz / ksplit;  // KS * ksplit stays far below 2^31
+  const int nst = (KS * (kz + 1) / ksplit - ks0) / J;
   const bf16x8* __restrict__ Xv = (const bf16x8*)X;
   const bf16x8* __restrict__ wp =
       (const bf16x8*)Wp + ((size_t)(wt * G_NW + w) * KS) * 64 + l;
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(G_NW * 64) void k_gemm_bf16(
 // weight tiles and the J*MT activation fragments) and every wave only
 // waits for the stage it is about to use.  One barrier per stage: after
 // it, every wave has finished the previous stage, whose slot is refilled.
-template <int MT, int J, int OUT>
+template <int MT, int J, int OUT, bool XP>
 __global__ __launch_bounds__(G_NW * 64) void k_gemm_dma(
     const uint16_t* __restrict__ X, int MTT, const uint16_t* __restrict__ Wp, int K,
     int ksplit, float* __restrict__ P, int N, int M, uint16_t* __restrict__ A,
@@ -180,8 +180,8 @@ __global__ __launch_bounds__(G_NW * 64) void k_gemm_dma(
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int wt = blockIdx.x, kz = blockIdx.y;
   const int KS = K >> 5;
-  const int ks0 = (int)((long)KS * kz / ksplit);
-  const int nst = ((int)((long)KS * (kz + 1) / ksplit) - ks0) / J;
+  const int ks0 = KS * kz / ksplit;  // KS * ksplit stays far below 2^31
+  const int nst = (KS * (kz + 1) / ksplit - ks0) / J;
   const uint16_t* wb = Wp + (size_t)(wt * G_NW + w) * KS * 512 + l * 8;
 
   // stage st into ring slot b; past the end the last stage is re-issued
@@ -207,14 +207,57 @@ __global__ __launch_bounds__(G_NW * 64) void k_gemm_dma(
     }
   };
 
+  // The activation fragments were written by the previous kernel, so no
+  // XCD's L2 holds them, and every stage would wait on L2 misses that all
+  // of the XCD's workgroups share (measured: the fused gate/up GEMM takes
+  // 48 us after itself, 52-53 us after a kernel that rewrote its input,
+  // unchanged after one that wrote other memory).  With XP (at least 4
+  // token tiles and at most 2 K splits: large fragment ranges per
+  // workgroup; no gain measured with 8 splits) each workgroup touches one
+  // slice of its K range's fragments right after issuing the ring's first
+  // stage, 8 lanes per 128-byte line so that a load instruction covers 8
+  // lines like any coalesced load: workgroups are dealt to the 8 XCDs
+  // round robin, so the workgroups of one K range on one XCD (grid x index
+  // / 8 = slice) touch the whole range once between them and their L2
+  // holds it before the ring needs it.  Every thread issues exactly XPF
+  // such loads (lines past its slice repeat the slice's last line), so the
+  // first stage's wait can count them; the values are consumed only after
+  // the main loop.
+  constexpr int XPF = XP ? 8 : 0;  // prefetch loads per thread (64 KiB per workgroup)
+  static_assert((D - 2) * LPS + XPF < 64 && (D - 1) * LPS + XPF < 64, "vmcnt");
+  uint32_t xpf[XP ? XPF : 1];
+  auto prefetch = [&]() {
+    if constexpr (XP) {
+      const uint32_t nsl = max(gridDim.x >> 3, 1u), sl = min((uint32_t)wt >> 3, nsl - 1);
+      // the K range's k-steps hold MTT tiles of 8 lines each; the first MT
+      // tiles of every k-step are read
+      const char* xr = (const char*)(X + (size_t)ks0 * MTT * 512);
+      const uint32_t lines = (uint32_t)(nst * J) * MT * 8;
+      const uint32_t b0 = lines * sl / nsl, b1 = lines * (sl + 1) / nsl;
+#pragma unroll
+      for (int i = 0; i < XPF; i++) {
+        const uint32_t ln = min(b0 + (uint32_t)((i * G_NW + w) * 8 + (l >> 3)), max(b1, 1u) - 1);
+        const uint32_t kk = ln / (MT * 8), r = ln - kk * (MT * 8);
+        xpf[i] = *(const uint32_t*)(xr + ((size_t)kk * MTT * 8 + r) * 128 + (l & 7) * 16);
+      }
+    }
+  };
+
   f32x4 acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; m++) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  issue(0, 0);
+  prefetch();
 #pragma unroll
-  for (int i = 0; i < D - 1; i++) issue(i, i);
+  for (int i = 1; i < D - 1; i++) issue(i, i);
   for (int st = 0; st < nst; st++) {
-    wait_vm<(D - 2) * LPS>();  // this thread's part of stage st has landed
-    lds_barrier();              // ... everyone's; and stage st-1 is consumed
+    // this thread's part of stage st has landed (stage 0: the XPF
+    // prefetch loads issued after it may still be in flight)
+    if (st == 0)
+      wait_vm<(D - 2) * LPS + XPF>();
+    else
+      wait_vm<(D - 2) * LPS>();
+    lds_barrier();  // ... everyone's; and stage st-1 is consumed
     issue(st + D - 1, (st + D - 1) % D);
     const unsigned char* sb = lds + (st % D) * STAGE;
 #pragma unroll
@@ -228,6 +271,10 @@ __global__ __launch_bounds__(G_NW * 64) void k_gemm_dma(
     }
   }
   wait_vm<0>();  // drain the re-issued stages before the LDS is reused or freed
+  if constexpr (XP) {
+#pragma unroll
+    for (int i = 0; i < XPF; i++) asm volatile("" ::"v"(xpf[i]));  // keep the prefetch loads
+  }
 
   // lane holds rows n = 16*tile + 4*(l/16) + v of token 16*m + l%16
   if (OUT == 0) {
@@ -311,10 +358,14 @@ static void launch_j(int MT, dim3 grid, const uint16_t* X, int MTT, const uint16
 template <int J>
 static void launch_dma_part(int MT, dim3 grid, const uint16_t* X, int MTT, const uint16_t* Wp,
                             int K, int ks, float* P, int N, int M, hipStream_t s) {
-#define LA_GEMM_CASE(mt)                                                                     \
-  case mt:                                                                                   \
-    hipLaunchKernelGGL((k_gemm_dma<mt, J, 0>), grid, dim3(G_NW * 64), 0, s, X, MTT, Wp, K, ks, \
-                       P, N, M, nullptr, nullptr, 0, 0.f);                                   \
+#define LA_GEMM_CASE(mt)                                                                         \
+  case mt:                                                                                       \
+    if (ks <= 2)                                                                                 \
+      hipLaunchKernelGGL((k_gemm_dma<mt, J, 0, true>), grid, dim3(G_NW * 64), 0, s, X, MTT, Wp, \
+                         K, ks, P, N, M, nullptr, nullptr, 0, 0.f);                              \
+    else                                                                                         \
+      hipLaunchKernelGGL((k_gemm_dma<mt, J, 0, false>), grid, dim3(G_NW * 64), 0, s, X, MTT, Wp, \
+                         K, ks, P, N, M, nullptr, nullptr, 0, 0.f);                              \
     break;
   switch (MT) {
     LA_GEMM_CASE(4) LA_GEMM_CASE(5) LA_GEMM_CASE(6) LA_GEMM_CASE(7)
@@ -347,8 +398,8 @@ static void launch_dma_swiglu(int MT, dim3 grid, const uint16_t* X, int MTT, con
                               float eps, hipStream_t s) {
 #define LA_GEMM_CASE(mt)                                                                    \
   case mt:                                                                                  \
-    hipLaunchKernelGGL((k_gemm_dma<mt, J, 1>), grid, dim3(G_NW * 64), 0, s, X, MTT, Wp, K, 1, \
-                       nullptr, N, M, A, ssq, ssn, eps);                                    \
+    hipLaunchKernelGGL((k_gemm_dma<mt, J, 1, (mt >= 4)>), grid, dim3(G_NW * 64), 0, s, X, MTT, \
+                       Wp, K, 1, nullptr, N, M, A, ssq, ssn, eps);                          \
     break;
   switch (MT) {
     LA_GEMM_CASE(1) LA_GEMM_CASE(2) LA_GEMM_CASE(3) LA_GEMM_CASE(4)
