@@ -76,7 +76,7 @@ def traffic_from_profiles(kernel_key: str):
 
 
 COPY_PROBE_BYTES = 1 << 29  # bytes read (and written) by one --copy-probe launch
-GATEUP_RE = r"k_gemm_(bf16|dma)<\d+, \d+, 1>"
+GATEUP_RE = r"k_gemm_(bf16|dma)<\d+, \d+, 1(, \w+)?>"
 COPY_RE = r"neg_kernel"
 
 
