@@ -246,8 +246,9 @@ class LookaheadDecoder:
                     "la_seed_pool_seq")
 
     def profile_kernel(self, klass: str, reps: int = 32) -> float:
-        """Mean microseconds per launch of one kernel class (layer 0's), from
-        reps back-to-back launches between two HIP events."""
+        """Mean microseconds per launch of one kernel class, from reps
+        back-to-back launches between two HIP events; launch i uses layer
+        (i mod n_layers)'s weights, so no launch finds its weights cached."""
         us = C.c_float()
         self._check(lib().la_profile_kernel(self._h, PROF_CLASSES.index(klass), int(reps),
                                             C.byref(us)), "la_profile_kernel")

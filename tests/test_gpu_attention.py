@@ -53,7 +53,11 @@ CASES = [
     dict(prefix=130, n_heads=8, n_kv_heads=2),         # grouped KV heads
     dict(prefix=64, W=25, N=5, G=25),                  # 201 rows
     dict(prefix=5, W=1, N=2, G=0),                     # 2 rows
-    dict(prefix=2000, n_heads=4, W=7, N=5, G=7),       # longer context
+    dict(prefix=2000, n_heads=4, W=7, N=5, G=7),       # longer context, 57 rows (64-row group)
+    dict(prefix=1100, n_heads=8, W=10, N=5, G=10),     # 81 rows: 3 row groups, last holds 17
+    dict(prefix=300, n_heads=8, n_kv_heads=2, W=3, N=5, G=8),  # 45 rows, grouped KV heads
+    dict(prefix=64, n_heads=4, W=4, N=5, G=4),         # 33 rows: a wave's second tile empty
+    dict(prefix=700, n_heads=4, W=12, N=5, G=12),      # 97 rows: last group has one tile
 ]
 
 
