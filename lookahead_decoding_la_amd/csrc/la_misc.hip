@@ -261,22 +261,43 @@ void launch_pool_insert(DevState*, int32_t key, const int32_t* tail_dev, int32_t
 // copies, and each distinct key's list is written back once.
 constexpr int POOL_LDS_INTS = 6144;
 
-// Insert tail into list lst (len entries of n1 tokens, oldest first).
-__device__ inline int pool_insert_list(int32_t* lst, int len, int n1, int G, const int32_t* tail) {
+// Insert tail into the LDS list lst (len entries of n1 <= 31 tokens, oldest
+// first) with the one 64-lane wave of the workgroup; every lane returns the
+// new length.  Same result as pool_insert_serial: a tail already present is
+// moved to the newest end, else it is appended, the oldest entry dropped
+// when the list holds G.  Lanes compare 64 entries at a time (the lowest
+// match wins), then move entries gap+1 .. len-1 down by one, every lane
+// reading its source entry before any lane writes.
+__device__ inline int pool_insert_wave(int32_t* lst, int len, int n1, int G, const int32_t* tail) {
+  const int lane = threadIdx.x & 63;
   int found = -1;
-  for (int e = 0; e < len && found < 0; e++) {
-    bool same = true;
+  for (int e0 = 0; e0 < len && found < 0; e0 += 64) {
+    const int e = e0 + lane;
+    bool same = e < len;
     for (int i = 0; i < n1; i++) same = same && lst[e * n1 + i] == tail[i];
-    if (same) found = e;
+    const uint64_t m = __ballot(same);
+    if (m) found = e0 + __ffsll((unsigned long long)m) - 1;
   }
-  int gap;
+  int gap, nlen = len;
   if (found >= 0) gap = found;
   else if (len == G) gap = 0;
-  else gap = len++;
-  for (int e = gap; e + 1 < len; e++)
-    for (int i = 0; i < n1; i++) lst[e * n1 + i] = lst[(e + 1) * n1 + i];
-  for (int i = 0; i < n1; i++) lst[(len - 1) * n1 + i] = tail[i];
-  return len;
+  else gap = nlen++;
+  for (int e0 = gap; e0 + 1 < nlen; e0 += 64) {
+    const int e = e0 + lane;
+    const bool mv = e + 1 < nlen;
+    int v[31];
+#pragma unroll
+    for (int i = 0; i < 31; i++)
+      if (i < n1 && mv) v[i] = lst[(e + 1) * n1 + i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 31; i++)
+      if (i < n1 && mv) lst[e * n1 + i] = v[i];
+    __syncthreads();
+  }
+  if (lane < n1) lst[(nlen - 1) * n1 + lane] = tail[lane];
+  __syncthreads();
+  return nlen;
 }
 
 // One workgroup per sequence of the batch (its rows, window, pool, result).
@@ -373,19 +394,28 @@ __global__ __launch_bounds__(64) void k_verify(DevState* st, const int32_t* __re
     st->L = L + k + 1;
     st->cur = bonus;
     res->kv_len = L + k + 1;
-    // n-gram pool: insert every column's n-gram in column order
-    for (int j = 0; j < W; j++) {
-      for (int l = 2; l <= n1; l++) tail[l - 2] = lwin[(l - 1) * W + j];
-      tail[n1 - 1] = ynew[j];
-      if (staged) {
-        const int sl = lslot[j];
-        llen[sl] = pool_insert_list(llist + sl * per, llen[sl], n1, G, tail);
-      } else {
+    // n-gram pool, lists not staged: insert every column's n-gram in
+    // column order, one lane
+    if (!staged)
+      for (int j = 0; j < W; j++) {
+        for (int l = 2; l <= n1; l++) tail[l - 2] = lwin[(l - 1) * W + j];
+        tail[n1 - 1] = ynew[j];
         pool_insert_serial(pool_len, pool, N, G, lwin[j], tail);
       }
-    }
   }
   __syncthreads();
+  if (staged) {
+    // staged lists: the same inserts, in column order, by the whole wave
+    for (int j = 0; j < W; j++) {
+      if (lane < n1 - 1) tail[lane] = lwin[(lane + 1) * W + j];
+      if (lane == n1 - 1) tail[lane] = ynew[j];
+      __syncthreads();
+      const int sl = lslot[j];
+      const int nl = pool_insert_wave(llist + sl * per, llen[sl], n1, G, tail);
+      if (lane == 0) llen[sl] = nl;
+      __syncthreads();
+    }
+  }
   if (staged) {
     for (int j = lane; j < W; j += 64)
       if (lslot[j] == j) pool_len[lkey[j]] = llen[j];
