@@ -23,6 +23,8 @@
 //     workgroups; each split writes fp32 partial sums and a reduce kernel
 //     (which also applies the epilogue) adds them in split order, so
 //     results are deterministic and no workgroup waits on another.
+#include <algorithm>
+
 #include "la_epilogue.h"
 
 namespace la {
@@ -159,30 +161,46 @@ __global__ __launch_bounds__(G_NW * 64) void k_gemm_bf16(
 
 // The same product with every operand loaded straight into LDS
 // (global_load_lds, 1 KiB per wave instruction): no staging registers, so
-// the ring can hold G_DD stages (each J k-steps of this workgroup's eight
-// weight tiles and the J*MT activation fragments) and every wave only
-// waits for the stage it is about to use.  One barrier per stage: after
-// it, every wave has finished the previous stage, whose slot is refilled.
-template <int MT, int J, int OUT, bool XP>
-__global__ __launch_bounds__(G_NW * 64) void k_gemm_dma(
+// the ring can hold D stages (each J k-steps of this workgroup's NW weight
+// tiles and the J*MT activation fragments) and every wave only waits for
+// the stage it is about to use.  One barrier per stage: after it, every
+// wave has finished the previous stage, whose slot is refilled.
+// OUT == 0: workgroup wt owns weight tiles NW*wt .. NW*wt + NW-1.
+// OUT == 1 (fused gate/up + SwiGLU; gate tile i and up tile i are tiles 2i
+// and 2i + 1): the N/32 tile pairs are dealt to the grid's workgroups as
+// evenly as possible, up to NW/2 pairs each, so that every CU streams
+// about the same weight bytes (with 8-wave groups at 688 pairs, 172
+// workgroups left 84 CUs idle); a wave without a pair loads its group's
+// last pair again (an L2 hit beside the wave that owns it) and stores
+// nothing.
+template <int MT, int J, int OUT, bool XP, int NW = G_NW>
+__global__ __launch_bounds__(NW * 64) void k_gemm_dma(
     const uint16_t* __restrict__ X, int MTT, const uint16_t* __restrict__ Wp, int K,
     int ksplit, float* __restrict__ P, int N, int M, uint16_t* __restrict__ A,
     const float* __restrict__ ssq, int ssn, float eps) {
   constexpr int NF = J * MT;                   // activation fragments per stage
-  constexpr int FPW = (NF + G_NW - 1) / G_NW;  // of them loaded per wave
-  constexpr int LPS = J + FPW;                 // load instructions per thread per stage
-  constexpr int WKB = G_NW * J;                // weight KiB per stage
+  constexpr int FPW = (NF + NW - 1) / NW;  // of them loaded per wave
+  constexpr int LPS = J + FPW;             // load instructions per thread per stage
+  constexpr int WKB = NW * J;              // weight KiB per stage
   constexpr int STAGE = (WKB + NF) * 1024;
   constexpr int D = STAGE * 4 <= 160 * 1024 ? 4 : 3;
   static_assert(D * STAGE <= 160 * 1024 && (D - 2) * LPS < 64, "ring");
-  static_assert(OUT == 0 || D * STAGE >= (G_NW / 2) * MT * 64 * 16, "LDS exchange");
+  static_assert(OUT == 0 || (NW % 2 == 0 && D * STAGE >= (NW / 2) * MT * 64 * 16), "LDS exchange");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[D * STAGE];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int wt = blockIdx.x, kz = blockIdx.y;
   const int KS = K >> 5;
   const int ks0 = KS * kz / ksplit;  // KS * ksplit stays far below 2^31
   const int nst = (KS * (kz + 1) / ksplit - ks0) / J;
-  const uint16_t* wb = Wp + (size_t)(wt * G_NW + w) * KS * 512 + l * 8;
+  // pairs [p0, p1) of a fused gate/up workgroup; wave w's weight tile
+  int p0 = 0, p1 = 0, tile = wt * NW + w;
+  if constexpr (OUT == 1) {
+    const int pairs = N >> 5, base = pairs / (int)gridDim.x, extra = pairs % (int)gridDim.x;
+    p0 = wt * base + min(wt, extra);
+    p1 = p0 + base + (wt < extra ? 1 : 0);
+    tile = 2 * min(p0 + (w >> 1), p1 - 1) + (w & 1);
+  }
+  const uint16_t* wb = Wp + (size_t)tile * KS * 512 + l * 8;
 
   // stage st into ring slot b; past the end the last stage is re-issued
   // (same count of loads every stage), never read.  Weights are read once:
@@ -200,7 +218,7 @@ __global__ __launch_bounds__(G_NW * 64) void k_gemm_dma(
                                        16, 0, 2);
 #pragma unroll
     for (int q = 0; q < FPW; q++) {
-      const int f = (w + q * G_NW) % NF;  // waves past NF repeat a fragment: same bytes, same slot
+      const int f = (w + q * NW) % NF;  // waves past NF repeat a fragment: same bytes, same slot
       __builtin_amdgcn_global_load_lds(
           (const void*)(X + ((size_t)(kb + f / MT) * MTT + f % MT) * 512 + l * 8),
           (__attribute__((address_space(3))) void*)(sb + (WKB + f) * 1024), 16, 0, 0);
@@ -236,7 +254,7 @@ __global__ __launch_bounds__(G_NW * 64) void k_gemm_dma(
       const uint32_t b0 = lines * sl / nsl, b1 = lines * (sl + 1) / nsl;
 #pragma unroll
       for (int i = 0; i < XPF; i++) {
-        const uint32_t ln = min(b0 + (uint32_t)((i * G_NW + w) * 8 + (l >> 3)), max(b1, 1u) - 1);
+        const uint32_t ln = min(b0 + (uint32_t)((i * NW + w) * 8 + (l >> 3)), max(b1, 1u) - 1);
         const uint32_t kk = ln / (MT * 8), r = ln - kk * (MT * 8);
         xpf[i] = *(const uint32_t*)(xr + ((size_t)kk * MTT * 8 + r) * 128 + (l & 7) * 16);
       }
@@ -279,7 +297,7 @@ __global__ __launch_bounds__(G_NW * 64) void k_gemm_dma(
   // lane holds rows n = 16*tile + 4*(l/16) + v of token 16*m + l%16
   if (OUT == 0) {
     float* out = P + (size_t)kz * M * N;
-    const int n = (wt * G_NW + w) * 16 + (l >> 4) * 4;
+    const int n = tile * 16 + (l >> 4) * 4;
 #pragma unroll
     for (int m = 0; m < MT; m++) {
       const int t = m * 16 + (l & 15);
@@ -287,20 +305,20 @@ __global__ __launch_bounds__(G_NW * 64) void k_gemm_dma(
     }
   } else {
     // wave 2i holds gate rows, wave 2i+1 the matching up rows (FFN tile
-    // 4*wt + i); the up values pass through the (idle) ring.  The input
+    // p0 + i); the up values pass through the (idle) ring.  The input
     // rows were not normalized: both products take the row's 1/rms here.
     f32x4* ex = (f32x4*)lds;
-    float* invs = (float*)(lds + (G_NW / 2) * MT * 64 * 16);  // 1/rms of each token row
-    static_assert(OUT == 0 || D * STAGE >= (G_NW / 2) * MT * 64 * 16 + MT * 16 * 4, "LDS");
+    float* invs = (float*)(lds + (NW / 2) * MT * 64 * 16);  // 1/rms of each token row
+    static_assert(OUT == 0 || D * STAGE >= (NW / 2) * MT * 64 * 16 + MT * 16 * 4, "LDS");
     lds_barrier();
-    if (tid < M) invs[tid] = row_inv_rms(ssq, ssn, tid, K, eps);
+    for (int t = tid; t < M; t += NW * 64) invs[t] = row_inv_rms(ssq, ssn, t, K, eps);
     if (w & 1) {
 #pragma unroll
       for (int m = 0; m < MT; m++) ex[((w >> 1) * MT + m) * 64 + l] = acc[m];
     }
     __syncthreads();
-    if (!(w & 1)) {
-      const int j = (wt * (G_NW / 2) + (w >> 1)) * 16 + (l >> 4) * 4;
+    if (!(w & 1) && p0 + (w >> 1) < p1) {
+      const int j = (p0 + (w >> 1)) * 16 + (l >> 4) * 4;
 #pragma unroll
       for (int m = 0; m < MT; m++) {
         const int t = m * 16 + (l & 15);
@@ -392,14 +410,14 @@ void launch_gemm_bf16(const uint16_t* X, int MTT, const uint16_t* Wp, int K, int
   else launch_j<1, 0>(MT, grid, X, MTT, Wp, K, plan.ksplit, P, N, M, nullptr, s);
 }
 
-template <int J>
+template <int J, int NW>
 static void launch_dma_swiglu(int MT, dim3 grid, const uint16_t* X, int MTT, const uint16_t* Wp,
                               int K, int N, int M, uint16_t* A, const float* ssq, int ssn,
                               float eps, hipStream_t s) {
-#define LA_GEMM_CASE(mt)                                                                    \
-  case mt:                                                                                  \
-    hipLaunchKernelGGL((k_gemm_dma<mt, J, 1, (mt >= 4)>), grid, dim3(G_NW * 64), 0, s, X, MTT, \
-                       Wp, K, 1, nullptr, N, M, A, ssq, ssn, eps);                          \
+#define LA_GEMM_CASE(mt)                                                                        \
+  case mt:                                                                                      \
+    hipLaunchKernelGGL((k_gemm_dma<mt, J, 1, (mt >= 4), NW>), grid, dim3(NW * 64), 0, s, X, MTT, \
+                       Wp, K, 1, nullptr, N, M, A, ssq, ssn, eps);                              \
     break;
   switch (MT) {
     LA_GEMM_CASE(1) LA_GEMM_CASE(2) LA_GEMM_CASE(3) LA_GEMM_CASE(4)
@@ -411,13 +429,27 @@ static void launch_dma_swiglu(int MT, dim3 grid, const uint16_t* X, int MTT, con
 #undef LA_GEMM_CASE
 }
 
+// Fused gate/up: 8-wave workgroups, 4 gate/up tile pairs each, while that
+// takes at most 256 workgroups (one round on the CUs).  Beyond that (more
+// than 1024 pairs: 34B shape, 1376) the pairs are dealt evenly over 256
+// 12-wave workgroups, up to 6 pairs each, instead of a second round on
+// part of the CUs (34B: gate/up 148 -> 120 us, step 15.8 -> 14.4 ms).
+// Spreading fewer pairs over more workgroups measured no gain: every
+// workgroup loads all activation fragments (13B, 864 pairs over 256
+// workgroups instead of 216: 58 -> 66 us; 7B, 688 pairs with 6-wave
+// groups: within +-1 us).
 void launch_gemm_bf16_swiglu(const uint16_t* X, int MTT, const uint16_t* Wp, int K, int N, int M,
                              int J, uint16_t* A, const float* ssq, int ssn, float eps,
                              hipStream_t s) {
   const int MT = (M + 15) / 16;
-  dim3 grid(N / G_ROWS, 1);
-  if (J == 2) launch_dma_swiglu<2>(MT, grid, X, MTT, Wp, K, N, M, A, ssq, ssn, eps, s);
-  else launch_dma_swiglu<1>(MT, grid, X, MTT, Wp, K, N, M, A, ssq, ssn, eps, s);
+  const int pairs = N / 32;
+  if (pairs > 1024 && pairs <= 6 * 256) {
+    launch_dma_swiglu<1, 12>(MT, dim3(256, 1), X, MTT, Wp, K, N, M, A, ssq, ssn, eps, s);
+    return;
+  }
+  const dim3 grid(pairs / 4, 1);  // N % 128 == 0
+  if (J == 2) launch_dma_swiglu<2, 8>(MT, grid, X, MTT, Wp, K, N, M, A, ssq, ssn, eps, s);
+  else launch_dma_swiglu<1, 8>(MT, grid, X, MTT, Wp, K, N, M, A, ssq, ssn, eps, s);
 }
 
 // ---------------------------------------------------------------------------

@@ -71,6 +71,15 @@ BF16 = [
     lasynth.get_config("7b", name="bf16_plain", n_layers=2, d_model=512, n_heads=4,
                        n_kv_heads=4, d_ffn=1408, vocab=2048, prompt_len=64,
                        span_len=8, n_spans=2, W=0, G=0),
+    # a wide FFN (1056 gate/up tile pairs, as the 34B shape's 1376: dealt
+    # over 256 twelve-wave workgroups) and a 16-way split of the down GEMM;
+    # 57-row steps and plain decode
+    lasynth.get_config("34b", name="bf16_wide_ffn_w7", n_layers=1, d_model=256, n_heads=2,
+                       n_kv_heads=2, d_ffn=16896, vocab=1024, prompt_len=96,
+                       span_len=8, n_spans=2),
+    lasynth.get_config("34b", name="bf16_wide_ffn_plain", n_layers=1, d_model=256, n_heads=2,
+                       n_kv_heads=2, d_ffn=16896, vocab=1024, prompt_len=96,
+                       span_len=8, n_spans=2, W=0, G=0),
 ]
 
 
