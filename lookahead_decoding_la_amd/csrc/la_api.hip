@@ -194,10 +194,11 @@ size_t carve(la_ctx* c, void* base) {
     c->xnf = cv.take<uint16_t>((size_t)c->MR * d);
     c->of = cv.take<uint16_t>((size_t)c->MR * c->qdim);
     c->af = cv.take<uint16_t>((size_t)c->MR * F);
-    c->p_qkv = gemm_bf16_plan(c->qkv_rows, d);
-    c->p_o = gemm_bf16_plan(d, c->qdim);
+    const int step_rows = c->T * B;  // the plans follow the step's row count
+    c->p_qkv = gemm_bf16_plan(c->qkv_rows, d, step_rows);
+    c->p_o = gemm_bf16_plan(d, c->qdim, step_rows);
     c->p_gu = GemmPlan{1, (d / 32) % 2 == 0 ? 2 : 1};  // no split: SwiGLU fused
-    c->p_d = gemm_bf16_plan(d, F);
+    c->p_d = gemm_bf16_plan(d, F, step_rows);
     c->p_lm = GemmPlan{1, (d / 32) % 2 == 0 ? 2 : 1};
     size_t gp = 0;
     gp = std::max(gp, (size_t)c->p_qkv.ksplit * c->MR * c->qkv_rows);

@@ -338,19 +338,33 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_dma(
 
 bool gemm_bf16_shape_ok(int N, int K) { return N % G_ROWS == 0 && K % 32 == 0; }
 
-GemmPlan gemm_bf16_plan(int N, int K) {
+// K split of a plain GEMM for a step of `rows` rows, with at least 6
+// k-steps per split.
+//  - From 4 token tiles on (the LDS-direct kernel, every workgroup loading
+//    its K range's activation fragments): the largest split count that
+//    keeps the workgroups within one round on the 256 CUs (tiles * ks <=
+//    256); more would start a second round on part of the CUs for no
+//    smaller share of K per CU, plus partial-sum traffic (13B O and down:
+//    4 splits instead of 8, 34B QKV 2 instead of 4: steps 0.8% faster).
+//  - Below (one-token decode: a workgroup's work is nearly all weights):
+//    the smallest split count that reaches 192 workgroups; there more
+//    workgroups are only more parallelism (the one-round rule made 13B and
+//    34B plain decode 4-6% slower).
+GemmPlan gemm_bf16_plan(int N, int K, int rows) {
   GemmPlan p;
   const int tiles = N / G_ROWS, KS = K / 32;
+  const bool one_round = (rows + 15) / 16 >= 4;
   p.ksplit = 1;
   p.J = KS % 2 == 0 ? 2 : 1;
-  const int cands[] = {1, 2, 4, 8, 16};
+  const int cands[] = {2, 4, 8, 16};
   for (int ks : cands) {
     if (KS % ks) continue;
     const int per = KS / ks;
     if (per < 6) break;
+    if (one_round && tiles * ks > 256) break;
+    if (!one_round && tiles * p.ksplit >= 192) break;
     p.ksplit = ks;
     p.J = per % 2 == 0 ? 2 : 1;
-    if (tiles * ks >= 192) break;
   }
   return p;
 }

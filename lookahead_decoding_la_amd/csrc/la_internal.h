@@ -200,7 +200,7 @@ struct GemmPlan {
   int J;       // k-steps per pipeline stage
 };
 bool gemm_bf16_shape_ok(int N, int K);
-GemmPlan gemm_bf16_plan(int N, int K);
+GemmPlan gemm_bf16_plan(int N, int K, int rows);
 void launch_gemm_bf16(const uint16_t* X, int MTT, const uint16_t* Wp, int K, int N, int M,
                       const GemmPlan& plan, float* P, hipStream_t s);
 // Fused gate/up (alternating 16-row gate / up tiles, no K split) with the
