@@ -76,7 +76,7 @@ def traffic_from_profiles(kernel_key: str):
 
 
 COPY_PROBE_BYTES = 1 << 29  # bytes read (and written) by one --copy-probe launch
-GATEUP_RE = r"k_gemm_(bf16|dma)<\d+, \d+, 1(, \w+)?>"
+GATEUP_RE = r"k_gemm_(bf16|dma)<\d+, \d+, 1(, \w+)*>"
 COPY_RE = r"neg_kernel"
 
 
@@ -446,7 +446,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profiles(f"gate_up_{cfg.name}"),
-                "kernel": "k_gemm_dma<8, 2, 1, true> (fused gate/up + SwiGLU)",
+                "kernel": "k_gemm_dma<8, 2, 1, true, 8> (fused gate/up + SwiGLU)",
                 "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_s * 1e6, 2),
                 "avg_launch_us_step_events": round(gu_step * 1e3, 2)}
     # the same step with sampled verification (temperature 0.8, top-k 50,
