@@ -340,8 +340,9 @@ static int argmax_f32(const double *lg, int V) {
 }
 
 /* ------------------------------------------------------------------------ */
-/* sampling (the pages say the method supports several
- * sampling schemes but give no algorithm, so all of this is a reading)     */
+/* sampling ("Break the Sequential Dependency of LLM Inference Using
+ * Lookahead Decoding", Summary: the method supports sampling as well as
+ * greedy decoding, with no algorithm given, so all of this is a reading)   */
 
 /* Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and
  * Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC'11): ten rounds;

@@ -1,4 +1,5 @@
-"""Pin the oracle's sampled decoding.
+"""Pin the oracle's sampled decoding ("Break the Sequential Dependency of LLM
+Inference Using Lookahead Decoding", Summary: sampling is supported).
 
 The pages say lookahead decoding supports several sampling schemes but give
 no algorithm; the oracle's reading (C source, "sampling"):
