@@ -330,6 +330,62 @@ def cpu_baseline(cfg, prompt, win, n_steps=3):
     }
 
 
+def attention_bench(steps, warmup):
+    """The kernel-only masked attention workload (lasynth.ATTN: 32 heads x
+    128, committed prefix 1024, W15 N5 G15 = 121 query rows; Q, K, V drawn
+    N(0, 1) in bf16 from a seeded generator): one la_attention call per
+    layer-sized problem, HBM-cold (16 copies of the inputs, 330 MB in all,
+    used in turn, so no call finds its K/V in the 256 MB last-level cache),
+    timed with HIP events around `steps` calls on one stream.  Roofline:
+    the bytes one call must move (K and V for prefix + block, Q in, output
+    out: 20.74 MB) at 8 TB/s.  Prints one JSON line."""
+    import torch
+    import lookahead_decoding_la_amd as la
+    a = lasynth.ATTN
+    H, Hkv, dh, L = a["n_heads"], a["n_kv_heads"], a["head_dim"], a["prefix"]
+    W, N, G = a["W"], a["N"], a["G"]
+    T = 1 + (W + G) * (N - 1)
+    ctx = ((L + T + 63) // 64) * 64
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    copies = []
+    for _ in range(16):
+        q = torch.randn((T, H, dh), generator=gen, device=dev).to(torch.bfloat16)
+        k = torch.randn((Hkv, ctx, dh), generator=gen, device=dev).to(torch.bfloat16)
+        vt = torch.randn((Hkv, dh, ctx), generator=gen, device=dev).to(torch.bfloat16)
+        copies.append((q, k, vt))
+    out = torch.empty((T, H, dh), dtype=torch.bfloat16, device=dev)
+    need = int(la.lib().la_attention_workspace_bytes(H, dh, ctx, W, N, G))
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        q, k, vt = copies[i % len(copies)]
+        la.attention(q, k, vt, out, H, Hkv, L, W, N, G, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        q, k, vt = copies[i % len(copies)]
+        la.attention(q, k, vt, out, H, Hkv, L, W, N, G, workspace=ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    nbytes = 2 * Hkv * (L + T) * dh * 2 + 2 * T * H * dh * 2
+    gbs = nbytes / (us * 1e-6) / 1e9
+    log(f"attention {H}x{dh}, prefix {L}, {T} rows: {us:.2f} us per call (attention + merge), "
+        f"{nbytes / 1e6:.2f} MB -> {gbs:.0f} GB/s, {gbs / 8000:.3f} of 8 TB/s")
+    print(json.dumps({
+        "metric": "kernel-only masked attention us per call", "value": round(us, 3),
+        "unit": "us", "higher_is_better": False, "steps": steps, "warmup": warmup,
+        "dtype": "bf16", "data": "synthetic: Q, K, V ~ N(0,1), seeded; 16 input copies used in turn",
+        "config": {"workload": f"masked attention {H} heads x {dh}, prefix {L}, "
+                               f"W={W} N={N} G={G} ({T} query rows)"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(gbs / 8000, 4), "bytes_per_call": nbytes,
+                     "t_roof_us": round(nbytes / 8e12 * 1e6, 3)}}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -348,6 +404,8 @@ def main():
                     help="throughput vs batch size (sequences per step) and step shape")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only the copy kernel used to calibrate HBM counters")
+    ap.add_argument("--attention", action="store_true",
+                    help="the kernel-only masked attention workload (one JSON line)")
     ap.add_argument("--write-traffic", nargs=4, metavar="DIR",
                     help="rocprofv3 csv runs: bench FETCH_SIZE, bench WRITE_SIZE, "
                          "copy FETCH_SIZE, copy WRITE_SIZE; writes profiles/traffic.json")
@@ -367,6 +425,10 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the "
               "lookahead step runs on a single MI355X", file=sys.stderr)
         sys.exit(2)
+
+    if args.attention:
+        attention_bench(args.steps * 16, args.warmup)
+        return
 
     import torch
     import lookahead_decoding_la_amd as la
