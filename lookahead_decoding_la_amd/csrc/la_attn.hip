@@ -34,15 +34,26 @@ constexpr int AKC = 64;        // keys per chunk
 constexpr int A_DH = 128;      // head_dim of the bf16 kernel
 constexpr float LOG2E = 1.4426950408889634f;
 
+// Max / sum over the four 16-lane groups of a wave (lanes l, l^16, l^32,
+// l^48), with the gfx950 row swaps instead of LDS permutes:
+// permlane16_swap(v, v) yields rows (0, 0, 2, 2) and (1, 1, 3, 3) of v,
+// permlane32_swap(v, v) halves (0, 0) and (1, 1); combining each pair gives
+// every lane the same operands, in the same order, as xor-16 then xor-32
+// shuffles would.
+__device__ inline float swap_max16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ inline float wave_max_groups(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  v = swap_max16(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ inline float wave_sum_groups(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ inline bool key_visible(int mode, const RowDesc& rd, int t, int M,
