@@ -64,7 +64,7 @@ typedef struct {
                        token, and a step forwards B blocks of rows at once */
 } la_config;
 /* Supported shapes.  LA_BF16: head_dim 128, d_model % 128 == 0 and
- * <= 8192, d_ffn % 64 == 0, vocab % 128 == 0.  LA_F32 (small models): head_dim even and
+ * <= 8192, d_ffn % 64 == 0, vocab % 128 == 0, max_ctx <= 2^24.  LA_F32 (small models): head_dim even and
  * <= 256, d_model, d_ffn and vocab even, max_ctx <= 16384.  Both:
  * n_heads % n_kv_heads == 0 and B (1 + (W + G)(N - 1)) <= 256 (B = batch).
  * W = G = 0 gives the plain one-token greedy decode step.
@@ -256,7 +256,8 @@ la_status la_debug_state(la_ctx *c, int32_t *kv_len, int32_t *current);
  *   ctx_stride % 64 == 0 and prefix_len + rows <= ctx_stride.
  *   workspace: DEVICE, la_attention_workspace_bytes() bytes (split-KV
  *   partial results); stream: hipStream_t or NULL.  Asynchronous.
- * Errors: LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED (head_dim != 128),
+ * Errors: LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED (head_dim != 128 or
+ * ctx_stride > 2^24),
  * LA_ERR_OUT_OF_CAPACITY (workspace too small), LA_ERR_HIP. */
 size_t la_attention_workspace_bytes(int32_t n_heads, int32_t head_dim,
                                     int32_t ctx_stride, int32_t W, int32_t N,

@@ -4,7 +4,10 @@
 
 Every HIP source in csrc/ is compiled with hipcc to an object file, then
 linked into lookahead_decoding_la_amd/liblaamd.so.  Packed-fp32 instructions
-are turned off for all device code.
+are turned off for all device code.  The attention source selects its MFMAs
+with VGPR accumulators: its softmax rescales the accumulators with vector
+ALU operations, which cannot read AGPRs, and with AGPR accumulators the
+compiler copies all of them between the two register files in every chunk.
 """
 from __future__ import annotations
 
@@ -24,6 +27,9 @@ CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-result", "-I", os.path.join(ROOT, "include")]
 
+# extra flags per source file
+FILE_FLAGS = {"la_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
 
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
@@ -37,7 +43,7 @@ def build(verbose: bool = False) -> str:
     for src in sources():
         obj = os.path.join(OBJ, os.path.basename(src)[:-4] + ".o")
         objs.append(obj)
-        cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+        cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), file=sys.stderr)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,

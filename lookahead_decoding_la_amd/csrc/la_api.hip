@@ -154,6 +154,7 @@ la_status check_config(const la_config* cfg, std::string* why) {
     if (c.d_model % 128 || c.d_ffn % 64 || c.vocab % 128)
       return uns("bf16 kernels need d_model and vocab multiples of 128, d_ffn of 64");
     if (c.d_model > 8192) return uns("bf16 kernels need d_model <= 8192");
+    if (c.max_ctx > (1 << 24)) return uns("bf16 kernels need max_ctx <= 16777216");
   } else {
     if (c.head_dim > 256) return uns("f32 kernels need head_dim <= 256");
     if (c.d_model % 2 || c.d_ffn % 2 || c.vocab % 2) return uns("f32 kernels need even sizes");
@@ -956,7 +957,7 @@ la_status la_attention(const void* q, const void* k_cache, const void* vt_cache,
   if (n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads || N < 2 || N > 32 || W < 0 || G < 0 ||
       prefix_len < 0 || ctx_stride < 1)
     return LA_ERR_INVALID_ARG;
-  if (head_dim != 128) return LA_ERR_UNSUPPORTED;
+  if (head_dim != 128 || ctx_stride > (1 << 24)) return LA_ERR_UNSUPPORTED;
   const long T = 1 + (long)(W + G) * (N - 1);
   if (T > MAX_ROWS) return LA_ERR_UNSUPPORTED;
   if (ctx_stride % 64 || prefix_len + T > ctx_stride) return LA_ERR_INVALID_ARG;

@@ -184,7 +184,9 @@ __global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
   const int RG = (M + QROWS - 1) / QROWS;  // row groups
   const int h = blockIdx.x, sq = blockIdx.z;  // head, sequence
   const int sp = blockIdx.y / RG, tb = (blockIdx.y % RG) * QROWS;  // key split, first row
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c16 = l & 15;
+  // the wave index is wave-uniform: LDS destinations and chunk bases go to scalar registers
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63,
+            g = l >> 4, c16 = l & 15;
   const int rp = w % NRP, kp = w / NRP;
   const int r0 = sq * a.rps;  // the sequence's first row in q and out
 
@@ -225,41 +227,44 @@ __global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
   const uint16_t* kc = (const uint16_t*)a.k_cache + sq * a.kv_seq + (size_t)kvh * a.ctx_stride * A_DH;
   const uint16_t* vc = (const uint16_t*)a.vt_cache + sq * a.kv_seq + (size_t)kvh * A_DH * a.ctx_stride;
 
-  // Row masks of this wave's two tiles (padding tokens take a valid row).
-  // They are computed, not loaded: an ordinary global load in flight next
-  // to the LDS-direct loads makes the compiler wait for every outstanding
-  // load before its first use.
-  uint64_t rm[2][4];
+  // Rows of this wave's two tiles (padding tokens take a valid row).
   int trow[2];
 #pragma unroll
   for (int u = 0; u < 2; u++) {
     const int t = tb + (2 * rp + u) * 16 + c16;
     trow[u] = t < M ? t : (causal ? M - 1 : 0);
-#pragma unroll
-    for (int i = 0; i < 4; i++) rm[u][i] = 0ull;
-    if (!causal) step_row_mask(trow[u], a.W, a.N, rm[u][0], rm[u][1], rm[u][2], rm[u][3]);
   }
   const bool act = tb + 2 * rp * 16 < M;  // tile 2 rp holds tokens
   const bool act1 = tb + (2 * rp + 1) * 16 < M;
 
   // Issue chunk c into ring slot b.  Instruction j of a chunk (wave-uniform
   // LDS base, 1 KiB per instruction) covers K keys 4j..4j+3 or V^T dims
-  // 8j..8j+7; lane l loads the global piece that belongs at LDS slot l.
+  // 8j..8j+7; lane l loads the global piece that belongs at LDS slot l.  The
+  // lane's byte offsets within a chunk are fixed (32-bit: the V^T rows of one
+  // head span 128 x ctx_stride x 2 bytes, ctx_stride <= 2^24); the chunk's
+  // own offset is wave-uniform.
+  uint32_t koff[LPC / 2], voff[LPC / 2];
+#pragma unroll
+  for (int q = 0; q < LPC / 2; q++) {
+    const int j = w + q * NW;  // 0..15
+    const int r = 4 * j + (l >> 4), sk = l & 15;
+    koff[q] = (uint32_t)(r * A_DH + ((sk ^ kswz(r)) * 8)) * 2u;
+    const int d = 8 * j + (l >> 3), sv = l & 7;
+    voff[q] = ((uint32_t)d * (uint32_t)a.ctx_stride + (uint32_t)((sv ^ ((d >> 1) & 7)) * 8)) * 2u;
+  }
   auto issue = [&](int c, int b) {
     c = min(c, nch - 1);  // an empty range (c0 == nch) stages a valid chunk
     unsigned char* kb = lds + b * CH_BYTES;
     unsigned char* vb = kb + CH_K_BYTES;
+    const unsigned char* kg = (const unsigned char*)(kc + (size_t)c * AKC * A_DH);
+    const unsigned char* vg = (const unsigned char*)(vc + (size_t)c * AKC);
 #pragma unroll
     for (int q = 0; q < LPC / 2; q++) {
-      const int j = w + q * NW;  // 0..15
-      const int r = 4 * j + (l >> 4), sk = l & 15;
-      const uint16_t* gk = kc + (size_t)(c * AKC + r) * A_DH + ((sk ^ kswz(r)) * 8);
-      __builtin_amdgcn_global_load_lds((const void*)gk,
+      const int j = w + q * NW;
+      __builtin_amdgcn_global_load_lds((const void*)(kg + koff[q]),
                                        (__attribute__((address_space(3))) void*)(kb + j * 1024),
                                        16, 0, 0);
-      const int d = 8 * j + (l >> 3), sv = l & 7;
-      const uint16_t* gv = vc + (size_t)d * a.ctx_stride + c * AKC + ((sv ^ ((d >> 1) & 7)) * 8);
-      __builtin_amdgcn_global_load_lds((const void*)gv,
+      __builtin_amdgcn_global_load_lds((const void*)(vg + voff[q]),
                                        (__attribute__((address_space(3))) void*)(vb + j * 1024),
                                        16, 0, 0);
     }
@@ -271,14 +276,11 @@ __global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
   for (int i = 0; i < NBUF - 1; i++) issue(c0 + min(i, max(nloc - 1, 0)), i);
   wait_vm<(NBUF - 2) * LPC>();  // Q (issued first) has landed
   lds_barrier();
-  bf16x8 qf[2][4];
+  // Q fragments of this wave's tiles are read from LDS in every chunk (not
+  // held in registers: the register budget goes to the accumulators).
+  const unsigned char* qrow[2];
 #pragma unroll
-  for (int u = 0; u < 2; u++) {
-    const int t = (2 * rp + u) * 16 + c16;
-#pragma unroll
-    for (int ks = 0; ks < 4; ks++)
-      qf[u][ks] = *(const bf16x8*)(qb + t * 256 + (((4 * ks + g) ^ c16) << 4));
-  }
+  for (int u = 0; u < 2; u++) qrow[u] = qb + ((2 * rp + u) * 16 + c16) * 256;
 
   f32x4 o[2][8];
   float m_run[2], l_run[2];
@@ -290,118 +292,147 @@ __global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
     for (int i = 0; i < 8; i++) o[u][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int i = 0; i < nloc; i++) {
-    const int c = c0 + i;
-    // keep NBUF - 1 chunks in flight: chunk i + NBUF - 1 goes into the slot
-    // chunk i - 1 used (every wave finished with it at the last barrier);
-    // past the end the last chunk is re-issued, never read
-    issue(c0 + min(i + NBUF - 1, nloc - 1), (i + NBUF - 1) % NBUF);
-    wait_vm<(NBUF - 1) * LPC>();  // this thread's part of chunk i has landed
-    lds_barrier();                 // ... and everyone else's
-    unsigned char* kb = lds + (i % NBUF) * CH_BYTES;
-    unsigned char* vb = kb + CH_K_BYTES;
-    const bool full = (c + 1) * AKC <= L;  // whole chunk in the committed prefix
-    const int b0 = c * AKC - L;
-    // the second tile is skipped (MFMAs, softmax) when it holds no rows
-    auto chunk = [&](auto two) {
-      constexpr bool TWO = decltype(two)::value;
-      f32x4 s[2][KT];
+  // One 64-key chunk for this wave's tiles: TWO = the second tile holds
+  // rows (else its MFMAs and softmax are skipped), MASKED = the chunk reaches
+  // into the block (else every key is committed prefix, visible to every
+  // row, and lies inside the context).  Scores stay unscaled until the
+  // exponent: max(s) * scale is the max of the scaled scores (rounding is
+  // monotone), and exp2(s * scale - m) is one fma.
+  auto chunk = [&](auto two, auto masked, const unsigned char* kb, const unsigned char* vb,
+                   int c) {
+    constexpr bool TWO = decltype(two)::value, MASKED = decltype(masked)::value;
+    f32x4 s[2][KT];
 #pragma unroll
-      for (int j = 0; j < KT; j++) {
-        const int kt = kp * KT + j;
-        s[0][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        s[1][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int r = score_key(kt, c16);
-        const unsigned char* krow = kb + r * 256;
-        const int sw = kswz(r);
+    for (int j = 0; j < KT; j++) {
+      const int kt = kp * KT + j;
+      s[0][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      s[1][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int r = score_key(kt, c16);
+      const unsigned char* krow = kb + r * 256;
+      const int sw = kswz(r);
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++) {
-          const bf16x8 kf = *(const bf16x8*)(krow + (((4 * ks + g) ^ sw) << 4));
-          s[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], s[0][j], 0, 0, 0);
-          if constexpr (TWO)
-            s[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][ks], s[1][j], 0, 0, 0);
+      for (int ks = 0; ks < 4; ks++) {
+        const bf16x8 kf = *(const bf16x8*)(krow + (((4 * ks + g) ^ sw) << 4));
+        const bf16x8 q0 = *(const bf16x8*)(qrow[0] + (((4 * ks + g) ^ c16) << 4));
+        s[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, q0, s[0][j], 0, 0, 0);
+        if constexpr (TWO) {
+          const bf16x8 q1 = *(const bf16x8*)(qrow[1] + (((4 * ks + g) ^ c16) << 4));
+          s[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, q1, s[1][j], 0, 0, 0);
         }
       }
-      bf16x8 pf[2][KT / 2];
+    }
+    bf16x8 pf[2][KT / 2];
 #pragma unroll
-      for (int u = 0; u < (TWO ? 2 : 1); u++) {
-        const uint64_t win = full ? ~0ull
-                                  : chunk_window(causal, trow[u], b0, rm[u][0], rm[u][1],
-                                                 rm[u][2], rm[u][3]) >> (8 * g);
-        float mx = -INFINITY;
+    for (int u = 0; u < (TWO ? 2 : 1); u++) {
+      if constexpr (MASKED) {  // the row's 256-bit block mask, recomputed (few chunks are masked)
+        uint64_t rm0 = 0ull, rm1 = 0ull, rm2 = 0ull, rm3 = 0ull;
+        if (!causal) step_row_mask(trow[u], a.W, a.N, rm0, rm1, rm2, rm3);
+        const uint64_t win = chunk_window(causal, trow[u], c * AKC - L, rm0, rm1, rm2, rm3) >> (8 * g);
 #pragma unroll
         for (int j = 0; j < KT; j++) {
           const int kt = kp * KT + j;
 #pragma unroll
           for (int v = 0; v < 4; v++) {
             const int bit = 32 * (kt >> 1) + 4 * (kt & 1) + v;
-            const float x = ((win >> bit) & 1ull) ? s[u][j][v] * sl2 : -INFINITY;
-            s[u][j][v] = x;
-            mx = fmaxf(mx, x);
+            if (!((win >> bit) & 1ull)) s[u][j][v] = -INFINITY;
           }
         }
-        mx = wave_max_groups(mx);
-        if (__builtin_amdgcn_ballot_w64(mx > m_run[u] + RESCALE_LOG2)) {  // wave-uniform
-          const float m_new = fmaxf(m_run[u], mx);
-          const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[u] - m_new);
-          l_run[u] *= alpha;
-#pragma unroll
-          for (int d = 0; d < 8; d++) o[u][d] *= alpha;
-          m_run[u] = m_new;
-        }
-        const float m_use = m_run[u] == -INFINITY ? 0.f : m_run[u];  // nothing visible yet
-        float ps = 0.f;
-#pragma unroll
-        for (int j = 0; j < KT; j++)
-#pragma unroll
-          for (int v = 0; v < 4; v++) {
-            const float p = __builtin_amdgcn_exp2f(s[u][j][v] - m_use);
-            s[u][j][v] = p;
-            ps += p;
-          }
-        l_run[u] += ps;
-#pragma unroll
-        for (int j2 = 0; j2 < KT / 2; j2++)
-#pragma unroll
-          for (int v = 0; v < 4; v++) {
-            pf[u][j2][v] = (__bf16)s[u][2 * j2][v];
-            pf[u][j2][4 + v] = (__bf16)s[u][2 * j2 + 1][v];
-          }
       }
-      // O^T += V^T P^T over this wave's 32-key steps.  Keys past ctx (last
-      // chunk only) have zero probability, but their V^T entries may be
-      // stale or uninitialised memory: mask them to zero so that no NaN
-      // reaches the MFMA.
-      const int nvk = ctx - c * AKC;
+      float mx = -INFINITY;
 #pragma unroll
-      for (int j2 = 0; j2 < KT / 2; j2++) {
-        const int s2 = kp * (KT / 2) + j2;
-        const int kv = nvk - (32 * s2 + 8 * g);  // valid keys among this lane's 8
-        const uint32_t vm0 = kv >= 2 ? ~0u : (kv == 1 ? 0xffffu : 0u);
-        const uint32_t vm1 = kv >= 4 ? ~0u : (kv == 3 ? 0xffffu : 0u);
-        const uint32_t vm2 = kv >= 6 ? ~0u : (kv == 5 ? 0xffffu : 0u);
-        const uint32_t vm3 = kv >= 8 ? ~0u : (kv == 7 ? 0xffffu : 0u);
+      for (int j = 0; j < KT; j++)
 #pragma unroll
-        for (int dt = 0; dt < 8; dt++) {
-          const int d = dt * 16 + c16;
-          bf16x8 vf = *(const bf16x8*)(vb + d * 128 + (((4 * s2 + g) ^ ((d >> 1) & 7)) << 4));
+        for (int v = 0; v < 4; v++) mx = fmaxf(mx, s[u][j][v]);
+      mx = wave_max_groups(mx) * sl2;
+      if (__builtin_amdgcn_ballot_w64(mx > m_run[u] + RESCALE_LOG2)) {  // wave-uniform
+        const float m_new = fmaxf(m_run[u], mx);
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[u] - m_new);
+        l_run[u] *= alpha;
+#pragma unroll
+        for (int d = 0; d < 8; d++) o[u][d] *= alpha;
+        m_run[u] = m_new;
+      }
+      const float nm = m_run[u] == -INFINITY ? 0.f : -m_run[u];  // nothing visible yet: 0
+      float ps = 0.f;
+#pragma unroll
+      for (int j = 0; j < KT; j++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[u][j][v], sl2, nm));
+          s[u][j][v] = p;
+          ps += p;
+        }
+      l_run[u] += ps;
+#pragma unroll
+      for (int j2 = 0; j2 < KT / 2; j2++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+          pf[u][j2][v] = (__bf16)s[u][2 * j2][v];
+          pf[u][j2][4 + v] = (__bf16)s[u][2 * j2 + 1][v];
+        }
+    }
+    // O^T += V^T P^T over this wave's 32-key steps.  Keys past ctx (last
+    // chunk only, a masked one) have zero probability, but their V^T entries
+    // may be stale or uninitialised memory: mask them to zero so that no NaN
+    // reaches the MFMA.
+    const int nvk = ctx - c * AKC;
+#pragma unroll
+    for (int j2 = 0; j2 < KT / 2; j2++) {
+      const int s2 = kp * (KT / 2) + j2;
+      const int kv = nvk - (32 * s2 + 8 * g);  // valid keys among this lane's 8
+      const uint32_t vm0 = kv >= 2 ? ~0u : (kv == 1 ? 0xffffu : 0u);
+      const uint32_t vm1 = kv >= 4 ? ~0u : (kv == 3 ? 0xffffu : 0u);
+      const uint32_t vm2 = kv >= 6 ? ~0u : (kv == 5 ? 0xffffu : 0u);
+      const uint32_t vm3 = kv >= 8 ? ~0u : (kv == 7 ? 0xffffu : 0u);
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++) {
+        const int d = dt * 16 + c16;
+        bf16x8 vf = *(const bf16x8*)(vb + d * 128 + (((4 * s2 + g) ^ ((d >> 1) & 7)) << 4));
+        if constexpr (MASKED) {
           if (nvk < AKC) {  // uniform
             uint4 vr = __builtin_bit_cast(uint4, vf);
             vr.x &= vm0; vr.y &= vm1; vr.z &= vm2; vr.w &= vm3;
             vf = __builtin_bit_cast(bf16x8, vr);
           }
-          o[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[0][j2], o[0][dt], 0, 0, 0);
-          if constexpr (TWO)
-            o[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[1][j2], o[1][dt], 0, 0, 0);
         }
+        o[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[0][j2], o[0][dt], 0, 0, 0);
+        if constexpr (TWO)
+          o[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[1][j2], o[1][dt], 0, 0, 0);
       }
-    };
-    if (act1)
-      chunk(std::true_type{});
-    else if (act)
-      chunk(std::false_type{});
+    }
+  };
+
+  // The chunk loop, one copy per tile count (WORK: 2 = both tiles hold rows,
+  // 1 = the first only, 0 = neither: the wave only loads and meets the
+  // barriers), and within it one run over the chunks wholly inside the
+  // committed prefix (no mask) followed by one over those reaching into the
+  // block, so no branch on either sits inside a loop.
+  const int nfree = min(max(L / AKC - c0, 0), nloc);  // chunks c0 .. c0 + nfree - 1 need no mask
+  auto step = [&](int i, auto work, auto masked) {
+    constexpr int WORK = decltype(work)::value;
+    // keep NBUF - 1 chunks in flight: chunk i + NBUF - 1 goes into the slot
+    // chunk i - 1 used (every wave finished with it at the last barrier);
+    // past the end the last chunk is re-issued, never read
+    issue(c0 + min(i + NBUF - 1, nloc - 1), (i + NBUF - 1) % NBUF);
+    wait_vm<(NBUF - 1) * LPC>();  // this thread's part of chunk i has landed
+    lds_barrier();                 // ... and everyone else's
+    if constexpr (WORK > 0) {
+      const unsigned char* kb = lds + (i % NBUF) * CH_BYTES;
+      chunk(std::integral_constant<bool, WORK == 2>{}, masked, kb, kb + CH_K_BYTES, c0 + i);
+    }
     lds_barrier();  // slot i % NBUF is free for the next issue
-  }
+  };
+  auto run = [&](auto work) {
+    int i = 0;
+    for (; i < nfree; i++) step(i, work, std::false_type{});
+    for (; i < nloc; i++) step(i, work, std::true_type{});
+  };
+  if (act1)
+    run(std::integral_constant<int, 2>{});
+  else if (act)
+    run(std::integral_constant<int, 1>{});
+  else
+    run(std::integral_constant<int, 0>{});
   wait_vm<0>();  // drain the ring's redundant loads (also before LDS reuse)
 
   float lsum[2];

@@ -54,6 +54,9 @@ def test_create_rejects_bad_config_without_gpu():
     assert not h.value
     c = la.make_config(lasynth.get_config("7b", dtype="bf16", d_model=4008), 1024)
     assert lib.la_create(C.byref(c), ptrs, C.c_void_p(1), 1 << 20, None, C.byref(h)) == la.LA_ERR_UNSUPPORTED
+    # bf16 attention addresses a head's V^T rows with 32-bit offsets: max_ctx <= 2^24
+    c = la.make_config(lasynth.get_config("7b", dtype="bf16"), (1 << 24) + 1)
+    assert lib.la_create(C.byref(c), ptrs, C.c_void_p(1), 1 << 20, None, C.byref(h)) == la.LA_ERR_UNSUPPORTED
     c = _cfg()
     assert lib.la_create(C.byref(c), ptrs, C.c_void_p(1), 16, None, C.byref(h)) == la.LA_ERR_OUT_OF_CAPACITY
     assert lib.la_create(C.byref(c), None, C.c_void_p(1), 1 << 30, None, C.byref(h)) == la.LA_ERR_INVALID_ARG
@@ -81,6 +84,8 @@ def test_attention_argument_checks_without_gpu():
     assert lib.la_attention(one, one, one, one, 32, 32, 128, 16, 100, 15, 5, 15, one, 1 << 30, None) == la.LA_ERR_INVALID_ARG
     assert lib.la_attention(one, one, one, one, 32, 32, 128, 200, 256, 15, 5, 15, one, 1 << 30, None) == la.LA_ERR_INVALID_ARG
     assert lib.la_attention(one, one, one, one, 32, 32, 128, 16, 256, 15, 5, 15, one, 8, None) == la.LA_ERR_OUT_OF_CAPACITY
+    assert lib.la_attention(one, one, one, one, 32, 32, 128, 16, (1 << 24) + 64, 15, 5, 15, one, 1 << 30,
+                            None) == la.LA_ERR_UNSUPPORTED
     assert lib.la_attention_workspace_bytes(32, 128, 1152, 15, 5, 15) > 0
 
 
