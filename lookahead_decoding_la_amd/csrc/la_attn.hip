@@ -553,17 +553,23 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 // groups from 65 to 128 rows, one workgroup per head otherwise.
 static int attn_row_groups(int M) { return M > 64 && M <= 128 ? (M + 31) / 32 : 1; }
 
+// Waves per workgroup of that instance.
+static int attn_waves(int M) { return M > 32 && M <= 64 ? 4 : (M <= 128 ? 2 : 8); }
+
 // Splits the launch provides for (the grid's second dimension and the
 // partial buffers): what eff_splits asks for at the longest context, capped
-// so that heads x sequences x row groups x splits stays near 512 workgroups
-// (one resident round at two per CU): more splits than that only add
-// prologues, merge traffic and a second round of workgroups (measured at 40
-// heads x 81 rows, 1100 committed tokens: 4 splits 22 us, 7 splits 27-29
-// us; at 64 heads x 57 rows, 2100 tokens: 4 splits 26 us, 8 splits 33 us),
-// and a large batch fills the chip without splitting the keys.  H counts the
-// heads of all sequences.
+// so that up to 128 rows heads x sequences x row groups x splits x waves
+// stays near 1024 waves (one per SIMD; above 128 rows near 512 workgroups):
+// more splits than that only add prologues, merge traffic and waves that
+// share a SIMD.  Measured in captured graphs: 40 heads x 81 rows, 1100
+// committed tokens: 3-4 splits 17.8 us, 6 splits 19.2 us, 8 splits 21.4 us;
+// 64 heads (8 KV heads) x 57 rows, 2100 tokens: 4 splits 20.8 us, 8 splits
+// 24.2 us; 32 heads x 121 rows, 1024 tokens: 4 splits 17.5 us, 3 splits
+// 19.5 us.  A large batch fills the chip without splitting the keys.  H
+// counts the heads of all sequences.
 int attn_bf16_splits(int H, int M, int max_ctx) {
-  const int cap = std::max(1, 512 / (H * attn_row_groups(M)));
+  const int per = H * attn_row_groups(M);
+  const int cap = std::max(1, M <= 128 ? 1024 / (per * attn_waves(M)) : 512 / per);
   return eff_splits((max_ctx + M + AKC - 1) / AKC, std::min(A_MAX_SPLITS, cap), M);
 }
 
@@ -586,7 +592,7 @@ void launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   // committed tokens: 1-4 us per layer faster than one 128-row workgroup per
   // head; at 57 rows, 64 heads and 2100 tokens one 64-row group is 3.7 us
   // faster than two of 32); above 128 rows one workgroup of 8 row pairs per
-  // head.  attn_row_groups mirrors this choice.
+  // head.  attn_row_groups and attn_waves mirror this choice.
   if (a.M <= 32)
     launch_attn_inst<1, 2, 2>(a, s);
   else if (a.M <= 64)
