@@ -276,11 +276,14 @@ __global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
   for (int i = 0; i < NBUF - 1; i++) issue(c0 + min(i, max(nloc - 1, 0)), i);
   wait_vm<(NBUF - 2) * LPC>();  // Q (issued first) has landed
   lds_barrier();
-  // Q fragments of this wave's tiles are read from LDS in every chunk (not
-  // held in registers: the register budget goes to the accumulators).
-  const unsigned char* qrow[2];
+  bf16x8 qf[2][4];  // Q fragments of this wave's tiles, held for the whole loop
 #pragma unroll
-  for (int u = 0; u < 2; u++) qrow[u] = qb + ((2 * rp + u) * 16 + c16) * 256;
+  for (int u = 0; u < 2; u++) {
+    const int t = (2 * rp + u) * 16 + c16;
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++)
+      qf[u][ks] = *(const bf16x8*)(qb + t * 256 + (((4 * ks + g) ^ c16) << 4));
+  }
 
   f32x4 o[2][8];
   float m_run[2], l_run[2];
@@ -313,12 +316,9 @@ __global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 4; ks++) {
         const bf16x8 kf = *(const bf16x8*)(krow + (((4 * ks + g) ^ sw) << 4));
-        const bf16x8 q0 = *(const bf16x8*)(qrow[0] + (((4 * ks + g) ^ c16) << 4));
-        s[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, q0, s[0][j], 0, 0, 0);
-        if constexpr (TWO) {
-          const bf16x8 q1 = *(const bf16x8*)(qrow[1] + (((4 * ks + g) ^ c16) << 4));
-          s[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, q1, s[1][j], 0, 0, 0);
-        }
+        s[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], s[0][j], 0, 0, 0);
+        if constexpr (TWO)
+          s[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][ks], s[1][j], 0, 0, 0);
       }
     }
     bf16x8 pf[2][KT / 2];
