@@ -115,3 +115,29 @@ def test_batch_config_limits():
     assert la.workspace_bytes(cfg, 1024, batch=3) == 0  # 363 rows > 256
     assert la.workspace_bytes(cfg, 1024, batch=0) == la.workspace_bytes(cfg, 1024, batch=1)
     assert la.workspace_bytes(cfg, 1024, batch=-1) == 0
+
+
+def _attn_splits(lib, H, W, N, G, ctx):
+    """Split count the bf16 attention launch provides, read back from its workspace size."""
+    T = 1 + (W + G) * (N - 1)
+    rows16 = (T + 15) // 16 * 16
+    nbytes = lib.la_attention_workspace_bytes(H, 128, ctx, W, N, G)
+    for s in range(1, 17):
+        rows = H * s * rows16
+        al = lambda x: (x + 255) // 256 * 256
+        if al(rows * 128 * 4) + al(rows * 8) == nbytes:
+            return s
+    raise AssertionError(nbytes)
+
+
+def test_attention_split_counts_without_gpu():
+    # Splits per (head, row group) for the longest context: about three 64-key chunks each
+    # (one or two up to 16 rows, at most 8), capped near one wave per SIMD (1024 waves) up
+    # to 128 rows and near 512 workgroups above; measured choices for the step shapes.
+    lib = la.lib()
+    assert _attn_splits(lib, 32, 15, 5, 15, 1152) == 4   # 7B step: 4 row groups x 2 waves
+    assert _attn_splits(lib, 40, 10, 5, 10, 1280) == 4   # 13B step: 3 row groups x 2 waves
+    assert _attn_splits(lib, 64, 7, 5, 7, 2240) == 4     # 34B step: one 64-row group x 4 waves
+    assert _attn_splits(lib, 32, 0, 5, 0, 4096) == 8     # one-token decode: up to 8
+    assert _attn_splits(lib, 32, 15, 5, 15, 256) == 2    # short context: ~3 chunks per split
+    assert _attn_splits(lib, 32, 25, 5, 25, 4096) == 16  # > 128 rows: 512-workgroup cap, max 16
