@@ -262,61 +262,67 @@ void launch_pool_insert(DevState*, int32_t key, const int32_t* tail_dev, int32_t
 constexpr int POOL_LDS_INTS = 6144;
 
 // Insert tail into the LDS list lst (len entries of n1 <= 31 tokens, oldest
-// first) with the one 64-lane wave of the workgroup; every lane returns the
-// new length.  Same result as pool_insert_serial: a tail already present is
-// moved to the newest end, else it is appended, the oldest entry dropped
-// when the list holds G.  Lanes compare 64 entries at a time (the lowest
-// match wins), then move entries gap+1 .. len-1 down by one, every lane
-// reading its source entry before any lane writes.
-__device__ inline int pool_insert_wave(int32_t* lst, int len, int n1, int G, const int32_t* tail) {
-  const int lane = threadIdx.x & 63;
-  int found = -1;
-  for (int e0 = 0; e0 < len && found < 0; e0 += 64) {
-    const int e = e0 + lane;
-    bool same = e < len;
-    for (int i = 0; i < n1; i++) same = same && lst[e * n1 + i] == tail[i];
-    const uint64_t m = __ballot(same);
-    if (m) found = e0 + __ffsll((unsigned long long)m) - 1;
-  }
+// first) with a group of GS lanes of one wave (GS >= G: lane e of the group
+// looks after entry e); returns the new length.  Same result as
+// pool_insert_serial: a tail already present is moved to the newest end,
+// else it is appended, the oldest entry dropped when the list holds G.  The
+// lowest matching entry wins; entries gap+1 .. len-1 then move down by one,
+// each lane reading its source entry before it writes (LDS operations of one
+// wave execute in program order, so every read of the move precedes every
+// write of it, and the group needs no barrier).
+template <int GS>
+__device__ inline int pool_insert_group(int32_t* lst, int len, int n1, int G, const int32_t* tail) {
+  const int lane = threadIdx.x & 63, e = lane & (GS - 1);
+  const int gbase = lane & ~(GS - 1);
+  bool same = e < len;
+  if (same)  // entries past the length are not read
+    for (int i = 0; i < n1; i++) same &= lst[e * n1 + i] == tail[i];
+  const uint64_t m = (__ballot(same) >> gbase) & (GS == 64 ? ~0ull : ((1ull << GS) - 1ull));
   int gap, nlen = len;
-  if (found >= 0) gap = found;
+  if (m) gap = __ffsll((unsigned long long)m) - 1;
   else if (len == G) gap = 0;
   else gap = nlen++;
-  for (int e0 = gap; e0 + 1 < nlen; e0 += 64) {
-    const int e = e0 + lane;
-    const bool mv = e + 1 < nlen;
-    int v[31];
+  // ints [(gap + 1) n1, nlen n1) move down by n1: all reads, then all writes
+  constexpr int MAXI = GS == 16 ? 16 : 31;  // G <= GS entries of n1 <= 16 (GS 16) or 31 ints
+  const int from = (gap + 1) * n1, end = nlen * n1;
+  int v[MAXI];
 #pragma unroll
-    for (int i = 0; i < 31; i++)
-      if (i < n1 && mv) v[i] = lst[(e + 1) * n1 + i];
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 31; i++)
-      if (i < n1 && mv) lst[e * n1 + i] = v[i];
-    __syncthreads();
+  for (int q = 0; q < MAXI; q++) {
+    const int idx = from + e + q * GS;
+    if (idx < end) v[q] = lst[idx];
   }
-  if (lane < n1) lst[(nlen - 1) * n1 + lane] = tail[lane];
-  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < MAXI; q++) {
+    const int idx = from + e + q * GS;
+    if (idx < end) lst[idx - n1] = v[q];
+  }
+  if (e < n1) lst[(nlen - 1) * n1 + e] = tail[e];
   return nlen;
 }
 
-// One workgroup per sequence of the batch (its rows, window, pool, result).
-__global__ __launch_bounds__(64) void k_verify(DevState* st, const int32_t* __restrict__ tokens,
-                                               const int32_t* __restrict__ amax, int32_t* win,
-                                               int32_t* pool_len, int32_t* pool, int V, int W,
-                                               int N, int G, DevResult* res) {
+// One workgroup of VER_T threads per sequence of the batch (its rows,
+// window, pool, result).
+constexpr int VER_T = 256;
+
+__global__ __launch_bounds__(VER_T) void k_verify(DevState* st, const int32_t* __restrict__ tokens,
+                                                  const int32_t* __restrict__ amax, int32_t* win,
+                                                  int32_t* pool_len, int32_t* pool, int V, int W,
+                                                  int N, int G, DevResult* res) {
   __shared__ int32_t ynew[256];
   __shared__ int32_t lwin[256];             // window, (N-1) x W <= 255
+  __shared__ int32_t ltail[256];            // column j's tail at j * (N-1) (staged inserts)
   __shared__ int32_t tail[32];
-  __shared__ int32_t lkey[256], lslot[256], llen[256];
+  __shared__ int32_t lkey[256], lslot[256], llen[256], lnext[256];
   __shared__ int32_t ltok[256], lamax[256];  // the block's tokens and row argmax
   __shared__ int32_t llist[POOL_LDS_INTS];
-  const int lane = threadIdx.x;
+  __shared__ int32_t best[2];
+  const int tid = threadIdx.x, lane = tid & 63;
   const int n1 = N - 1;
   const int nwin = n1 * W;
   const int T = 1 + (W + G) * n1;
   const int per = G * n1;  // ints per key list
-  const bool staged = G > 0 && W > 0 && W * per <= POOL_LDS_INTS;
+  // staged: the W lists fit in LDS and a group of at most 64 lanes covers a list
+  const bool staged = G > 0 && W > 0 && W * per <= POOL_LDS_INTS && G <= 64;
   {
     const int b = blockIdx.x;
     st += b;
@@ -328,54 +334,80 @@ __global__ __launch_bounds__(64) void k_verify(DevState* st, const int32_t* __re
     res += b;
   }
   // every global read that does not depend on another goes out first
-  for (int i = lane; i < T; i += 64) {
+  for (int i = tid; i < T; i += VER_T) {
     ltok[i] = tokens[i];
     lamax[i] = amax[i];
   }
-  for (int i = lane; i < nwin; i += 64) lwin[i] = win[i];
+  for (int i = tid; i < nwin; i += VER_T) lwin[i] = win[i];
   const int nc = st->n_cand;
   __syncthreads();
   const int a0 = lamax[0];
-  for (int j = lane; j < W; j += 64) ynew[j] = lamax[1 + (n1 - 1) * W + j];
-  // per-candidate accepted length, reduced to (max k, lowest g)
-  int bk = -1, bg = 0x7fffffff;
-  for (int g = lane; g < nc; g += 64) {
-    const int base = 1 + nwin + g * n1;  // row (g, 1)
-    int k = 0;
-    while (k < n1) {
-      const int pred = k == 0 ? a0 : lamax[base + k - 1];
-      if (ltok[base + k] != pred) break;
-      k++;
-    }
-    if (k > bk || (k == bk && g < bg)) { bk = k; bg = g; }
-  }
-  for (int o = 32; o > 0; o >>= 1) {
-    const int ok = __shfl_xor(bk, o), og = __shfl_xor(bg, o);
-    if (ok > bk || (ok == bk && og < bg)) { bk = ok; bg = og; }
-  }
-  __syncthreads();
+  for (int j = tid; j < W; j += VER_T) ynew[j] = lamax[1 + (n1 - 1) * W + j];
   if (staged) {
     // lists are read whole (entries past the length are never used), so
     // the lengths and the lists load together
-    for (int j = lane; j < W; j += 64) {
+    for (int j = tid; j < W; j += VER_T) {
       const int key = lwin[j];
       lkey[j] = key;
       llen[j] = pool_len[key];
     }
-    for (int idx = lane; idx < W * per; idx += 64) {
-      const int j = idx / per, rem = idx - j * per;
-      llist[idx] = pool[(size_t)lwin[j] * per + rem];
+    // every list load of the thread goes out before the first LDS store
+    constexpr int MAXL = POOL_LDS_INTS / VER_T;
+    int lv[MAXL];
+#pragma unroll
+    for (int q = 0; q < MAXL; q++) {
+      const int idx = tid + q * VER_T;
+      if (idx < W * per) {
+        const int j = idx / per;
+        lv[q] = pool[(size_t)lwin[j] * per + (idx - j * per)];
+      }
     }
-    __syncthreads();
-    for (int j = lane; j < W; j += 64) {
-      int sl = j;
-      for (int q = 0; q < j; q++)
-        if (lkey[q] == lkey[j]) { sl = q; break; }
-      lslot[j] = sl;
+#pragma unroll
+    for (int q = 0; q < MAXL; q++) {
+      const int idx = tid + q * VER_T;
+      if (idx < W * per) llist[idx] = lv[q];
     }
-    __syncthreads();
   }
-  if (lane == 0) {
+  if (tid < 64) {
+    // per-candidate accepted length, reduced to (max k, lowest g)
+    int bk = -1, bg = 0x7fffffff;
+    for (int g = lane; g < nc; g += 64) {
+      const int base = 1 + nwin + g * n1;  // row (g, 1)
+      int k = 0;
+      while (k < n1) {
+        const int pred = k == 0 ? a0 : lamax[base + k - 1];
+        if (ltok[base + k] != pred) break;
+        k++;
+      }
+      if (k > bk || (k == bk && g < bg)) { bk = k; bg = g; }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      const int ok = __shfl_xor(bk, o), og = __shfl_xor(bg, o);
+      if (ok > bk || (ok == bk && og < bg)) { bk = ok; bg = og; }
+    }
+    if (lane == 0) {
+      best[0] = bk;
+      best[1] = bg;
+    }
+  }
+  if (staged) {
+    for (int j = tid; j < W; j += VER_T) {  // first and next column with the same key
+      int sl = j, nx = W;
+      for (int q = 0; q < j; q++)
+        if (lwin[q] == lwin[j]) { sl = q; break; }
+      for (int q = W - 1; q > j; q--)
+        if (lwin[q] == lwin[j]) nx = q;
+      lslot[j] = sl;
+      lnext[j] = nx;
+    }
+    for (int i = tid; i < nwin; i += VER_T) {  // tail of column j: levels 2..N-1, then the new token
+      const int j = i / n1, l = i - j * n1;
+      ltail[i] = l + 1 < n1 ? lwin[(l + 1) * W + j] : lamax[1 + (n1 - 1) * W + j];
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int bk = best[0], bg = best[1];
     const int k = nc > 0 ? bk : 0;
     const int gs = nc > 0 ? bg : -1;
     const int base = 1 + nwin + (gs < 0 ? 0 : gs) * n1;
@@ -403,38 +435,46 @@ __global__ __launch_bounds__(64) void k_verify(DevState* st, const int32_t* __re
         pool_insert_serial(pool_len, pool, N, G, lwin[j], tail);
       }
   }
-  __syncthreads();
   if (staged) {
-    // staged lists: the same inserts, in column order, by the whole wave
-    for (int j = 0; j < W; j++) {
-      if (lane < n1 - 1) tail[lane] = lwin[(lane + 1) * W + j];
-      if (lane == n1 - 1) tail[lane] = ynew[j];
-      __syncthreads();
-      const int sl = lslot[j];
-      const int nl = pool_insert_wave(llist + sl * per, llen[sl], n1, G, tail);
-      if (lane == 0) llen[sl] = nl;
-      __syncthreads();
-    }
-  }
-  if (staged) {
-    for (int j = lane; j < W; j += 64)
+    // staged lists: the inserts of one key in column order by one lane
+    // group (key slot s by group s mod the group count), the groups side by
+    // side: each walks the columns with its own cursor, so the groups of a
+    // wave run their next inserts together (16-lane groups up to G = 16 and
+    // N - 1 = 16 tail tokens, whole waves up to 64)
+    auto inserts = [&](auto gsz) {
+      constexpr int GS = decltype(gsz)::value;
+      const int grp = tid / GS, ngrp = VER_T / GS;
+      for (int sl = grp; sl < W; sl += ngrp) {  // uniform over the group
+        if (lslot[sl] != sl) continue;  // not the first column of its key
+        int len = llen[sl];
+        for (int j = sl; j < W; j = lnext[j])
+          len = pool_insert_group<GS>(llist + sl * per, len, n1, G, ltail + j * n1);
+        if ((tid & (GS - 1)) == 0) llen[sl] = len;
+      }
+    };
+    if (G <= 16 && n1 <= 16)
+      inserts(std::integral_constant<int, 16>{});
+    else
+      inserts(std::integral_constant<int, 64>{});
+    __syncthreads();
+    for (int j = tid; j < W; j += VER_T)
       if (lslot[j] == j) pool_len[lkey[j]] = llen[j];
-    for (int idx = lane; idx < W * per; idx += 64) {
+    for (int idx = tid; idx < W * per; idx += VER_T) {
       const int j = idx / per, rem = idx - j * per;
       if (lslot[j] == j && rem < llen[j] * n1) pool[(size_t)lkey[j] * per + rem] = llist[idx];
     }
   }
-  // shift the window by one level
-  for (int j = lane; j < W; j += 64) {
-    for (int l = 1; l < n1; l++) win[(l - 1) * W + j] = lwin[l * W + j];
-    win[(n1 - 1) * W + j] = ynew[j];
+  // shift the window by one level (lwin holds the old levels)
+  for (int i = tid; i < nwin; i += VER_T) {
+    const int l = i / W, j = i - l * W;
+    win[i] = l + 1 < n1 ? lwin[(l + 1) * W + j] : ynew[j];
   }
 }
 
 void launch_verify(DevState* st, const int32_t* tokens, const int32_t* amax, int32_t* win,
                    int32_t* pool_len, int32_t* pool, int nseq, int V, int W, int N, int G,
                    DevResult* res, hipStream_t s) {
-  hipLaunchKernelGGL(k_verify, dim3(nseq), dim3(64), 0, s, st, tokens, amax, win, pool_len, pool,
+  hipLaunchKernelGGL(k_verify, dim3(nseq), dim3(VER_T), 0, s, st, tokens, amax, win, pool_len, pool,
                      V, W, N, G, res);
 }
 
