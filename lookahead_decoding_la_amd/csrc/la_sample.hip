@@ -38,11 +38,17 @@ constexpr int SEL_T = 1024;  // threads per row
 constexpr int SEL_PER = SAMPLE_MAX_VOCAB / SEL_T;
 constexpr int SEL_WAVES = SEL_T / 64;
 
+constexpr int SEL_KEPT = 64;  // top-k up to this: top-p and the draw on the kept tokens
+
 struct SelShared {
   float f[2][SEL_WAVES];  // double-buffered: one barrier per block sum
   uint32_t n[2][SEL_WAVES];
   int32_t i[SEL_WAVES];
   int32_t tok;
+  uint32_t cnt;                // kept tokens appended
+  uint32_t kkey[SEL_KEPT];     // their order keys, ids and weights (append order)
+  int32_t kid[SEL_KEPT];
+  float kw[SEL_KEPT];
 };
 
 // Philox4x32-10: word 0 of the output block.
@@ -266,6 +272,71 @@ __device__ inline void cut_after(uint32_t (&k)[SEL_PER], const KeyTok& kt) {
   }
 }
 
+// Top-p and the draw over at most SEL_KEPT kept tokens (the rest out of
+// play), by wave 0: the kept tokens are gathered in LDS, sorted into the
+// draw order (key descending, id ascending: a total order, so the result
+// does not depend on the gather order), and their weights summed in that
+// order; the same selections as select_token on the same weights, with the
+// running totals summed token by token in the draw order.
+__device__ int draw_kept(const uint32_t (&k)[SEL_PER], const float (&w)[SEL_PER], float top_p,
+                         float u, SelShared& sh) {
+  const int tid = threadIdx.x;
+  if (tid == 0) sh.cnt = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < SEL_PER; e++)
+    if (k[e] != 0u) {
+      const uint32_t at = atomicAdd(&sh.cnt, 1u);
+      if (at < SEL_KEPT) {  // the count-exact top-k cut keeps exactly top_k <= SEL_KEPT
+        sh.kkey[at] = k[e];
+        sh.kid[at] = tid + e * SEL_T;
+        sh.kw[at] = w[e];
+      }
+    }
+  __syncthreads();
+  if (tid < 64) {
+    const uint32_t n = min(sh.cnt, (uint32_t)SEL_KEPT);
+    uint32_t key = tid < (int)n ? sh.kkey[tid] : 0u;  // padding sorts last
+    int id = tid < (int)n ? sh.kid[tid] : 0x7fffffff;
+    float wt = tid < (int)n ? sh.kw[tid] : 0.f;
+    // bitonic sort over the wave into the draw order
+    for (int kk = 2; kk <= 64; kk <<= 1)
+      for (int j = kk >> 1; j > 0; j >>= 1) {
+        const uint32_t pkey = (uint32_t)__shfl_xor((int)key, j);
+        const int pid = __shfl_xor(id, j);
+        const float pw = __shfl_xor(wt, j);
+        const bool self_first = key > pkey || (key == pkey && id < pid);
+        const bool lower = (tid & j) == 0, up = (tid & kk) == 0;
+        if (self_first != (lower == up)) {
+          key = pkey;
+          id = pid;
+          wt = pw;
+        }
+      }
+    // running totals in the draw order, token by token
+    float run = 0.f, mine = 0.f;
+    for (int q = 0; q < 64; q++) {
+      run += __shfl(wt, q);
+      if (q == tid) mine = run;
+    }
+    const float total = __shfl(mine, (int)n - 1);
+    int last = (int)n - 1;  // last kept token
+    if (top_p < 1.f) {
+      const uint64_t m = __ballot(tid < (int)n && mine >= top_p * total);
+      if (m) last = __ffsll((unsigned long long)m) - 1;
+    }
+    const float kept = __shfl(mine, last);
+    const uint64_t m = __ballot(tid <= last && mine > u * kept);
+    const int at = m ? __ffsll((unsigned long long)m) - 1 : last;
+    const int tok = __shfl(id, at);
+    if (tid == 0) sh.tok = tok;
+  }
+  __syncthreads();
+  const int tok = sh.tok;
+  __syncthreads();
+  return tok;
+}
+
 // One row's draw; z holds the thread's logits (tokens past V unused).
 __device__ int draw_row(const float (&z)[SEL_PER], int V, const SampleParams& p, float u,
                         SelShared& sh) {
@@ -281,8 +352,10 @@ __device__ int draw_row(const float (&z)[SEL_PER], int V, const SampleParams& p,
     w[e] = j < V ? expf((z[e] - zmax) * invT) : 0.f;
   }
   int buf = 0;
-  if (p.top_k > 0 && p.top_k < V)
+  if (p.top_k > 0 && p.top_k < V) {
     cut_after(k, select_token<false>(k, w, (uint32_t)p.top_k, 0.f, false, sh, buf));
+    if (p.top_k <= SEL_KEPT) return draw_kept(k, w, p.top_p, u, sh);
+  }
   auto total = [&]() {
     float s = 0.f;
 #pragma unroll

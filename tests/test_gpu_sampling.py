@@ -29,7 +29,9 @@ from lockstep import BatchLockstep, Lockstep, draw_tol, log
 pytestmark = pytest.mark.gpu
 
 PARAMS = [(1.0, 0, 1.0, 7), (0.7, 0, 0.9, 8), (1.3, 40, 1.0, 9), (0.5, 5, 0.8, 10),
-          (2.0, 0, 0.5, 11)]
+          (2.0, 0, 0.5, 11),
+          (1.0, 64, 0.7, 12),   # largest top-k drawn from the sorted kept tokens
+          (0.9, 65, 0.95, 13)]  # smallest top-k on the whole-vocabulary searches
 
 
 @pytest.mark.parametrize("T,k,p,seed", PARAMS)
