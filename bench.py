@@ -452,7 +452,7 @@ def main():
         print(json.dumps(out), flush=True)
         return
     n_prof, n_samp = 3, 16
-    total = args.warmup + args.steps + n_prof + n_samp
+    total = args.warmup + args.steps + min(16, args.steps) + n_prof + n_samp
     max_ctx = cfg.prompt_len + (total + 2) * cfg.N + cfg.T + 64
     dec = la.LookaheadDecoder(cfg, dev_w, max_ctx)
     first = dec.prefill(prompt, win)
@@ -466,21 +466,36 @@ def main():
     emitted = 0
     roof_s = 0.0
     wb, kvb = streamed_weight_bytes(cfg), kv_bytes_per_token(cfg)
+    # Pipelined stepping (la_step_submit / la_step_collect): step k+1 is
+    # enqueued before step k's result is read, so the GPU does not idle while
+    # the host takes a result; per-step times are the intervals between
+    # collects.
     t_start = time.perf_counter()
     L = L0
-    for _ in range(args.steps):
-        a = time.perf_counter()
-        r = dec.step()
-        per.append(time.perf_counter() - a)
+    a = t_start
+    dec.step_submit()
+    for i in range(args.steps):
+        if i + 1 < args.steps:
+            dec.step_submit()
+        r = dec.step_collect()
+        b = time.perf_counter()
+        per.append(b - a)
+        a = b
         emitted += r["n_emitted"]
         roof_s += (wb + L * kvb + r["n_emitted"] * kvb) / (HBM_PEAK_GBS * 1e9)
         L = r["kv_len"]
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
+    # the same loop with the blocking call (la_step: launch, wait, read)
+    nb = min(16, args.steps)
+    tb = time.perf_counter()
+    for _ in range(nb):
+        dec.step()
+    blocking_ms = (time.perf_counter() - tb) / nb * 1e3
     ms_step = elapsed / args.steps * 1e3
     tok_s = emitted / elapsed
     log(f"{args.steps} steps: {ms_step:.3f} ms/step, {emitted / args.steps:.2f} tokens/step, "
-        f"{tok_s:.1f} tokens/s")
+        f"{tok_s:.1f} tokens/s (pipelined); blocking la_step {blocking_ms:.3f} ms/step")
 
     # per-kernel timing (HIP events around every launch, on the launch stream)
     prof = {}
@@ -568,6 +583,7 @@ def main():
         "sampled_step_ms": {"ms_per_step": round(samp_ms, 4), "temperature": 0.8,
                             "top_k": 50, "top_p": 0.95},
         "step_ms_p10_p50_p90": [round(float(np.percentile(per_ms, q)), 4) for q in (10, 50, 90)],
+        "blocking_step_ms": round(blocking_ms, 4),
         "step_hbm_roofline": {"t_roof_ms": round(roof_s / args.steps * 1e3, 4),
                               "frac": round(roof_s / elapsed, 4),
                               "bytes": "streamed weights + KV prefix + committed KV rows, at 8 TB/s"},

@@ -134,6 +134,23 @@ la_status la_prefill_seq(la_ctx *c, int32_t seq, const int32_t *prompt, int32_t 
  * sequence steps), LA_ERR_INVALID_ARG (out NULL), LA_ERR_HIP. */
 la_status la_step(la_ctx *c, la_step_result *out);
 
+/* Pipelined stepping, for a serving loop that should keep the GPU busy
+ * while it reads results: la_step_submit enqueues the next step of every
+ * sequence on the context's stream and returns at once; la_step_collect
+ * blocks until the oldest submitted step has finished and writes its
+ * results (host la_step_result [batch]), exactly those la_step would have
+ * returned for it.  A step only needs the device state the step before it
+ * left, so submitting step k+1 before collecting step k is allowed; at most
+ * two steps may be in flight.  While any is in flight every other call on
+ * the context but la_destroy returns LA_ERR_STATE.  The capacity check of
+ * a submit assumes each step in flight commits its maximum of N tokens.
+ * Errors: la_step_submit: LA_ERR_STATE (two in flight, a sequence not
+ * prefilled, poisoned), LA_ERR_OUT_OF_CAPACITY, LA_ERR_HIP;
+ * la_step_collect: LA_ERR_STATE (none in flight, poisoned),
+ * LA_ERR_INVALID_ARG (out NULL), LA_ERR_HIP. */
+la_status la_step_submit(la_ctx *c);
+la_status la_step_collect(la_ctx *c, la_step_result *out);
+
 /* Seed the n-gram pool with every N-gram of a token sequence (host int32
  * [n], ids < vocab), in position order: key seq[p], tail seq[p+1 .. p+N-1]
  * for p = 0 .. n-N, each inserted with the pool's policy (distinct tails per

@@ -24,7 +24,8 @@ LA_ERR_OUT_OF_CAPACITY, LA_ERR_HIP, LA_ERR_UNSUPPORTED = -3, -4, -5
 LA_F32, LA_BF16 = 0, 1
 
 EXPORTS = [
-    "la_workspace_bytes", "la_create", "la_prefill", "la_step", "la_destroy",
+    "la_workspace_bytes", "la_create", "la_prefill", "la_step", "la_step_submit",
+    "la_step_collect", "la_destroy",
     "la_status_string", "la_last_error", "la_step_rows", "la_debug_logits",
     "la_debug_block", "la_debug_window", "la_debug_pool",
     "la_debug_pool_insert", "la_debug_kv", "la_debug_state",
@@ -78,6 +79,8 @@ def lib():
                                     C.POINTER(C.c_void_p)]),
             "la_prefill": (C.c_int, [P, pi, I32, pi, pi]),
             "la_step": (C.c_int, [P, C.POINTER(LaStepResult)]),
+            "la_step_submit": (C.c_int, [P]),
+            "la_step_collect": (C.c_int, [P, C.POINTER(LaStepResult)]),
             "la_destroy": (C.c_int, [P]),
             "la_status_string": (C.c_char_p, [C.c_int]),
             "la_last_error": (C.c_char_p, [P]),
@@ -218,6 +221,16 @@ class LookaheadDecoder:
     def step(self):
         r = (LaStepResult * self.B)()
         self._check(lib().la_step(self._h, r), "la_step")
+        return self._squeeze([_result(x) for x in r])
+
+    def step_submit(self) -> None:
+        """Enqueue the next step without waiting (at most two in flight)."""
+        self._check(lib().la_step_submit(self._h), "la_step_submit")
+
+    def step_collect(self):
+        """Wait for the oldest submitted step; its results, as step() returns them."""
+        r = (LaStepResult * self.B)()
+        self._check(lib().la_step_collect(self._h, r), "la_step_collect")
         return self._squeeze([_result(x) for x in r])
 
     def profile_step(self):

@@ -105,11 +105,18 @@ struct la_ctx {
   GemmPlan p_qkv{1, 1}, p_o{1, 1}, p_gu{1, 1}, p_d{1, 1}, p_lm{1, 1};
   int attn_splits = 1;
   // host
-  DevResult* res_host = nullptr;  // pinned [B]
+  DevResult* res_host = nullptr;  // pinned [B]: where the step's result copy lands
+  // pipelined stepping: two pinned result slots, one captured step per slot
+  // (the slot's copy baked into its graph), an event per slot
+  DevResult* res_slot[2] = {nullptr, nullptr};
+  hipGraphExec_t gexec_slot1 = nullptr;
+  hipGraph_t graph_slot1 = nullptr;
+  hipEvent_t slot_ev[2] = {nullptr, nullptr};
+  int inflight = 0, next_slot = 0, oldest_slot = 0;
   int32_t* pin = nullptr;         // pinned staging
   size_t pin_count = 0;
   hipGraph_t graph = nullptr;
-  hipGraphExec_t gexec = nullptr;
+  hipGraphExec_t gexec = nullptr;  // result copy into res_slot[0]
   std::vector<hipEvent_t> events;  // profiling only
 };
 
@@ -456,9 +463,17 @@ void enqueue_step(la_ctx* c, hipStream_t s, Prof* pf = nullptr) {
 #undef P_BEGIN
 #undef P_END
 
-la_status check_usable(la_ctx* c) {
+la_status check_alive(la_ctx* c) {
   if (!c) return LA_ERR_INVALID_ARG;
   if (c->poisoned) return fail(c, LA_ERR_STATE, "context poisoned by an earlier HIP failure: " + c->err);
+  return LA_OK;
+}
+
+// Usable for every call but the pipelined pair: alive, no step in flight.
+la_status check_usable(la_ctx* c) {
+  const la_status us = check_alive(c);
+  if (us != LA_OK) return us;
+  if (c->inflight) return fail(c, LA_ERR_STATE, "steps submitted and not collected");
   return LA_OK;
 }
 
@@ -536,6 +551,10 @@ la_status la_create(const la_config* cfg, const void* const* weights, void* work
   // pinned host buffers
   c->pin_count = std::max<size_t>(c->MR, (size_t)std::max(1, (g.N - 1) * g.W)) + 64;
   LA_HIP(c, hipHostMalloc((void**)&c->res_host, sizeof(DevResult) * c->B, hipHostMallocDefault));
+  LA_HIP(c, hipHostMalloc((void**)&c->res_slot[1], sizeof(DevResult) * c->B, hipHostMallocDefault));
+  c->res_slot[0] = c->res_host;
+  memset(c->res_slot[1], 0, sizeof(DevResult) * c->B);
+  for (int i = 0; i < 2; i++) LA_HIP(c, hipEventCreateWithFlags(&c->slot_ev[i], hipEventDisableTiming));
   LA_HIP(c, hipHostMalloc((void**)&c->pin, c->pin_count * sizeof(int32_t), hipHostMallocDefault));
   memset(c->res_host, 0, sizeof(DevResult) * c->B);
   c->kv_len_host.assign(c->B, 0);
@@ -603,6 +622,17 @@ la_status la_create(const la_config* cfg, const void* const* weights, void* work
       e = hipStreamEndCapture(cs, &c->graph);
     }
     if (e == hipSuccess) e = hipGraphInstantiate(&c->gexec, c->graph, nullptr, nullptr, 0);
+    // the same step with its result copy into slot 1 (pipelined stepping)
+    if (e == hipSuccess) {
+      c->res_host = c->res_slot[1];
+      e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+      if (e == hipSuccess) {
+        enqueue_step(c, cs);
+        e = hipStreamEndCapture(cs, &c->graph_slot1);
+      }
+      c->res_host = c->res_slot[0];
+    }
+    if (e == hipSuccess) e = hipGraphInstantiate(&c->gexec_slot1, c->graph_slot1, nullptr, nullptr, 0);
     (void)hipStreamDestroy(cs);
     if (e != hipSuccess) return fail(c, LA_ERR_HIP, std::string("step graph capture: ") + hipGetErrorString(e));
   }
@@ -678,6 +708,45 @@ la_status la_step(la_ctx* c, la_step_result* out) {
   }
   LA_HIP(c, hipStreamSynchronize(c->stream));
   take_results(c, out);
+  return LA_OK;
+}
+
+la_status la_step_submit(la_ctx* c) {
+  la_status us = check_alive(c);
+  if (us != LA_OK) return us;
+  if (c->inflight == 2) return fail(c, LA_ERR_STATE, "two steps in flight: collect one first");
+  for (int b = 0; b < c->B; b++)
+    if (!c->prefilled[b]) return fail(c, LA_ERR_STATE, "la_step_submit before every sequence was prefilled");
+  // a step commits at most N tokens; steps in flight have not reported theirs
+  for (int b = 0; b < c->B; b++)
+    if ((long)c->kv_len_host[b] + (long)c->inflight * c->cfg.N + c->T > c->cfg.max_ctx)
+      return fail(c, LA_ERR_OUT_OF_CAPACITY, "kv_len + steps in flight + step rows exceed max_ctx");
+  const int slot = c->next_slot;
+  if (c->use_graph) {
+    LA_HIP(c, hipGraphLaunch(slot ? c->gexec_slot1 : c->gexec, c->stream));
+  } else {
+    c->res_host = c->res_slot[slot];
+    enqueue_step(c, c->stream);
+    c->res_host = c->res_slot[0];
+    LA_HIP(c, hipGetLastError());
+  }
+  LA_HIP(c, hipEventRecord(c->slot_ev[slot], c->stream));
+  c->next_slot ^= 1;
+  c->inflight++;
+  return LA_OK;
+}
+
+la_status la_step_collect(la_ctx* c, la_step_result* out) {
+  la_status us = check_alive(c);
+  if (us != LA_OK) return us;
+  if (!out) return fail(c, LA_ERR_INVALID_ARG, "out is NULL");
+  if (!c->inflight) return fail(c, LA_ERR_STATE, "no step in flight");
+  const int slot = c->oldest_slot;
+  LA_HIP(c, hipEventSynchronize(c->slot_ev[slot]));
+  memcpy(out, c->res_slot[slot], sizeof(*out) * c->B);
+  for (int b = 0; b < c->B; b++) c->kv_len_host[b] = out[b].kv_len;
+  c->oldest_slot ^= 1;
+  c->inflight--;
   return LA_OK;
 }
 
@@ -791,6 +860,11 @@ la_status la_destroy(la_ctx* c) {
   (void)hipStreamSynchronize(c->stream);
   if (c->gexec) (void)hipGraphExecDestroy(c->gexec);
   if (c->graph) (void)hipGraphDestroy(c->graph);
+  if (c->gexec_slot1) (void)hipGraphExecDestroy(c->gexec_slot1);
+  if (c->graph_slot1) (void)hipGraphDestroy(c->graph_slot1);
+  for (hipEvent_t e : c->slot_ev)
+    if (e) (void)hipEventDestroy(e);
+  if (c->res_slot[1]) (void)hipHostFree(c->res_slot[1]);
   for (hipEvent_t e : c->events) (void)hipEventDestroy(e);
   if (c->res_host) (void)hipHostFree(c->res_host);
   if (c->pin) (void)hipHostFree(c->pin);

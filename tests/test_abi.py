@@ -74,6 +74,8 @@ def test_calls_on_null_context():
     assert lib.la_seed_pool(None, toks, 4) == la.LA_ERR_INVALID_ARG
     us = C.c_float()
     assert lib.la_profile_kernel(None, 3, 8, C.byref(us)) == la.LA_ERR_INVALID_ARG
+    assert lib.la_step_submit(None) == la.LA_ERR_INVALID_ARG
+    assert lib.la_step_collect(None, C.byref(r)) == la.LA_ERR_INVALID_ARG
 
 
 def test_attention_argument_checks_without_gpu():
