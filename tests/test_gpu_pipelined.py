@@ -65,3 +65,28 @@ def test_pipelined_state_errors():
     d.step_collect()
     d.step_collect()
     d.step()
+
+
+def test_pipelined_batch_equals_step():
+    # two sequences per forward pass, each with its own prompt: every collected
+    # result list (one result per sequence) equals la_step's
+    cfg = lasynth.get_config("tiny")
+    dev_w = la.upload_weights(lasynth.make_weights(cfg))
+    p0 = lasynth.make_prompt(cfg)
+    p1 = lasynth.make_prompt(cfg, seed=1)
+
+    def make():
+        d = la.LookaheadDecoder(cfg, dev_w, 512, batch=2)
+        for s, p in enumerate((p0, p1)):
+            d.prefill(p, lasynth.make_init_window(cfg, p), seq=s)
+        return d
+
+    ref, pipe = make(), make()
+    want = [ref.step() for _ in range(8)]
+    got = []
+    pipe.step_submit()
+    for i in range(8):
+        if i + 1 < 8:
+            pipe.step_submit()
+        got.append(pipe.step_collect())
+    assert got == want
