@@ -531,8 +531,11 @@ def main():
     dec.set_sampling(0.8, 50, 0.95, 1)
     torch.cuda.synchronize()
     a = time.perf_counter()
-    for _ in range(n_samp):
-        dec.step()
+    dec.step_submit()  # pipelined, like the greedy loop
+    for i in range(n_samp):
+        if i + 1 < n_samp:
+            dec.step_submit()
+        dec.step_collect()
     torch.cuda.synchronize()
     samp_ms = (time.perf_counter() - a) / n_samp * 1e3
     log(f"sampled step (T 0.8, top-k 50, top-p 0.95): {samp_ms:.3f} ms/step")
@@ -547,8 +550,11 @@ def main():
             d0.step()
         torch.cuda.synchronize()
         a = time.perf_counter()
-        for _ in range(args.steps):
-            d0.step()
+        d0.step_submit()  # driven like the lookahead loop: pipelined
+        for i in range(args.steps):
+            if i + 1 < args.steps:
+                d0.step_submit()
+            d0.step_collect()
         torch.cuda.synchronize()
         plain = (time.perf_counter() - a) / args.steps * 1e3
         d0.close()
