@@ -246,7 +246,7 @@ void launch_pool_insert(DevState*, int32_t key, const int32_t* tail_dev, int32_t
 }
 
 // ---------------------------------------------------------------------------
-// Greedy verification + lookahead update (one wave).
+// Greedy verification + lookahead update (one 4-wave workgroup per sequence).
 //   k_g = longest prefix of candidate g that follows the greedy chain:
 //     cand[g][0] == argmax(row 0), cand[g][i] == argmax(row (g, i));
 //   winner g* = lowest g with the largest k_g (k = 0 and g* = -1 without
