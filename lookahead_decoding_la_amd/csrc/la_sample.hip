@@ -137,6 +137,21 @@ __device__ inline Pair block_pair(float s, uint32_t n, SelShared& sh, int& buf) 
   return p;
 }
 
+// Count only (the count-based selections carry no weights).
+__device__ inline uint32_t block_count(uint32_t n, SelShared& sh, int& buf) {
+  n = wave_sum_u(n);
+  if ((threadIdx.x & 63) == 0) sh.n[buf][threadIdx.x >> 6] = n;
+  __syncthreads();
+  uint32_t t = 0u;
+  for (int q = 0; q < SEL_WAVES; q++) t += sh.n[buf][q];
+  buf ^= 1;
+  return t;
+}
+__device__ inline Pair block_total(bool weighted, float s, uint32_t n, SelShared& sh, int& buf) {
+  if (weighted) return block_pair(s, n, sh, buf);
+  return Pair{0.f, block_count(n, sh, buf)};
+}
+
 // Largest logit, lowest id on ties, over the block.
 __device__ inline int block_argmax(const float (&z)[SEL_PER], int V, float* vmax, SelShared& sh) {
   float bv = -INFINITY;
@@ -202,7 +217,7 @@ __device__ KeyTok select_token(const uint32_t (&k)[SEL_PER], const float (&w)[SE
       if (WEIGHTED) s += k[e] >= c ? w[e] : 0.f;
       else n += k[e] >= c ? 1u : 0u;
     }
-    return block_pair(s, n, sh, buf);
+    return block_total(WEIGHTED, s, n, sh, buf);
   };
   // the largest key t whose running total meets the target
   uint32_t t = 0u;
@@ -215,7 +230,7 @@ __device__ KeyTok select_token(const uint32_t (&k)[SEL_PER], const float (&w)[SE
   uint32_t ne = 0u;
 #pragma unroll
   for (int e = 0; e < SEL_PER; e++) ne += (t != 0u && k[e] == t) ? 1u : 0u;
-  const uint32_t neq = block_pair(0.f, ne, sh, buf).n;
+  const uint32_t neq = block_count(ne, sh, buf);
   if (neq <= 1u) {
     // one token at t; or none (rounding): the last token in play, i.e. the
     // smallest key, highest id among equals
@@ -257,7 +272,7 @@ __device__ KeyTok select_token(const uint32_t (&k)[SEL_PER], const float (&w)[SE
       s += in ? w[e] : 0.f;
       n += in ? 1u : 0u;
     }
-    const Pair p = block_pair(s, n, sh, buf);
+    const Pair p = block_total(WEIGHTED, s, n, sh, buf);
     if (!meets(above.s + p.s, above.n + p.n)) J += 1 << bit;
   }
   return KeyTok{t, J};
