@@ -269,3 +269,147 @@ def test_prompt_seeded_pool_keeps_greedy_output(tiny):
     toks, steps = oracle.Oracle(cfg, w, 256).generate(p, win, M, seed_prompt=True)
     assert toks == ref
     assert all(1 <= s["n_emitted"] <= cfg.N for s in steps)
+
+
+def _plant(o, cfg, tails):
+    for t in tails:
+        o.pool_insert(o.current, np.asarray(t, np.int32))
+
+
+def test_argmax_equals_numpy_argmax_of_fp32_logits(tiny):
+    """Every valid row's decision in a greedy step is numpy.argmax of that
+    row's logits rounded to fp32 (numpy returns the first, i.e. lowest-id,
+    maximum); invalid candidate slots carry -1."""
+    cfg, w, p, win = tiny
+    o = oracle.Oracle(cfg, w, 256)
+    o.prefill(p, win)
+    rng = np.random.default_rng(3)
+    seen_invalid = False
+    for step in range(4):
+        _plant(o, cfg, [rng.integers(0, cfg.vocab, cfg.N - 1) for _ in range(step % 3)])
+        tok, valid, nc = o.block_tokens()
+        lg = o.forward_block(tok, valid, keep=True)
+        amax = o.block_argmax()
+        for r in range(cfg.T):
+            if valid[r]:
+                assert amax[r] == int(np.argmax(lg[r].astype(np.float32))), (step, r)
+            else:
+                seen_invalid = True
+                assert amax[r] == -1
+        o.commit()
+    assert seen_invalid
+
+
+def test_argmax_ties_take_the_lowest_token_id(tiny):
+    """Exact ties built into the weights: an LM head whose rows are all zero
+    except three identical rows (ids 5, 17, 300).  Every row's logits are
+    then exactly 0 except three bit-identical values z; the decision must be
+    5 where z > 0 and 0 (the lowest id among the zeros) where z <= 0.  A
+    highest-id rule, or a reversed comparison, fails here."""
+    cfg, w, p, win = tiny
+    w2 = [x.copy() for x in w]
+    lm = w2[2]
+    assert lm.shape == (cfg.vocab, cfg.d_model)
+    lm[:] = 0
+    row = np.random.default_rng(11).normal(0.0, 0.5, cfg.d_model).astype(lm.dtype)
+    for t in (5, 17, 300):
+        lm[t] = row
+    o = oracle.Oracle(cfg, w2, 256)
+    first, lgp = o.prefill(p, win, logits=True)
+    z = lgp[-1][5]
+    assert lgp[-1][17] == z and lgp[-1][300] == z
+    assert first == (5 if np.float32(z) > 0 else 0)
+    signs = set()
+    for _ in range(3):
+        _plant(o, cfg, [[5] * (cfg.N - 1), [0] * (cfg.N - 1)])
+        tok, valid, nc = o.block_tokens()
+        lg = o.forward_block(tok, valid, keep=True)
+        amax = o.block_argmax()
+        for r in np.nonzero(valid)[0]:
+            zr = lg[r][5]
+            others = np.delete(lg[r], [5, 17, 300])
+            assert np.all(others == 0.0) and lg[r][17] == zr and lg[r][300] == zr
+            want = 5 if np.float32(zr) > 0 else 0
+            signs.add(want)
+            assert amax[r] == want, (r, zr)
+        o.commit()
+    assert signs, "no valid rows"
+
+
+def _verify_case(tiny, tails, decide):
+    """Plant `tails` under the current token, forward the block, then commit
+    with the decisions `decide(row_of_candidate, amax)` fixes on top of the
+    oracle's own argmax; returns (result, block tokens)."""
+    cfg, w, p, win = tiny
+    o = oracle.Oracle(cfg, w, 256)
+    o.prefill(p, win)
+    _plant(o, cfg, tails)
+    tok, valid, nc = o.block_tokens()
+    assert nc == len(tails)
+    o.forward_block(tok, valid, keep=True)
+    amax = o.block_argmax()
+    n1, W = cfg.N - 1, cfg.W
+
+    def cand_row(g, i):  # row of candidate g's token i (1-based)
+        return 1 + n1 * W + g * n1 + (i - 1)
+
+    decide(cand_row, amax)
+    return o.commit(amax), tok
+
+
+def test_winner_is_lowest_index_among_equal_accepted_lengths(tiny):
+    """Hand-worked verification (N = 3, two candidate tokens each):
+    candidates (a, b) and (a, c) both accept k = 2 when row 0 decides a and
+    both candidates' first rows decide their second tokens; the winner is
+    candidate 0, and the bonus token is the decision of candidate 0's last
+    row."""
+    cfg = tiny[0]
+    assert cfg.N == 3 and cfg.G >= 3
+    a, b, c = 7, 8, 9
+
+    def decide(row, amax):
+        amax[0] = a
+        amax[row(0, 1)] = b   # cand 0: a, b -> k = 2
+        amax[row(1, 1)] = c   # cand 1: a, c -> k = 2
+        amax[row(0, 2)] = 41  # bonus of cand 0
+        amax[row(1, 2)] = 42  # bonus of cand 1
+    res, _ = _verify_case(tiny, [[a, b], [a, c]], decide)
+    assert res["accepted"] == 2 and res["winner"] == 0
+    assert res["tokens"] == [a, b, 41] and res["n_emitted"] == 3
+
+
+def test_winner_is_the_longest_accepted_prefix(tiny):
+    """A later candidate with a longer accepted prefix wins: (a, x) accepts
+    1, (a, b) accepts 2 -> winner 1, emits a, b and candidate 1's bonus."""
+    a, b, x = 7, 8, 9
+
+    def decide(row, amax):
+        amax[0] = a
+        amax[row(0, 1)] = b   # cand 0 is (a, x): stops after a
+        amax[row(1, 1)] = b   # cand 1 is (a, b): accepts both
+        amax[row(0, 2)] = 50
+        amax[row(1, 2)] = 51
+    res, _ = _verify_case(tiny, [[a, x], [a, b]], decide)
+    assert res["accepted"] == 2 and res["winner"] == 1
+    assert res["tokens"] == [a, b, 51]
+
+
+def test_winner_with_nothing_accepted_is_candidate_zero(tiny):
+    """No candidate's first token equals row 0's decision: k = 0, the winner
+    is candidate 0 (candidates were present), one token is emitted (row 0's
+    decision); with three candidates of k = 1, 1, 0 the winner is 0."""
+    a = 7
+
+    def none(row, amax):
+        amax[0] = a
+    res, _ = _verify_case(tiny, [[1, 2], [3, 4], [5, 6]], none)
+    assert res["accepted"] == 0 and res["winner"] == 0
+    assert res["tokens"] == [a] and res["n_candidates"] == 3
+
+    def ones(row, amax):
+        amax[0] = a
+        amax[row(0, 1)] = 99  # cand 0 (a, 2): k = 1
+        amax[row(1, 1)] = 98  # cand 1 (a, 4): k = 1
+    res, _ = _verify_case(tiny, [[a, 2], [a, 4], [5, 6]], ones)
+    assert res["accepted"] == 1 and res["winner"] == 0
+    assert res["tokens"] == [a, 99]
