@@ -43,7 +43,7 @@ class _Cfg(C.Structure):
                 ("vocab", C.c_int32), ("rope_theta", C.c_double),
                 ("rms_eps", C.c_double), ("W", C.c_int32), ("N", C.c_int32),
                 ("G", C.c_int32), ("max_ctx", C.c_int32),
-                ("wdtype", C.c_int32)]
+                ("wdtype", C.c_int32), ("act_bf16", C.c_int32)]
 
 
 class _Res(C.Structure):
@@ -92,6 +92,7 @@ def lib():
             "orc_sample_logits": (I, [D, I, C.c_double, I, C.c_double, C.c_double, D]),
             "orc_block_select": (I, [P, I32, D]),
             "orc_set_sampling": (I, [P, C.c_double, I, C.c_double, C.c_uint64]),
+            "orc_round_bf16": (C.c_double, [C.c_double]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -110,12 +111,19 @@ def _f64p(a):
     return a.ctypes.data_as(C.POINTER(C.c_double))
 
 
-def make_cfg(cfg, max_ctx: int = 0) -> _Cfg:
-    """C config from a lasynth.ModelConfig-like object."""
+STORAGES = ("exact", "bf16")
+
+
+def make_cfg(cfg, max_ctx: int = 0, storage: str = "exact") -> _Cfg:
+    """C config from a lasynth.ModelConfig-like object.  storage: "exact"
+    (no activation is rounded) or "bf16" (the seven stored activations of a
+    bf16 datapath are rounded to bfloat16; see the C source header)."""
+    if storage not in STORAGES:
+        raise ValueError(f"storage must be one of {STORAGES}")
     return _Cfg(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.n_kv_heads,
                 cfg.head_dim, cfg.d_ffn, cfg.vocab, cfg.rope_theta,
                 cfg.rms_eps, cfg.W, cfg.N, cfg.G, max_ctx,
-                1 if cfg.dtype == "bf16" else 0)
+                1 if cfg.dtype == "bf16" else 0, 1 if storage == "bf16" else 0)
 
 
 def set_threads(n: int) -> None:
@@ -143,6 +151,11 @@ def philox4x32_10(ctr, key):
     o = (C.c_uint32 * 4)()
     lib().orc_philox4x32_10(c, k, o)
     return [int(x) for x in o]
+
+
+def round_bf16(v: float) -> float:
+    """bfloat16 storage of one value (the bf16 storage mode's rounding)."""
+    return float(lib().orc_round_bf16(float(v)))
 
 
 def uniform(seed: int, pos: int) -> float:
@@ -179,12 +192,14 @@ def attention(cfg, L, q, k, v, bf16: bool, valid=None):
 class Oracle:
     """One decoding context on the CPU: KV cache, window, pool."""
 
-    def __init__(self, cfg, weights, max_ctx: int):
+    def __init__(self, cfg, weights, max_ctx: int, storage: str = "exact"):
+        """storage: "exact" (default) or "bf16" activation storage."""
         self.cfg = cfg
+        self.storage = storage
         self._weights = [np.ascontiguousarray(w) for w in weights]
         ptrs = (C.c_void_p * len(self._weights))(
             *[w.ctypes.data for w in self._weights])
-        self._c = make_cfg(cfg, max_ctx)
+        self._c = make_cfg(cfg, max_ctx, storage)
         self._h = lib().orc_create(C.byref(self._c), ptrs)
         if not self._h:
             raise ValueError("oracle: invalid configuration or out of memory")

@@ -36,6 +36,25 @@
  * never on the thread count.  Argmax decisions are taken on the logits
  * rounded to fp32 (the precision the HIP library's logits have), lowest
  * token id on ties.
+ *
+ * Storage precision (reading: the pages fix no number format).  With
+ * act_bf16 = 0 nothing is rounded: the exact model.  With act_bf16 = 1 the
+ * model of a bf16 datapath: every activation that a bf16 deployment keeps
+ * in memory between operations is stored as bfloat16 (rounded to fp32,
+ * then to 8 significant bits, ties to even at both steps), and everything
+ * else stays exact:
+ *   1. the attention block's normalized input, held as bf16(x * w) with the
+ *      row's 1/rms(x) applied to the products (equal to RMSNorm then
+ *      product in exact arithmetic);
+ *   2. q and k after the rotary embedding, and v: the query and the KV
+ *      cache (committed rows keep the rounded values);
+ *   3. the attention probabilities exp(s - max) entering the weighted sum
+ *      of values (the normalizer sums the unrounded ones);
+ *   4. the attention output (input of the output projection);
+ *   5. the FFN block's normalized input, as in 1;
+ *   6. the SwiGLU output (input of the down projection);
+ *   7. the LM head's input, RMSNorm(x) * w.
+ * The residual stream and every sum stay exact.
  */
 #include <math.h>
 #include <stdint.h>
@@ -52,6 +71,7 @@ typedef struct {
   int32_t W, N, G;
   int32_t max_ctx;
   int32_t wdtype; /* 0: float32 arrays; 1: bfloat16 bit patterns (uint16) */
+  int32_t act_bf16; /* 1: bf16 storage of activations (see the header) */
 } orc_config;
 
 typedef struct {
@@ -100,6 +120,25 @@ static double bf16_to_double(uint16_t b) {
   union { uint32_t u; float f; } v;
   v.u = (uint32_t)b << 16;
   return (double)v.f;
+}
+
+/* bfloat16 storage of a value: the value rounded to fp32 (binary32, to
+ * nearest even), then to the nearest bfloat16, i.e. to 8 significant bits,
+ * ties to even (nearbyint in the default rounding mode); bfloat16 is the
+ * upper half of a binary32 word, so the conversion is defined from fp32.
+ * Exponents stay in fp32's normal range for every value a model produces. */
+double orc_round_bf16(double v) {
+  const double f = (double)(float)v;
+  if (f == 0.0 || !isfinite(f)) return f;
+  int e;
+  const double m = frexp(f, &e); /* f = m 2^e, 0.5 <= |m| < 1 */
+  return ldexp(nearbyint(ldexp(m, 8)), e - 8);
+}
+#define round_bf16 orc_round_bf16
+
+/* A stored activation: rounded in bf16 storage mode, exact otherwise. */
+static double stored(const orc *o, double v) {
+  return o->c.act_bf16 ? round_bf16(v) : v;
 }
 
 static double wget(const void *p, size_t i, int dt) {
@@ -173,6 +212,30 @@ static void rmsnorm(const orc *o, const double *x, int R, const void *w,
   }
 }
 
+/* bf16 storage (1 and 5 of the header): the block input is held as
+ * bf16(x * w); inv[r] = 1/rms(x_r) scales row r of the products instead. */
+static void norm_input_bf16(const orc *o, const double *x, int R, const void *w,
+                            double *out, double *inv) {
+  int d = o->c.d_model, dt = o->c.wdtype;
+  for (int r = 0; r < R; r++) {
+    const double *xr = x + (size_t)r * d;
+    double ss = 0;
+    for (int i = 0; i < d; i++) ss += xr[i] * xr[i];
+    inv[r] = 1.0 / sqrt(ss / d + o->c.rms_eps);
+    for (int i = 0; i < d; i++)
+      out[(size_t)r * d + i] = round_bf16(xr[i] * wget(w, (size_t)i, dt));
+  }
+}
+
+static void scale_rows(double *y, int R, int n, const double *inv) {
+  for (int r = 0; r < R; r++)
+    for (int i = 0; i < n; i++) y[(size_t)r * n + i] *= inv[r];
+}
+
+static void round_all(double *y, size_t n) {
+  for (size_t i = 0; i < n; i++) y[i] = round_bf16(y[i]);
+}
+
 /* Rotary embedding of one head vector at absolute position pos, rotating the
  * adjacent pairs (2i, 2i+1) by pos * theta^(-2i/dh). */
 static void rope(const orc *o, double *v, int pos) {
@@ -212,6 +275,8 @@ static void forward(orc *o, int R, const int32_t *tok, const int32_t *pos,
   double *tmp = malloc(sizeof(double) * (size_t)R * d);
   double *g = malloc(sizeof(double) * (size_t)R * F);
   double *u = malloc(sizeof(double) * (size_t)R * F);
+  double *inv = malloc(sizeof(double) * (size_t)R);
+  const int bf = c->act_bf16;
   /* per-row key order among the block rows */
   int *order = malloc(sizeof(int) * (size_t)R * R);
   int *nord = malloc(sizeof(int) * (size_t)R);
@@ -238,13 +303,24 @@ static void forward(orc *o, int R, const int32_t *tok, const int32_t *pos,
   double scale = 1.0 / sqrt((double)dh);
   for (int l = 0; l < c->n_layers; l++) {
     double *lk = bk + (size_t)l * R * kvd, *lv = bv + (size_t)l * R * kvd;
-    rmsnorm(o, x, R, lw(o, l, L_ANORM), n);
+    if (bf) norm_input_bf16(o, x, R, lw(o, l, L_ANORM), n, inv);
+    else rmsnorm(o, x, R, lw(o, l, L_ANORM), n);
     matmul_wt(n, R, d, lw(o, l, L_Q), qd, dt, q);
     matmul_wt(n, R, d, lw(o, l, L_K), kvd, dt, lk);
     matmul_wt(n, R, d, lw(o, l, L_V), kvd, dt, lv);
+    if (bf) {
+      scale_rows(q, R, qd, inv);
+      scale_rows(lk, R, kvd, inv);
+      scale_rows(lv, R, kvd, inv);
+    }
     for (int r = 0; r < R; r++) {
       for (int h = 0; h < H; h++) rope(o, q + (size_t)r * qd + h * dh, pos[r]);
       for (int h = 0; h < Hkv; h++) rope(o, lk + (size_t)r * kvd + h * dh, pos[r]);
+    }
+    if (bf) { /* 2: the query and the KV cache rows */
+      round_all(q, (size_t)R * qd);
+      round_all(lk, (size_t)R * kvd);
+      round_all(lv, (size_t)R * kvd);
     }
     const double *ck = o->kc + (size_t)l * Hkv * c->max_ctx * dh;
     const double *cv = o->vc + (size_t)l * Hkv * c->max_ctx * dh;
@@ -277,18 +353,24 @@ static void forward(orc *o, int R, const int32_t *tok, const int32_t *pos,
           for (int j = 0; j < nk; j++) {
             const double *vv = j < L ? cv + ((size_t)kh * c->max_ctx + j) * dh
                                      : lv + (size_t)order[(size_t)r * R + j - L] * kvd + kh * dh;
-            for (int i = 0; i < dh; i++) out[i] += sc[j] * vv[i];
+            const double pj = stored(o, sc[j]); /* 3 */
+            for (int i = 0; i < dh; i++) out[i] += pj * vv[i];
           }
-          for (int i = 0; i < dh; i++) out[i] /= z;
+          for (int i = 0; i < dh; i++) out[i] = stored(o, out[i] / z); /* 4 */
         }
       free(sc);
     }
     matmul_wt(att, R, qd, lw(o, l, L_O), d, dt, tmp);
     for (size_t i = 0; i < (size_t)R * d; i++) x[i] += tmp[i];
-    rmsnorm(o, x, R, lw(o, l, L_FNORM), n);
+    if (bf) norm_input_bf16(o, x, R, lw(o, l, L_FNORM), n, inv);
+    else rmsnorm(o, x, R, lw(o, l, L_FNORM), n);
     matmul_wt(n, R, d, lw(o, l, L_GATE), F, dt, g);
     matmul_wt(n, R, d, lw(o, l, L_UP), F, dt, u);
-    for (size_t i = 0; i < (size_t)R * F; i++) g[i] = silu(g[i]) * u[i];
+    if (bf) {
+      scale_rows(g, R, F, inv);
+      scale_rows(u, R, F, inv);
+    }
+    for (size_t i = 0; i < (size_t)R * F; i++) g[i] = stored(o, silu(g[i]) * u[i]); /* 6 */
     matmul_wt(g, R, F, lw(o, l, L_DOWN), d, dt, tmp);
     for (size_t i = 0; i < (size_t)R * d; i++) x[i] += tmp[i];
   }
@@ -303,6 +385,7 @@ static void forward(orc *o, int R, const int32_t *tok, const int32_t *pos,
     for (int r = 0; r < R; r++)
       if (!want || want[r]) memcpy(xs + (size_t)m++ * d, x + (size_t)r * d, sizeof(double) * d);
     rmsnorm(o, xs, nw, o->w[W_FNORM], n);
+    if (bf) round_all(n, (size_t)nw * d); /* 7 */
     matmul_wt(n, nw, d, o->w[W_LM], V, dt, ls);
     m = 0;
     for (int r = 0; r < R; r++)
@@ -310,7 +393,7 @@ static void forward(orc *o, int R, const int32_t *tok, const int32_t *pos,
     free(xs);
     free(ls);
   }
-  free(x); free(n); free(q); free(att); free(tmp); free(g); free(u);
+  free(x); free(n); free(q); free(att); free(tmp); free(g); free(u); free(inv);
   free(order); free(nord);
 }
 

@@ -21,7 +21,21 @@ def _w64(cfg, a):
     return torch.from_numpy(np.asarray(a, np.float64))
 
 
-def textbook_logits(cfg, weights, tokens):
+def _bf16(x):
+    """bfloat16 storage through torch's own conversion (float64 -> float32 ->
+    bfloat16, round to nearest even), widened back to float64."""
+    return x.to(torch.bfloat16).to(torch.float64)
+
+
+def textbook_logits(cfg, weights, tokens, storage="exact"):
+    """Causal logits of every row.  storage="bf16": the seven activations a
+    bf16 datapath stores are rounded with torch's bfloat16 conversion (the
+    normalized block inputs as bf16(x * w) with 1/rms applied to the
+    products, q/k after the rotary embedding and v, the attention
+    probabilities entering the value sum, the attention output, the SwiGLU
+    output and the LM head's normalized input); attention is then written
+    out (softmax with the rounded probabilities) instead of SDPA."""
+    bf = storage == "bf16"
     names = [n for n, _ in lasynth.weight_shapes(cfg)]
     W = {n: _w64(cfg, a) for n, a in zip(names, weights)}
     T = len(tokens)
@@ -39,21 +53,38 @@ def textbook_logits(cfg, weights, tokens):
         xc = torch.view_as_complex(x.reshape(T, x.shape[1], dh // 2, 2).contiguous())
         return torch.view_as_real(xc * rot[:, None, :]).reshape(x.shape)
 
+    def proj(x, wn, *mats):
+        """x's RMSNorm (weights wn) times each matrix; bf16 storage holds
+        bf16(x * wn) and scales the products by 1/rms."""
+        if not bf:
+            n = norm(x, wn)
+            return [n @ m.T for m in mats]
+        n = _bf16(x * wn)
+        s = torch.rsqrt(x.pow(2).mean(-1, keepdim=True) + cfg.rms_eps)
+        return [(n @ m.T) * s for m in mats]
+
+    keep = _bf16 if bf else (lambda t: t)
+    causal = torch.ones(T, T, dtype=torch.bool).tril()
     x = F.embedding(torch.as_tensor(tokens, dtype=torch.long), W["tok_emb"])
     for l in range(cfg.n_layers):
-        n = norm(x, W[f"l{l}.attn_norm"])
-        q = rope((n @ W[f"l{l}.wq"].T).reshape(T, H, dh))
-        k = rope((n @ W[f"l{l}.wk"].T).reshape(T, Hkv, dh))
-        v = (n @ W[f"l{l}.wv"].T).reshape(T, Hkv, dh)
+        q, k, v = proj(x, W[f"l{l}.attn_norm"], W[f"l{l}.wq"], W[f"l{l}.wk"], W[f"l{l}.wv"])
+        q = keep(rope(q.reshape(T, H, dh)))
+        k = keep(rope(k.reshape(T, Hkv, dh)))
+        v = keep(v.reshape(T, Hkv, dh))
         k = k.repeat_interleave(H // Hkv, dim=1)
         v = v.repeat_interleave(H // Hkv, dim=1)
-        a = F.scaled_dot_product_attention(q.transpose(0, 1), k.transpose(0, 1),
-                                           v.transpose(0, 1), is_causal=True)
+        if not bf:
+            a = F.scaled_dot_product_attention(q.transpose(0, 1), k.transpose(0, 1),
+                                               v.transpose(0, 1), is_causal=True)
+        else:
+            sc = (q.transpose(0, 1) @ k.permute(1, 2, 0)) / dh ** 0.5  # [H][T][T]
+            sc = sc.masked_fill(~causal, float("-inf"))
+            p = torch.exp(sc - sc.amax(-1, keepdim=True))
+            a = keep((keep(p) @ v.transpose(0, 1)) / p.sum(-1, keepdim=True))
         x = x + a.transpose(0, 1).reshape(T, H * dh) @ W[f"l{l}.wo"].T
-        n = norm(x, W[f"l{l}.ffn_norm"])
-        h = F.silu(n @ W[f"l{l}.w_gate"].T) * (n @ W[f"l{l}.w_up"].T)
-        x = x + h @ W[f"l{l}.w_down"].T
-    return (norm(x, W["final_norm"]) @ W["lm_head"].T).numpy()
+        g, u = proj(x, W[f"l{l}.ffn_norm"], W[f"l{l}.w_gate"], W[f"l{l}.w_up"])
+        x = x + keep(F.silu(g) * u) @ W[f"l{l}.w_down"].T
+    return (keep(norm(x, W["final_norm"])) @ W["lm_head"].T).numpy()
 
 
 SMALL = [
@@ -76,6 +107,22 @@ def test_causal_logits_match_textbook(cfg):
     _, lg = o.extend(toks, logits=True)
     ref = textbook_logits(cfg, w, toks)
     assert np.max(np.abs(lg - ref)) < 1e-9
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_bf16_storage_logits_match_textbook(cfg):
+    """The oracle's bf16 storage mode against the textbook decoder rounding
+    the same seven activations with torch's bfloat16 conversion."""
+    w = lasynth.make_weights(cfg, seed=3)
+    toks = np.random.default_rng(5).integers(0, cfg.vocab, size=40).astype(np.int32)
+    o = oracle.Oracle(cfg, w, 64, storage="bf16")
+    _, lg = o.extend(toks, logits=True)
+    ref = textbook_logits(cfg, w, toks, storage="bf16")
+    assert np.max(np.abs(lg - ref)) < 1e-9
+    # and the storage changes the logits (by rounding-sized amounts)
+    exact = textbook_logits(cfg, w, toks)
+    d = np.max(np.abs(lg - exact))
+    assert 1e-5 < d < 0.1, d
 
 
 def test_chunked_prefill_is_bit_identical(tiny):
