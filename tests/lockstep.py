@@ -38,20 +38,32 @@ def draw_tol(logit_tol, temperature):
 
 
 class Lockstep:
-    def __init__(self, cfg, weights, max_ctx, logit_tol, tie_margin=0.05, sampling=None):
-        """sampling: (temperature, top_k, top_p, seed) for both sides, or None."""
+    def __init__(self, cfg, weights, max_ctx, logit_tol, tie_margin=0.05, sampling=None,
+                 storage="exact", dev_weights=None):
+        """sampling: (temperature, top_k, top_p, seed) for both sides, or None.
+        storage: the oracle's activation storage ("exact" or "bf16").
+        dev_weights: device tensors already holding `weights` (else uploaded)."""
         self.cfg = cfg
         self.tol = logit_tol
         self.tie = tie_margin
-        self.dev = la.LookaheadDecoder(cfg, la.upload_weights(weights), max_ctx)
-        self.orc = oracle.Oracle(cfg, weights, max_ctx)
+        if dev_weights is None:
+            dev_weights = la.upload_weights(weights)
+        self.dev = la.LookaheadDecoder(cfg, dev_weights, max_ctx)
+        self.orc = oracle.Oracle(cfg, weights, max_ctx, storage=storage)
         self.sampling = sampling
         if sampling:
             self.dev.set_sampling(*sampling)
             self.orc.set_sampling(*sampling)
         self.ties = 0
         self.max_diff = 0.0
+        self.sq_sum, self.n_cmp = 0.0, 0
+        self.step_stats = []  # per step: (max |dlogit|, rms |dlogit|, excused ties)
+        self.excused = []  # (step, row, oracle margin) of every excused decision
         self.steps = []
+
+    @property
+    def rms_diff(self):
+        return (self.sq_sum / self.n_cmp) ** 0.5 if self.n_cmp else 0.0
 
     def _first_token_excused(self, lg, n_prompt, sampling):
         if sampling:
@@ -68,8 +80,18 @@ class Lockstep:
             ok, m = self._first_token_excused(lg, len(prompt), self.sampling)
             assert ok, f"prefill token {fg} vs oracle {fo}, margin {m}"
             self.ties += 1
+            self.excused.append((-1, 0, float(m)))
             self.orc.set_current(fg)
         return fg
+
+    def tokens_before_first_excuse(self, out):
+        """How many leading tokens of out (the prefill's token, then every
+        step's emitted tokens) were decided with no excused decision: all
+        of them, or those of the steps before the first that adopted one."""
+        if not self.excused:
+            return len(out)
+        s0 = min(s for s, _, _ in self.excused)
+        return 0 if s0 < 0 else 1 + sum(len(r["tokens"]) for r in self.steps[:s0])
 
     def seed(self, seq):
         """Seed both pools with the n-grams of seq; the pools must agree."""
@@ -102,8 +124,13 @@ class Lockstep:
         assert nc == rg["n_candidates"], (nc, rg)
         assert np.array_equal(tok_g[v], tok_o[v])
         lg_o = orc.forward_block(tok_o, valid, keep=True)
-        d = float(np.max(np.abs(lg_g[v].astype(np.float64) - lg_o[v])))
+        diff = lg_g[v].astype(np.float64) - lg_o[v]
+        d = float(np.max(np.abs(diff)))
+        sq = float(np.sum(diff * diff))
         self.max_diff = max(self.max_diff, d)
+        self.sq_sum += sq
+        self.n_cmp += diff.size
+        ties0 = self.ties
         assert d <= self.tol, f"logit diff {d} > {self.tol} at step {len(self.steps)}"
         amax_o, dmarg = orc.block_select()
         for r in np.nonzero(v)[0]:
@@ -116,7 +143,9 @@ class Lockstep:
                     f"step {len(self.steps)} row {r}: token {amax_g[r]} vs oracle "
                     f"{amax_o[r]}, oracle margin {m}")
                 self.ties += 1
+                self.excused.append((len(self.steps), int(r), float(m)))
                 amax_o[r] = amax_g[r]
+        self.step_stats.append((d, (sq / diff.size) ** 0.5, self.ties - ties0))
         ro = orc.commit(amax_o)
         assert ro == rg, (ro, rg)
         if cfg.W:
@@ -165,6 +194,9 @@ class BatchLockstep(Lockstep):
                 self.orcs[b].set_sampling(*sp)
         self.ties = 0
         self.max_diff = 0.0
+        self.sq_sum, self.n_cmp = 0.0, 0
+        self.step_stats = []
+        self.excused = []
         self.steps = []
 
     def prefill(self, prompts, wins):

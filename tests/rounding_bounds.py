@@ -3,16 +3,16 @@
     python tests/rounding_bounds.py [--out PATH] [7b 13b 34b]
         (default PATH: tests/golden/rounding_bounds.json)
 
-The bf16 library stores activations as bf16 at seven points of each layer
+A bf16 datapath stores activations as bf16 at seven points of each layer
 and accumulates everything else in fp32.  This script measures how far that
 storage alone moves the logits, on the same seeded weights the full-size
 tests draw (lasynth.make_weights_device) and the first TOKENS tokens of the
 workload's prompt (causal forward): one forward in fp64 with no rounding,
-one in fp64 that rounds to bf16 (nearest even) exactly where the library
-stores bf16:
+one in fp64 that rounds to bf16 (torch's conversion: through fp32, nearest
+even) at all seven points, and one per point with only that point rounded:
 
   1. the GEMM input of the attention block, x * w_attn_norm (the 1/rms
-     factor is applied to the fp32 product afterwards);
+     factor is applied to the products afterwards);
   2. q and k after the rotary embedding, and v (the query buffer and the
      KV cache);
   3. the attention probabilities exp(s - max) entering the PV product (the
@@ -20,13 +20,14 @@ stores bf16:
   4. the attention output (input of the O projection);
   5. the GEMM input of the FFN block, x * w_ffn_norm (1/rms afterwards);
   6. the SwiGLU output (input of the down projection);
-  7. the LM-head input, x * w_final_norm (1/rms afterwards).
+  7. the LM-head input, RMSNorm(x) * w_final_norm.
 
-The residual stream stays fp32 in the library and unrounded here.  The
-recorded figure per shape is the largest |logit difference| over all rows
-and the vocabulary; tests take 1.5x it as the bound of one bf16 run against
-exact arithmetic, and twice that for two bf16 runs against each other (each
-is within the bound of the exact logits).
+These are the storage points of the oracle's bf16 storage mode.  The
+residual stream stays unrounded.  Recorded per shape: the largest and rms
+|logit difference| over all rows and the vocabulary with all seven points
+("max_abs_dlogit", "rms_dlogit"), and the same for each point alone
+("by_point").  Tests take 1.5x max_abs_dlogit as the bound of one bf16 run
+against exact arithmetic.
 
 This is test infrastructure: torch only, no call into the HIP library.
 """
@@ -47,6 +48,21 @@ OUT = os.path.join(HERE, "golden", "rounding_bounds.json")
 
 def bf(x):
     return x.to(torch.bfloat16).to(x.dtype)
+
+
+VARIANTS = ["exact", "all"] + [f"only_{k}" for k in range(1, 8)]
+
+
+def _rounders(variant):
+    """r[k](v): point k's storage for this variant (bf16 or identity)."""
+    ident = lambda v: v
+    if variant == "exact":
+        on = set()
+    elif variant == "all":
+        on = set(range(1, 8))
+    else:
+        on = {int(variant.split("_")[1])}
+    return {k: (bf if k in on else ident) for k in range(1, 8)}
 
 
 def measure(name):
@@ -76,18 +92,18 @@ def measure(name):
         return 1.0 / torch.sqrt((x * x).mean(-1, keepdim=True) + cfg.rms_eps)
 
     emb = f64("tok_emb")[toks]
-    xs = [emb.clone(), emb.clone()]  # exact, rounded
+    rs = {v: _rounders(v) for v in VARIANTS}
+    xs = {v: emb.clone() for v in VARIANTS}
     for l in range(cfg.n_layers):
         p = f"l{l}."
         wq, wk, wv, wo = f64(p + "wq"), f64(p + "wk"), f64(p + "wv"), f64(p + "wo")
-        for i, rnd in enumerate((False, True)):
-            r = bf if rnd else (lambda v: v)
-            x = xs[i]
-            a = r(x * f64(p + "attn_norm"))
+        for var in VARIANTS:
+            r, x = rs[var], xs[var]
+            a = r[1](x * f64(p + "attn_norm"))
             s = inv_rms(x)
-            q = r(rope(((a @ wq.T) * s).view(T, H, dh)))
-            k = r(rope(((a @ wk.T) * s).view(T, Hkv, dh)))
-            v = r(((a @ wv.T) * s).view(T, Hkv, dh))
+            q = r[2](rope(((a @ wq.T) * s).view(T, H, dh)))
+            k = r[2](rope(((a @ wk.T) * s).view(T, Hkv, dh)))
+            v = r[2](((a @ wv.T) * s).view(T, Hkv, dh))
             k = k.repeat_interleave(H // Hkv, dim=1)
             v = v.repeat_interleave(H // Hkv, dim=1)
             qh = q.permute(1, 0, 2).contiguous()  # [H][T][dh]
@@ -95,31 +111,31 @@ def measure(name):
             vh = v.permute(1, 0, 2).contiguous()  # [H][T][dh]
             sc = torch.matmul(qh, kh) / math.sqrt(dh) + mask
             e = torch.exp(sc - sc.amax(-1, keepdim=True))
-            o = torch.matmul(r(e), vh) / e.sum(-1, keepdim=True)  # [H][T][dh]
-            x = x + r(o.permute(1, 0, 2).reshape(T, H * dh)) @ wo.T
-            xs[i] = x
+            o = torch.matmul(r[3](e), vh) / e.sum(-1, keepdim=True)  # [H][T][dh]
+            xs[var] = x + r[4](o.permute(1, 0, 2).reshape(T, H * dh)) @ wo.T
         del wq, wk, wv, wo
         wg, wu, wd = f64(p + "w_gate"), f64(p + "w_up"), f64(p + "w_down")
-        for i, rnd in enumerate((False, True)):
-            r = bf if rnd else (lambda v: v)
-            x = xs[i]
-            a = r(x * f64(p + "ffn_norm"))
+        for var in VARIANTS:
+            r, x = rs[var], xs[var]
+            a = r[5](x * f64(p + "ffn_norm"))
             s = inv_rms(x)
             g, u = (a @ wg.T) * s, (a @ wu.T) * s
-            xs[i] = x + r(torch.nn.functional.silu(g) * u) @ wd.T
+            xs[var] = x + r[6](torch.nn.functional.silu(g) * u) @ wd.T
         del wg, wu, wd
     lm = f64("lm_head")
-    lg = []
-    for i, rnd in enumerate((False, True)):
-        r = bf if rnd else (lambda v: v)
-        x = xs[i]
-        lg.append((r(x * f64("final_norm")) @ lm.T) * inv_rms(x))
-    dd = (lg[1] - lg[0]).abs()
-    res = {"layers": cfg.n_layers, "d_model": d, "tokens": T,
-           "max_abs_dlogit": float(dd.max()),
-           "rms_dlogit": float(dd.pow(2).mean().sqrt()),
-           "logit_std": float(lg[0].std())}
-    print(name, res, flush=True)
+    lg = {}
+    for var in VARIANTS:
+        x = xs[var]
+        lg[var] = rs[var][7](x * inv_rms(x) * f64("final_norm")) @ lm.T
+
+    def stats(var):
+        dd = (lg[var] - lg["exact"]).abs()
+        return {"max_abs_dlogit": float(dd.max()), "rms_dlogit": float(dd.pow(2).mean().sqrt())}
+
+    res = {"layers": cfg.n_layers, "d_model": d, "tokens": T, **stats("all"),
+           "logit_std": float(lg["exact"].std()),
+           "by_point": {v: stats(v) for v in VARIANTS[2:]}}
+    print(name, json.dumps(res), flush=True)
     del W, wt
     torch.cuda.empty_cache()
     return res

@@ -1,33 +1,31 @@
 """The LLaMA-2-7B-shaped workload at full size (GPU only), in the launch
 configuration bench.py times (121 rows per step, W15 N5 G15).
 
-- Sampled rows vs the oracle: after a short prompt, the true greedy
-  continuation is planted as a candidate; the step's row 0 and candidate
-  rows must match the oracle's causal logits of the same tokens, the argmax
-  decisions must agree wherever the oracle's top-2 margin exceeds twice the
-  logit tolerance, and the candidate must be accepted in full.
+- Headline lockstep: from the workload's 512-token prompt, six lookahead
+  steps in lockstep with the exact oracle, the pool seeded with the prompt's
+  n-grams and with the oracle's own greedy continuation, so that steps
+  accept candidates (KV compaction, multi-token emits).  Every step: all
+  valid rows' logits, every decision, the block tokens, the step result,
+  the window and the whole pool.
 - A property that holds at any size: the lookahead output equals plain
-  one-token greedy decoding (here both on the GPU, 512-token prompt, 256
-  tokens).  While the two share the history, a lookahead step's
-  current-token row and the plain step at the same position compute the
-  same logits through different row layouts and summation orders: they
-  must agree within the full-depth bound below, and a divergence is allowed
-  only where the plain run's top-2 margin is within twice that bound.
+  one-token greedy decoding (both on the GPU, 512-token prompt, 256
+  tokens); where the two runs part, the exact oracle (run over the shared
+  history) must rank both tokens within the decision margin of its best.
 
-Logit tolerance at full depth.  The bf16 datapath stores activations in
-bf16 at seven points per layer (normed inputs of the QKV and FFN GEMMs,
-q/k/v and the KV cache, attention probabilities, attention output, SwiGLU
-output, final normed input of the LM head).  Rounding alone, with every
-other operation exact, moves the logits of this 32-layer model by up to
-0.181 (rms 0.034; fp64 emulation on these weights over 32 prompt tokens x
-32000 logits, tests/rounding_bounds.py); any single one of the seven
-roundings already exceeds 2e-2 by four layers.  The 2e-2 bound therefore
-applies to the shallow bf16 parity configurations
-(tests/test_gpu_parity.py); here one GPU run against the oracle is held to
-1.5x the emulated rounding-only error, with argmax decisions excused where
-two logits that far off can swap (margin <= 2 x tolerance); two GPU runs
-against each other, to twice that bound (each is within it of the exact
-logits), with decisions excused at margins up to twice the comparison bound.
+Bounds at full depth (bf16 datapath against exact arithmetic; see
+helpers.full_depth_bounds).  The datapath stores seven activations per layer
+in bf16; that storage alone moves this model's logits by up to 0.185 (rms
+0.034) on its own weights (tests/rounding_bounds.py, all seven points; by
+point alone the KV cache and q/k/v move them most, 0.124).  No bf16
+reference helps here: a bf16-storage oracle rounding at the very same
+points differs from this datapath by as much as the exact oracle does, since
+two bf16 pipelines' rounding errors decorrelate within a few layers once
+their inputs differ by a fraction of a bf16 step.  The tests therefore hold
+every logit to 1.5x the rounding-only max (0.278), the rms difference to
+1.5x the rounding-only rms (0.051), and excuse a differing decision only
+where the oracle's top-2 margin is within 5 sqrt(2) times that rms (0.24).
+The 2e-2 logit bound and 0.05 decision margin hold on the shallow bf16
+configurations (tests/test_gpu_parity.py), not at 32 layers.
 """
 import numpy as np
 import pytest
@@ -36,13 +34,12 @@ import torch
 import lasynth
 import lookahead_decoding_la_amd as la
 import oracle
-from helpers import full_depth_logit_tol
-from lockstep import log, margin
+from helpers import full_depth_bounds
+from lockstep import Lockstep, log, margin
 
 pytestmark = pytest.mark.gpu
 
-LOGIT_TOL_7B = full_depth_logit_tol("7b")  # 1.5 x the rounding-only error: 0.272
-TIE_MARGIN_7B = 2 * LOGIT_TOL_7B
+MAX_TOL, RMS_TOL, DECISION_MARGIN = full_depth_bounds("7b")
 
 
 @pytest.fixture(scope="module")
@@ -56,51 +53,43 @@ def w7b():
     torch.cuda.empty_cache()
 
 
-def test_7b_sampled_rows_match_oracle(w7b):
+@pytest.mark.timeout(900)
+def test_7b_headline_lockstep(w7b):
     cfg, dev_w = w7b
-    c32 = cfg.with_(prompt_len=32, n_spans=1, span_len=8)
-    prompt = [int(x) for x in lasynth.make_prompt(c32)]
+    prompt = [int(x) for x in lasynth.make_prompt(cfg)]
     win = lasynth.make_init_window(cfg, np.array(prompt))
-    P, n1 = len(prompt), cfg.N - 1
-    dec = la.LookaheadDecoder(cfg, dev_w, 512)
-    first = dec.prefill(prompt, win)
-    plain = la.LookaheadDecoder(cfg.with_(W=0, G=0), dev_w, 512)
-    assert plain.prefill(prompt) == first
-    cont = []
-    while len(cont) < cfg.N:
-        cont += plain.step()["tokens"]
-    plain.close()
-    dec.debug_pool_insert(first, cont[:n1])
-    r = dec.step()
-    lg = dec.debug_logits()
-    _, amax = dec.debug_block()
-    log(f"[7b] step: accepted {r['accepted']} of {n1}; oracle forward of {P + cfg.N} rows")
-    orc = oracle.Oracle(cfg, lasynth.host_bits(dev_w), 64)
-    _, lo = orc.extend(prompt + [first] + cont[:n1], logits=True)
-    # GPU row 0 <-> oracle row P; candidate row (0, i) <-> oracle row P + i
-    rows = [0] + [1 + n1 * cfg.W + (i - 1) for i in range(1, cfg.N)]
-    ties = 0
-    ref_args = []
-    for j, r_gpu in enumerate(rows):
-        ref = lo[P + j]
-        d = float(np.max(np.abs(lg[r_gpu].astype(np.float64) - ref)))
-        ref_arg = int(np.argmax(ref.astype(np.float32)))
-        m = margin(ref)
-        log(f"  row {r_gpu}: max|dlogit| {d:.3e}, argmax {amax[r_gpu]} vs {ref_arg} (margin {m:.3f})")
-        assert d <= LOGIT_TOL_7B
-        if amax[r_gpu] != ref_arg:
-            assert m <= TIE_MARGIN_7B
-            ties += 1
-        ref_args.append(ref_arg)
-    # the prefill's decision too
-    m = margin(lo[P - 1])
-    assert int(np.argmax(lo[P - 1].astype(np.float32))) == first or m <= TIE_MARGIN_7B
-    # the planted continuation comes from the GPU's plain decoder: with no
-    # excused disagreement it is also the oracle's, and must be accepted
-    if not ties and ref_args == cont:
-        assert r["accepted"] == n1 and r["tokens"] == cont
+    assert len(prompt) == 512 and cfg.T == 121
+    ls = Lockstep(cfg, lasynth.host_bits(dev_w), 1024, logit_tol=MAX_TOL,
+                  tie_margin=DECISION_MARGIN, dev_weights=dev_w)
+    log("[7b] prefill of 512 tokens, GPU and oracle")
+    first = ls.prefill(prompt, win)
+    # the oracle's own greedy continuation (14 tokens: three accepting
+    # steps of N - 1 = 4 candidates plus a bonus each), then back
+    cont = [ls.orc.greedy_next() for _ in range(14)]
+    ls.orc.rewind(len(prompt), first)
+    ls.seed(prompt)
+    ls.seed([first] + cont)
+    for s in range(6):
+        r = ls.step()
+        d, rms, ties = ls.step_stats[-1]
+        log(f"[7b] step {s}: accepted {r['accepted']}, emitted {r['tokens']}, "
+            f"max|dlogit| {d:.4f}, rms {rms:.4f}, excused decisions {ties}")
+    far = [m for _, _, m in ls.excused if m > 0.05]
+    log(f"[7b] lockstep: max|dlogit| {ls.max_diff:.4f} (bound {MAX_TOL:.3f}), "
+        f"rms {ls.rms_diff:.4f} (bound {RMS_TOL:.3f}), {ls.ties} excused decisions of "
+        f"1 + 6 x {cfg.T} decisions; "
+        f"{len(far)} of them at oracle margins above 0.05 {sorted(far)}")
+    assert ls.rms_diff <= RMS_TOL
+    assert sum(st["accepted"] for st in ls.steps) >= cfg.N - 1
+    # KV compaction: layer 0's cache (whose rows depend on nothing but the
+    # token, its position and layer-0 weights) holds the right rows
+    kg, vg = ls.dev.debug_kv(0, 0, ls.orc.kv_len)
+    ko, vo = ls.orc.kv(0, 0, ls.orc.kv_len)
+    for g, o in ((kg, ko), (vg, vo)):
+        assert np.all(np.abs(g - o) <= 2.0 ** -7 * np.abs(o) + 2e-3)
 
 
+@pytest.mark.timeout(900)
 def test_7b_lookahead_output_equals_plain_greedy(w7b):
     cfg, dev_w = w7b
     prompt = lasynth.make_prompt(cfg)
@@ -116,23 +105,25 @@ def test_7b_lookahead_output_equals_plain_greedy(w7b):
         toks += r["tokens"]
     toks = toks[:M]
     dec.close()
-    acc = sum(s["n_emitted"] for s in steps) / len(steps)
-    log(f"[7b] lookahead: {len(steps)} steps for {M} tokens ({acc:.2f} tokens/step)")
     plain = la.LookaheadDecoder(cfg.with_(W=0, G=0), dev_w, 1024)
     ref = [plain.prefill(prompt)]
-    margins, dmax = [None], 0.0
+    dmax = 0.0
     while len(ref) < M:
         n = len(ref)
         ref += plain.step()["tokens"]
-        lg = plain.debug_logits()[0]
-        margins.append(margin(lg))
         if n in la_logits and toks[:n] == ref[:n]:
-            dmax = max(dmax, float(np.max(np.abs(la_logits[n] - lg))))
+            dmax = max(dmax, float(np.max(np.abs(la_logits[n] - plain.debug_logits()[0]))))
     plain.close()
     div = next((i for i in range(M) if toks[i] != ref[i]), None)
-    log(f"[7b] first divergence: {div}" +
-        (f" (plain margin {margins[div]:.3f})" if div else "") +
-        f"; max |logit difference| before it {dmax:.3f}")
-    assert dmax <= 2 * LOGIT_TOL_7B
-    if div is not None:
-        assert div > 0 and margins[div] <= 4 * LOGIT_TOL_7B, (div, margins[div])
+    log(f"[7b] {len(steps)} lookahead steps; first divergence from plain decoding: {div}; "
+        f"max |row-0 logit difference| before it {dmax:.3f}")
+    # each run is within MAX_TOL of the exact logits
+    assert dmax <= 2 * MAX_TOL
+    if div is not None:  # 0: the two contexts' prefills (different launch shapes) part
+        orc = oracle.Oracle(cfg, lasynth.host_bits(dev_w), len(prompt) + div + 8)
+        _, lo = orc.extend([int(x) for x in prompt] + toks[:div], logits=True)
+        z = lo[-1].astype(np.float32)
+        gap = [float(z.max() - z[t]) for t in (toks[div], ref[div])]
+        log(f"[7b] at the divergence the oracle ranks the two tokens {gap[0]:.3f} and "
+            f"{gap[1]:.3f} below its best (top-2 margin {margin(lo[-1]):.3f})")
+        assert max(gap) <= DECISION_MARGIN

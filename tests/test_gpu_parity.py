@@ -40,8 +40,12 @@ def test_fp32_lockstep(cfg):
     toks = ls.run(p, win, M=cfg.gen_tokens)
     ls.compare_kv(1e-4)
     log(f"  steps={len(ls.steps)} max|dlogit|={ls.max_diff:.2e} ties={ls.ties}")
-    # and the output is plain greedy decoding
-    assert toks[:cfg.gen_tokens] == oracle.Oracle(cfg, w, 512).greedy(p, cfg.gen_tokens) or ls.ties
+    # and the output is plain greedy decoding, up to the first step that
+    # adopted an excused decision (the oracle's greedy run never adopts)
+    M = cfg.gen_tokens
+    n = min(ls.tokens_before_first_excuse(toks), M)
+    assert toks[:n] == oracle.Oracle(cfg, w, 512).greedy(p, M)[:n]
+    log(f"  {n} of {M} tokens compared with plain greedy decoding")
 
 
 BF16 = [

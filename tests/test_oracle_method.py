@@ -413,3 +413,22 @@ def test_winner_with_nothing_accepted_is_candidate_zero(tiny):
     res, _ = _verify_case(tiny, [[a, 2], [a, 4], [5, 6]], ones)
     assert res["accepted"] == 1 and res["winner"] == 0
     assert res["tokens"] == [a, 99]
+
+
+def test_rewind_then_decode_again_is_identical(tiny):
+    """Decoding ahead with plain greedy steps and rewinding to the prefill
+    state leaves the context as a fresh prefill would: the next lookahead
+    step's result and logits are unchanged."""
+    cfg, w, p, win = tiny
+    a = oracle.Oracle(cfg, w, 256)
+    first = a.prefill(p, win)
+    ahead = [a.greedy_next() for _ in range(6)]
+    assert ahead == oracle.Oracle(cfg, w, 256).greedy(p, 7)[1:]
+    a.rewind(len(p), first)
+    ra, la_ = a.step(logits=True)
+    b = oracle.Oracle(cfg, w, 256)
+    b.prefill(p, win)
+    rb, lb = b.step(logits=True)
+    assert ra == rb and np.array_equal(la_, lb, equal_nan=True)
+    with pytest.raises(ValueError):
+        a.rewind(a.kv_len + 1, 0)
