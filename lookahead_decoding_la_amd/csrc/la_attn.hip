@@ -170,7 +170,6 @@ __host__ __device__ inline int eff_splits(int nch, int smax, int M) {
 template <int NRP, int KSPL, int NBUF>
 __global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
   constexpr int NW = NRP * KSPL;
-  constexpr int NT = NW * 64;
   constexpr int QROWS = 32 * NRP;                // query rows held
   constexpr int QPT = QROWS * 256 / 1024 / NW;   // Q load instructions per thread
   constexpr int LPC = 32 / NW;                   // chunk load instructions per thread
@@ -549,6 +548,222 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   *(uint2*)&((uint16_t*)a.out)[oi] = pk;
 }
 
+// ---------------------------------------------------------------------------
+// Blocks of more than 32 rows: one workgroup per (head, 16-row tile,
+// sequence) that covers every key, so no split merge is needed and the
+// grid (heads x tiles, 256 workgroups at 32 heads x 121 rows) fills the
+// CUs by itself.  K and V^T go through LDS in 128-key chunks
+// (global_load_lds, 1 KiB = 4 whole K rows or 4 whole V^T rows per
+// instruction) in a 2-chunk ring; the NW = 4 waves share every chunk, wave
+// w taking its keys 32 w .. 32 w + 31, and each runs its own online softmax
+// over its keys; (m, l, O) of the four are combined through LDS at the
+// end.  K/V of a head is read by all of its tiles' workgroups: grid x
+// enumerates heads KV head first, so that the tiles of a head, and the
+// query heads of one KV head, share an XCD and its L2.
+constexpr int AT_NW = 4;                 // waves per workgroup
+constexpr int AT_CK = 32 * AT_NW;        // keys per chunk
+constexpr int AT_KB = AT_CK * A_DH * 2;  // K bytes per chunk (32 KiB), V^T as many
+constexpr int AT_LPC = 2 * AT_CK / 4 / AT_NW;  // 1 KiB loads per thread per chunk (K and V^T)
+
+// LDS V^T layout for 128-key chunks: dim d owns bytes [256 d, 256 d + 256),
+// keys 8p .. 8p + 7 sit in slot p ^ (d & 15), so the 16 dims one PV operand
+// read touches spread over all 64 banks.
+__device__ inline int vswz16(int d) { return d & 15; }
+
+__global__ __launch_bounds__(AT_NW * 64) void k_attn_tile(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * 2 * AT_KB];
+  const int M = a.M;
+  const int gq = a.H / a.Hkv;  // query heads per KV head
+  const int kvh = blockIdx.x % a.Hkv, h = kvh * gq + blockIdx.x / a.Hkv;
+  const int tile = blockIdx.y, sq = blockIdx.z;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+  const int g = l >> 4, c16 = l & 15;
+  const int r0 = sq * a.rps;  // the sequence's first row in q and out
+  const bool causal = a.mode == MODE_CAUSAL;
+  const int t = tile * 16 + c16;  // this lane's query row
+  const int trow = t < M ? t : (causal ? M - 1 : 0);  // padding rows take a valid row
+
+  bf16x8 qf[4];  // Q^T fragments of the tile (B operand), k-step ks
+  {
+    const uint16_t* qp = (const uint16_t*)a.q + (size_t)(r0 + trow) * (a.H * A_DH) + h * A_DH + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) qf[ks] = *(const bf16x8*)(qp + 32 * ks);
+  }
+  const int L = a.st ? *(const __attribute__((address_space(4))) int32_t*)&a.st[sq].L : a.L_host;
+  const int ctx = L + M;
+  const int nch = (ctx + AT_CK - 1) / AT_CK;
+  const float sl2 = LOG2E / sqrtf((float)A_DH);
+
+  // Chunk loads: instruction j (of AT_LPC / 2 per thread for K, as many for
+  // V^T) covers K rows 4 j' .. 4 j' + 3 or V^T dims 4 j' .. 4 j' + 3 (j' =
+  // w + j NW); lane l loads the global piece that belongs at LDS slot l.
+  // Keys past the cache row (the last chunk may reach 64 keys beyond
+  // ctx_stride, a multiple of 64) are clamped to its last piece: they lie
+  // past the context and are never used.
+  const uint16_t* kc = (const uint16_t*)a.k_cache + sq * a.kv_seq + (size_t)kvh * a.ctx_stride * A_DH;
+  const uint16_t* vc = (const uint16_t*)a.vt_cache + sq * a.kv_seq + (size_t)kvh * A_DH * a.ctx_stride;
+  int krow[AT_LPC / 2], kpc[AT_LPC / 2], vdim[AT_LPC / 2], vkey[AT_LPC / 2];
+#pragma unroll
+  for (int q = 0; q < AT_LPC / 2; q++) {
+    const int j = w + q * AT_NW;  // 0 .. 31
+    krow[q] = 4 * j + (l >> 4);
+    kpc[q] = (l & 15) ^ kswz(krow[q] & 63);
+    vdim[q] = 4 * j + (l >> 4);
+    vkey[q] = 8 * ((l & 15) ^ vswz16(vdim[q]));
+  }
+  auto issue = [&](int c, int b) {
+    c = min(c, nch - 1);  // past the end: the last chunk again, never read
+    unsigned char* kb = lds + b * 2 * AT_KB;
+    unsigned char* vb = kb + AT_KB;
+#pragma unroll
+    for (int q = 0; q < AT_LPC / 2; q++) {
+      const int j = w + q * AT_NW;
+      const int key = min(c * AT_CK + krow[q], a.ctx_stride - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(kc + (size_t)key * A_DH + 8 * kpc[q]),
+                                       (__attribute__((address_space(3))) void*)(kb + j * 1024),
+                                       16, 0, 0);
+      const int k0 = min(c * AT_CK + vkey[q], a.ctx_stride - 8);
+      __builtin_amdgcn_global_load_lds((const void*)(vc + (size_t)vdim[q] * a.ctx_stride + k0),
+                                       (__attribute__((address_space(3))) void*)(vb + j * 1024),
+                                       16, 0, 0);
+    }
+  };
+
+  f32x4 o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; dt++) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // This wave's 32 keys of chunk c (slice s = 4 c + w: keys 32 s ..).  K row
+  // of score-tile row c16 in tile kt: key 8 (c16 / 4) + 4 kt + c16 % 4 of
+  // the slice, so that the 8 keys a lane holds after QK^T are keys
+  // 8 g .. 8 g + 7, the lane's P^T operand and one contiguous V^T piece.
+  auto compute = [&](const unsigned char* kb, const unsigned char* vb, int c) {
+    const int s = c * AT_NW + w;
+    f32x4 sc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++) {
+      sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int r = 32 * w + 8 * (c16 >> 2) + 4 * kt + (c16 & 3);
+      const unsigned char* kr = kb + r * 256;
+      const int sw = kswz(r & 63);
+#pragma unroll
+      for (int ks = 0; ks < 4; ks++) {
+        const bf16x8 kf = *(const bf16x8*)(kr + (((4 * ks + g) ^ sw) << 4));
+        sc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sc[kt], 0, 0, 0);
+      }
+    }
+    if (32 * s + 32 > L) {  // the slice reaches into the block (wave-uniform)
+      uint64_t rm0 = 0ull, rm1 = 0ull, rm2 = 0ull, rm3 = 0ull;
+      if (!causal) step_row_mask(trow, a.W, a.N, rm0, rm1, rm2, rm3);
+      const uint64_t win = chunk_window(causal, trow, 32 * s - L, rm0, rm1, rm2, rm3) >> (8 * g);
+#pragma unroll
+      for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+        for (int v = 0; v < 4; v++)
+          if (!((win >> (4 * kt + v)) & 1ull)) sc[kt][v] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+      for (int v = 0; v < 4; v++) mx = fmaxf(mx, sc[kt][v]);
+    mx = wave_max_groups(mx) * sl2;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + RESCALE_LOG2)) {  // wave-uniform
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++) o[dt] *= alpha;
+      m_run = m_new;
+    }
+    const float nm = m_run == -INFINITY ? 0.f : -m_run;  // nothing visible yet: 0
+    bf16x8 pf;
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+      for (int v = 0; v < 4; v++) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[kt][v], sl2, nm));
+        l_run += p;
+        pf[4 * kt + v] = (__bf16)p;
+      }
+    // Keys past the context (last chunk only) have zero probability, but
+    // their V^T entries may be stale memory: zero them so that no NaN
+    // reaches the MFMA.
+    const int nvk = ctx - 32 * s;
+    const int kv = nvk - 8 * g;  // valid keys among this lane's 8
+    const uint32_t vm0 = kv >= 2 ? ~0u : (kv == 1 ? 0xffffu : 0u);
+    const uint32_t vm1 = kv >= 4 ? ~0u : (kv == 3 ? 0xffffu : 0u);
+    const uint32_t vm2 = kv >= 6 ? ~0u : (kv == 5 ? 0xffffu : 0u);
+    const uint32_t vm3 = kv >= 8 ? ~0u : (kv == 7 ? 0xffffu : 0u);
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) {
+      const int d = dt * 16 + c16;
+      bf16x8 vf = *(const bf16x8*)(vb + d * 256 + (((4 * w + g) ^ vswz16(d)) << 4));
+      if (nvk < 32) {  // uniform
+        uint4 vr = __builtin_bit_cast(uint4, vf);
+        vr.x &= vm0; vr.y &= vm1; vr.z &= vm2; vr.w &= vm3;
+        vf = __builtin_bit_cast(bf16x8, vr);
+      }
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[dt], 0, 0, 0);
+    }
+  };
+
+  // ring of two chunks: chunk c + 1 loads while chunk c computes
+  issue(0, 0);
+  for (int c = 0; c < nch; c++) {
+    issue(c + 1, (c + 1) & 1);  // that slot's chunk (c - 1) was finished at the last barrier
+    wait_vm<AT_LPC>();          // this thread's part of chunk c has landed
+    lds_barrier();              // ... and everyone's
+    const unsigned char* kb = lds + (c & 1) * 2 * AT_KB;
+    if (32 * (c * AT_NW + w) < ctx) compute(kb, kb + AT_KB, c);  // keys of this wave exist
+    lds_barrier();  // the slot may be refilled
+  }
+  wait_vm<0>();   // the redundant last issue has landed ...
+  lds_barrier();  // ... in every wave, before the ring is reused
+
+  // combine the waves' (m, l, O) through the idle ring: wave w's O^T at
+  // [w][dt][lane], its m and l per row after them
+  f32x4* xo = (f32x4*)lds;
+  float* xm = (float*)(lds + AT_NW * 8 * 64 * 16);
+  float* xl = xm + AT_NW * 16;
+  const float lsum = wave_sum_groups(l_run);
+#pragma unroll
+  for (int dt = 0; dt < 8; dt++) xo[(w * 8 + dt) * 64 + l] = o[dt];
+  if (g == 0) {
+    xm[w * 16 + c16] = m_run;
+    xl[w * 16 + c16] = lsum;
+  }
+  __syncthreads();
+  float mstar = -INFINITY;
+#pragma unroll
+  for (int ww = 0; ww < AT_NW; ww++) mstar = fmaxf(mstar, xm[ww * 16 + c16]);
+  float wgt[AT_NW];
+  float den = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < AT_NW; ww++) {
+    const float m = xm[ww * 16 + c16];
+    wgt[ww] = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mstar);
+    den += wgt[ww] * xl[ww * 16 + c16];
+  }
+  const float inv = 1.f / den;
+  if (t >= M) return;
+  uint16_t* out = (uint16_t*)a.out;
+  // wave w writes dim tiles w and w + 4 of the tile's rows
+#pragma unroll
+  for (int dt = w; dt < 8; dt += AT_NW) {
+    f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ww = 0; ww < AT_NW; ww++) num += wgt[ww] * xo[(ww * 8 + dt) * 64 + l];
+    const int k = h * A_DH + dt * 16 + 4 * g;
+    const size_t o0 = a.out_mtt ? frag_index(r0 + t, k, a.out_mtt) : (size_t)(r0 + t) * (a.H * A_DH) + k;
+    uint2 pk;
+    pk.x = (uint32_t)f2bf(num[0] * inv) | ((uint32_t)f2bf(num[1] * inv) << 16);
+    pk.y = (uint32_t)f2bf(num[2] * inv) | ((uint32_t)f2bf(num[3] * inv) << 16);
+    *(uint2*)&out[o0] = pk;
+  }
+}
+
 // Row groups of the instance launch_attn_bf16 picks for M rows: 32-row
 // groups from 65 to 128 rows, one workgroup per head otherwise.
 static int attn_row_groups(int M) { return M > 64 && M <= 128 ? (M + 31) / 32 : 1; }
@@ -585,7 +800,21 @@ static void launch_attn_inst(const AttnArgs& a, hipStream_t s) {
                      dim3(NRP * KSPL * 64), 0, s, a);
 }
 
+// Blocks above 32 rows take k_attn_tile (no split, no merge) while the
+// cache rows are at most 1280 keys: there each CU reading the head's whole
+// K/V from L2 costs less than the split kernel's extra launch and merge
+// traffic.  Measured, HBM-cold, us per call (split + merge / k_attn_tile):
+// 32 heads x 121 rows at 550 committed keys 17.4 / 12.4, at 1024 19.8 /
+// 17.1; 40 heads x 81 rows at 1100: 19.5 / 19.0; 64 heads (8 KV heads) x
+// 57 rows at 2100: 20.7 / 25.4.  ctx_stride bounds every length the launch
+// (or a captured step graph) can see.
+bool attn_bf16_tiled(int M, int ctx_stride) { return M > 32 && ctx_stride <= 1280; }
+
 void launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
+  if (attn_bf16_tiled(a.M, a.ctx_stride)) {
+    hipLaunchKernelGGL(k_attn_tile, dim3(a.H, (a.M + 15) / 16, a.nseq), dim3(AT_NW * 64), 0, s, a);
+    return;
+  }
   // 2 key halves and a 2-chunk ring per workgroup; up to 32 rows one row
   // pair (72 KiB of LDS, two workgroups per CU), 33-64 rows two row pairs
   // (80 KiB), 65-128 rows row groups of 32 (measured at 121 rows and 0-1000

@@ -246,6 +246,8 @@ struct AttnArgs {
   int splits;
 };
 void launch_attn_bf16(const AttnArgs& a, hipStream_t s);
+// whether launch_attn_bf16 takes the unsplit per-tile kernel (no partials)
+bool attn_bf16_tiled(int M, int ctx_stride);
 int attn_bf16_splits(int H, int M, int max_ctx);
 size_t attn_bf16_partial_floats(int H, int M, int splits, int dh);
 void launch_attn_f32(const AttnArgs& a, hipStream_t s);
