@@ -1023,10 +1023,12 @@ size_t la_attention_workspace_bytes(int32_t n_heads, int32_t head_dim, int32_t c
   return align_up(rows * head_dim * 4, 256) + align_up(rows * 2 * 4, 256);
 }
 
-la_status la_attention(const void* q, const void* k_cache, const void* vt_cache, void* out,
-                       int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t prefix_len,
-                       int32_t ctx_stride, int32_t W, int32_t N, int32_t G, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+namespace {
+
+// Host-side checks of one kernel-level attention call (no HIP call).
+la_status attention_check(const void* q, const void* k_cache, const void* vt_cache, const void* out,
+                          int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                          int32_t prefix_len, int32_t ctx_stride, int32_t W, int32_t N, int32_t G) {
   if (!q || !k_cache || !vt_cache || !out) return LA_ERR_INVALID_ARG;
   if (n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads || N < 2 || N > 32 || W < 0 || G < 0 ||
       prefix_len < 0 || ctx_stride < 1)
@@ -1035,14 +1037,22 @@ la_status la_attention(const void* q, const void* k_cache, const void* vt_cache,
   const long T = 1 + (long)(W + G) * (N - 1);
   if (T > MAX_ROWS) return LA_ERR_UNSUPPORTED;
   if (ctx_stride % 64 || prefix_len + T > ctx_stride) return LA_ERR_INVALID_ARG;
-  const size_t need = la_attention_workspace_bytes(n_heads, head_dim, ctx_stride, W, N, G);
-  if (!workspace || workspace_bytes < need) return LA_ERR_OUT_OF_CAPACITY;
+  return LA_OK;
+}
+
+// Launch one checked call with the split-KV partials (if the launch uses
+// any) in ws.
+la_status attention_launch(const void* q, const void* k_cache, const void* vt_cache, void* out,
+                           int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                           int32_t prefix_len, int32_t ctx_stride, int32_t W, int32_t N, int32_t G,
+                           void* ws, void* stream) {
+  const int T = 1 + (W + G) * (N - 1);
   AttnArgs aa;
   memset(&aa, 0, sizeof(aa));
-  aa.splits = attn_bf16_splits(n_heads, (int)T, ctx_stride);
+  aa.splits = attn_bf16_splits(n_heads, T, ctx_stride);
   const size_t rows = (size_t)n_heads * aa.splits * ((T + 15) & ~15);
-  aa.part_o = (float*)workspace;
-  aa.part_ml = (float*)((char*)workspace + align_up(rows * head_dim * 4, 256));
+  aa.part_o = (float*)ws;
+  aa.part_ml = (float*)((char*)ws + align_up(rows * head_dim * 4, 256));
   aa.q = q;
   aa.k_cache = k_cache;
   aa.vt_cache = vt_cache;
@@ -1050,8 +1060,8 @@ la_status la_attention(const void* q, const void* k_cache, const void* vt_cache,
   aa.out_mtt = 0;
   aa.st = nullptr;
   aa.L_host = prefix_len;
-  aa.M = (int)T;
-  aa.rps = (int)T;
+  aa.M = T;
+  aa.rps = T;
   aa.nseq = 1;
   aa.kv_seq = 0;
   aa.mode = MODE_STEP;
@@ -1063,6 +1073,21 @@ la_status la_attention(const void* q, const void* k_cache, const void* vt_cache,
   aa.N = N;
   launch_attn_bf16(aa, (hipStream_t)stream);
   return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+}  // namespace
+
+la_status la_attention(const void* q, const void* k_cache, const void* vt_cache, void* out,
+                       int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t prefix_len,
+                       int32_t ctx_stride, int32_t W, int32_t N, int32_t G, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  const la_status st = attention_check(q, k_cache, vt_cache, out, n_heads, n_kv_heads, head_dim,
+                                       prefix_len, ctx_stride, W, N, G);
+  if (st != LA_OK) return st;
+  const size_t need = la_attention_workspace_bytes(n_heads, head_dim, ctx_stride, W, N, G);
+  if (!workspace || workspace_bytes < need) return LA_ERR_OUT_OF_CAPACITY;
+  return attention_launch(q, k_cache, vt_cache, out, n_heads, n_kv_heads, head_dim, prefix_len,
+                          ctx_stride, W, N, G, workspace, stream);
 }
 
 la_status la_sample(const float* logits, int32_t rows, int32_t vocab, float temperature,
