@@ -286,6 +286,27 @@ la_status la_attention(const void *q, const void *k_cache,
                        int32_t N, int32_t G, void *workspace,
                        size_t workspace_bytes, void *stream);
 
+/* The same call for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * no workspace argument; the split-KV partials go to a scratch array the
+ * library holds in device memory, LA_ATTENTION_NOALLOC_SCRATCH_BYTES per
+ * GPU, for the life of the process.  The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine).  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (concurrent
+ * streams, threads) race and must be serialized by the caller; nothing in
+ * the array needs to start at zero.  Arguments, layouts and results as
+ * la_attention.
+ * Errors: as la_attention; LA_ERR_OUT_OF_CAPACITY when the call needs more
+ * than LA_ATTENTION_NOALLOC_SCRATCH_BYTES (la_attention_workspace_bytes
+ * larger), before any HIP call; LA_ERR_HIP if the array's address cannot be
+ * resolved. */
+#define LA_ATTENTION_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+la_status la_attention_noalloc(const void *q, const void *k_cache,
+                               const void *vt_cache, void *out, int32_t n_heads,
+                               int32_t n_kv_heads, int32_t head_dim,
+                               int32_t prefix_len, int32_t ctx_stride, int32_t W,
+                               int32_t N, int32_t G, void *stream);
+
 /* ---- one draw per row on its own ---------------------------------------
  * The draw la_set_sampling describes (temperature > 0), for rows of
  * logits: out[r] = the token drawn from logits[r] with the uniform of

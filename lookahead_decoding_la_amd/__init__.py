@@ -21,6 +21,8 @@ from .build import LIB as _LIB_PATH, build  # noqa: F401
 
 LA_OK, LA_ERR_INVALID_ARG, LA_ERR_STATE = 0, -1, -2
 LA_ERR_OUT_OF_CAPACITY, LA_ERR_HIP, LA_ERR_UNSUPPORTED = -3, -4, -5
+# device scratch of la_attention_noalloc (include/la.h)
+LA_ATTENTION_NOALLOC_SCRATCH_BYTES = 16 << 20
 LA_F32, LA_BF16 = 0, 1
 
 EXPORTS = [
@@ -29,7 +31,7 @@ EXPORTS = [
     "la_status_string", "la_last_error", "la_step_rows", "la_debug_logits",
     "la_debug_block", "la_debug_window", "la_debug_pool",
     "la_debug_pool_insert", "la_debug_kv", "la_debug_state",
-    "la_attention_workspace_bytes", "la_attention", "la_profile_step",
+    "la_attention_workspace_bytes", "la_attention", "la_attention_noalloc", "la_profile_step",
     "la_profile_kernel", "la_seed_pool", "la_prefill_seq", "la_seed_pool_seq",
     "la_debug_pool_insert_seq", "la_set_sampling", "la_sample",
 ]
@@ -95,6 +97,8 @@ def lib():
             "la_attention_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
             "la_attention": (C.c_int, [P, P, P, P, I32, I32, I32, I32, I32, I32, I32,
                                        I32, P, SZ, P]),
+            "la_attention_noalloc": (C.c_int, [P, P, P, P, I32, I32, I32, I32, I32, I32,
+                                               I32, I32, P]),
             "la_profile_step": (C.c_int, [P, pf, pi, C.POINTER(LaStepResult)]),
             "la_profile_kernel": (C.c_int, [P, I32, I32, pf]),
             "la_seed_pool": (C.c_int, [P, pi, I32]),
@@ -369,4 +373,20 @@ def attention(q, k_cache, vt_cache, out, n_heads, n_kv_heads, prefix_len, W, N, 
                         s.cuda_stream)
     if st != LA_OK:
         raise LaError(st, "la_attention: " + L.la_status_string(st).decode())
+    return out
+
+
+def attention_noalloc(q, k_cache, vt_cache, out, n_heads, n_kv_heads, prefix_len, W, N, G,
+                      stream=None):
+    """la_attention_noalloc: as attention(), with the library's own device
+    scratch array instead of a workspace (nothing is allocated)."""
+    import torch
+    L = lib()
+    ctx = int(k_cache.shape[1])
+    s = stream if stream is not None else torch.cuda.current_stream()
+    st = L.la_attention_noalloc(q.data_ptr(), k_cache.data_ptr(), vt_cache.data_ptr(),
+                                out.data_ptr(), n_heads, n_kv_heads, 128, prefix_len, ctx,
+                                W, N, G, s.cuda_stream)
+    if st != LA_OK:
+        raise LaError(st, "la_attention_noalloc: " + L.la_status_string(st).decode())
     return out

@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1088,6 +1089,51 @@ la_status la_attention(const void* q, const void* k_cache, const void* vt_cache,
   if (!workspace || workspace_bytes < need) return LA_ERR_OUT_OF_CAPACITY;
   return attention_launch(q, k_cache, vt_cache, out, n_heads, n_kv_heads, head_dim, prefix_len,
                           ctx_stride, W, N, G, workspace, stream);
+}
+
+// ---- kernel-level attention without a caller workspace -----------------
+// The split-KV partials of la_attention_noalloc live in this file-scope
+// device array: one copy per GPU, held until the process ends.  On the
+// host the array's name is only a stand-in, never a device address: host
+// code takes the address hipGetSymbolAddress gives for the current device,
+// once per device, and passes that.
+static __device__ __align__(256) unsigned char scratch[LA_ATTENTION_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+constexpr int SCRATCH_MAX_DEVICES = 64;
+void* g_scratch_ptr[SCRATCH_MAX_DEVICES];
+
+// This device's copy of `scratch` (resolved on the device's first call).
+la_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_MAX_DEVICES) return LA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LA_OK;
+}
+}  // namespace
+
+la_status la_attention_noalloc(const void* q, const void* k_cache, const void* vt_cache, void* out,
+                               int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                               int32_t prefix_len, int32_t ctx_stride, int32_t W, int32_t N,
+                               int32_t G, void* stream) {
+  la_status st = attention_check(q, k_cache, vt_cache, out, n_heads, n_kv_heads, head_dim,
+                                 prefix_len, ctx_stride, W, N, G);
+  if (st != LA_OK) return st;
+  if (la_attention_workspace_bytes(n_heads, head_dim, ctx_stride, W, N, G) >
+      LA_ATTENTION_NOALLOC_SCRATCH_BYTES)
+    return LA_ERR_OUT_OF_CAPACITY;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != LA_OK) return st;
+  return attention_launch(q, k_cache, vt_cache, out, n_heads, n_kv_heads, head_dim, prefix_len,
+                          ctx_stride, W, N, G, ws, stream);
 }
 
 la_status la_sample(const float* logits, int32_t rows, int32_t vocab, float temperature,
