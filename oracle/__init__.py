@@ -93,6 +93,7 @@ def lib():
             "orc_block_select": (I, [P, I32, D]),
             "orc_set_sampling": (I, [P, C.c_double, I, C.c_double, C.c_uint64]),
             "orc_round_bf16": (C.c_double, [C.c_double]),
+            "orc_rewind": (I, [P, I, C.c_int32]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -223,6 +224,12 @@ class Oracle:
 
     def set_current(self, t: int) -> None:
         lib().orc_set_current(self._h, int(t))
+
+    def rewind(self, L: int, cur: int) -> None:
+        """Back to committed length L with current token cur (window and
+        pool kept)."""
+        if lib().orc_rewind(self._h, int(L), int(cur)):
+            raise ValueError("bad rewind")
 
     def window(self) -> np.ndarray:
         c = self.cfg

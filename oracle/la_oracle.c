@@ -973,6 +973,18 @@ int orc_greedy_next(orc *o, double *logits_out) {
   return t;
 }
 
+/* Rewind to committed length L (0 <= L <= the current length) with current
+ * token cur: cache positions from L on are dropped; window and pool are
+ * kept.  Tests use it to decode ahead with plain decoding and come back.
+ * Returns 0, or -1 for a bad argument. */
+int orc_rewind(orc *o, int L, int32_t cur) {
+  if (L < 0 || L > o->L || cur < 0 || cur >= o->c.vocab) return -1;
+  o->L = L;
+  o->cur = cur;
+  o->has_block = 0;
+  return 0;
+}
+
 /* State inspection. */
 void orc_get_window(const orc *o, int32_t *win) {
   memcpy(win, o->win, sizeof(int32_t) * (size_t)(o->c.N - 1) * o->c.W);
