@@ -52,10 +52,18 @@ def kv_bytes_per_token(cfg) -> int:
 
 
 def gateup_bytes_per_launch(cfg, rows) -> int:
-    """Algorithmic bytes of one fused gate/up launch: both weight matrices,
-    the normalized activations in, the SwiGLU activations out (bf16)."""
+    """Algorithmic bytes of one fused gate/up launch: its share of the
+    step's streamed weights, both weight matrices (the activations it reads
+    and writes are counted apart, gateup_activation_bytes)."""
     e = 2 if cfg.dtype == "bf16" else 4
-    return (2 * cfg.d_ffn * cfg.d_model + rows * cfg.d_model + rows * cfg.d_ffn) * e
+    return 2 * cfg.d_ffn * cfg.d_model * e
+
+
+def gateup_activation_bytes(cfg, rows) -> int:
+    """Activation bytes of one fused gate/up launch: the normalized input
+    rows in and the SwiGLU rows out (bf16)."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    return (rows * cfg.d_model + rows * cfg.d_ffn) * e
 
 
 def traffic_from_profiles(kernel_key: str):
@@ -278,26 +286,62 @@ def sweep_counters(run_dir):
     return out
 
 
-def cpu_baseline(cfg, prompt, win, n_steps=3):
+def cpu_baseline(cfg, dev_w, prompt, win, n_steps=3):
     """Time the CPU oracle (as it stands) on a bounded sample of the same
     workload: the full model and step shape, n_steps lookahead steps after a
     16-token prompt, with G candidates planted under each step's current
-    token so that every step forwards all T rows."""
+    token so that every step forwards all T rows.  The GPU runs the same
+    steps beside it (same prompt, window and planted candidates; the oracle
+    takes the GPU's decisions, so both stay on one path), and every valid
+    row's logits and every decision are compared: the step's parity against
+    the exact oracle, live.  Returns (cpu_baseline, parity)."""
     import oracle
+    import lookahead_decoding_la_amd as la
     P = 16
-    w = lasynth.host_bits(lasynth.make_weights_device(cfg, seed=0))
-    o = oracle.Oracle(cfg, w, P + (n_steps + 1) * cfg.T + 8)
-    o.prefill(prompt[:P], win)
+    w = lasynth.host_bits(dev_w)
+    max_ctx = P + (n_steps + 1) * cfg.T + 8
+    o = oracle.Oracle(cfg, w, max_ctx)
+    dev = la.LookaheadDecoder(cfg, dev_w, max_ctx)
+    fo, lgp = o.prefill(prompt[:P], win, logits=True)
+    fg = dev.prefill(prompt[:P], win)
+    adopted = []
+    if fg != fo:  # a near-tie decided the prefill's token differently
+        v = np.sort(lgp[-1].astype(np.float32))
+        adopted.append(float(v[-1] - v[-2]))
+        o.set_current(fg)
     rng = np.random.default_rng(0)
     secs, emitted = 0.0, 0
+    dmax, sq, ncmp, ndec, tokens_equal = 0.0, 0.0, 0, 0, True
     for _ in range(n_steps):
         for _ in range(cfg.G):
-            o.pool_insert(o.current, rng.integers(0, cfg.vocab, size=cfg.N - 1))
+            tail = rng.integers(0, cfg.vocab, size=cfg.N - 1)
+            dev.debug_pool_insert(o.current, tail)
+            o.pool_insert(o.current, tail)
+        dev.step()
+        lg_g = dev.debug_logits()
+        tok_g, amax_g = dev.debug_block()
         t0 = time.perf_counter()
-        r = o.step()
+        tok, valid, _ = o.block_tokens()
+        lg_o = o.forward_block(tok, valid, keep=True)
+        amax_o = o.block_argmax()
+        r = o.commit(amax_g)
         secs += time.perf_counter() - t0
         emitted += r["n_emitted"]
-    log(f"cpu oracle: {n_steps} steps in {secs:.1f} s ({oracle.max_threads()} threads)")
+        v = valid.astype(bool)
+        tokens_equal = tokens_equal and bool(np.array_equal(tok_g[v], tok[v]))
+        d = lg_g[v].astype(np.float64) - lg_o[v]
+        dmax = max(dmax, float(np.max(np.abs(d))))
+        sq += float(np.sum(d * d))
+        ncmp += d.size
+        for row in np.nonzero(v)[0]:
+            ndec += 1
+            if amax_g[row] != amax_o[row]:
+                z = np.sort(lg_o[row].astype(np.float32))
+                adopted.append(float(z[-1] - z[-2]))
+    log(f"cpu oracle: {n_steps} steps in {secs:.1f} s ({oracle.max_threads()} threads); "
+        f"GPU vs oracle: max|dlogit| {dmax:.4f}, rms {np.sqrt(sq / ncmp):.4f}, "
+        f"{len(adopted)} of {ndec + 1} decisions differ")
+    dev.close()
     del o
     # plain greedy decoding on the same oracle and weights (one row per token)
     g = oracle.Oracle(cfg.with_(W=0, G=0), w, P + 8)
@@ -315,7 +359,7 @@ def cpu_baseline(cfg, prompt, win, n_steps=3):
                              "")
     except OSError:
         pass
-    return {
+    cpu = {
         "value": emitted / secs,
         "unit": "tokens/s",
         "cores": oracle.max_threads(),
@@ -328,6 +372,90 @@ def cpu_baseline(cfg, prompt, win, n_steps=3):
         "nproc": os.cpu_count(),
         "cpu_model": cpu_model,
     }
+    try:
+        with open(os.path.join(ROOT, "tests", "golden", "rounding_bounds.json")) as f:
+            rb = json.load(f).get(cfg.name)
+    except (OSError, ValueError):
+        rb = None
+    parity = {
+        "against": "exact fp64 oracle, same blocks (the cpu_baseline sample: "
+                   f"{n_steps} steps of {cfg.T} rows after a {P}-token prompt)",
+        "max_abs_dlogit": round(dmax, 5),
+        "rms_dlogit": round(float(np.sqrt(sq / ncmp)), 5),
+        "north_star_logit_tol": 0.02,
+        "within_north_star_tol": dmax <= 0.02,
+        "bf16_storage_rounding_only": None if rb is None else
+        {"max_abs_dlogit": round(rb["max_abs_dlogit"], 5), "rms_dlogit": round(rb["rms_dlogit"], 5)},
+        "decisions": ndec + 1,
+        "decisions_differing": len(adopted),
+        "differing_oracle_margins": sorted(round(m, 4) for m in adopted),
+        "block_tokens_equal": tokens_equal,
+    }
+    return cpu, parity
+
+
+def accepting_loop(cfg, dev_w, prompt, win, steps):
+    """The step when candidates are accepted: random-init weights never
+    reproduce their prompt, so the pool is seeded with the model's own
+    output instead.  Run 0 decodes with the pool as la_prefill leaves it;
+    run i + 1 seeds the pool (la_seed_pool) with the tokens every earlier
+    run emitted after the prefill's token.  A run's emitted tokens are its
+    own decisions, and where two runs decided a near-tie differently (a
+    token decided by row 0 in one run is decided by a candidate row in the
+    next, through a different order of the attention sums) both branches
+    stay in the pool, so the runs converge (slowly: a position can be
+    decided by row 0 or by any of the N - 1 candidate rows, each its own
+    order of sums) towards a seeding under which every step finds its
+    continuation and accepts N - 1; at most 16 runs.  Then `steps` steps are
+    timed from that seeding, pipelined as in the main loop: each step
+    accepts, compacts the winner's KV rows and emits up to N tokens."""
+    import lookahead_decoding_la_amd as la
+    import torch
+    n1 = cfg.N - 1
+    need = cfg.N * (steps + 2)
+    max_ctx = cfg.prompt_len + need + 2 * cfg.N + cfg.T + 64
+    dec = la.LookaheadDecoder(cfg, dev_w, max_ctx)
+    seqs, runs = [], 0
+    for runs in range(1, 17):
+        first = dec.prefill(prompt, win)
+        for seq in seqs:
+            dec.seed_pool([first] + seq)
+        out, acc = [], []
+        while len(out) < need:
+            r = dec.step()
+            out += r["tokens"]
+            acc.append(r["accepted"])
+        full = sum(a == n1 for a in acc[:steps])
+        log(f"accepting loop, run {runs}: {len(acc)} steps for {len(out)} tokens, "
+            f"{full} of the first {min(steps, len(acc))} accept {n1}")
+        if full == min(steps, len(acc)) and len(acc) >= steps:
+            break
+        seqs.append(out)
+    first = dec.prefill(prompt, win)
+    for seq in seqs:
+        dec.seed_pool([first] + seq)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    dec.step_submit()
+    emitted, accepted = 0, 0
+    for i in range(steps):
+        if i + 1 < steps:
+            dec.step_submit()
+        r = dec.step_collect()
+        emitted += r["n_emitted"]
+        accepted += r["accepted"]
+    torch.cuda.synchronize()
+    sec = time.perf_counter() - t0
+    dec.close()
+    ms = sec / steps * 1e3
+    log(f"accepting step: {ms:.3f} ms/step, {emitted / steps:.2f} tokens/step, "
+        f"{emitted / sec:.1f} tokens/s")
+    return {"ms_per_step": round(ms, 4), "tokens_per_step": round(emitted / steps, 3),
+            "accepted_per_step": round(accepted / steps, 3),
+            "tokens_per_s": round(emitted / sec, 2), "steps": steps,
+            "seeding_runs": runs,
+            "pool": "seeded (la_seed_pool) with the model's own output, found as a fixpoint "
+                    "of repeated runs; the step's work is that of any accepting step"}
 
 
 def attention_bench(steps, warmup):
@@ -394,6 +522,8 @@ def main():
     ap.add_argument("--config", default="7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-plain", action="store_true")
+    ap.add_argument("--no-accepting", action="store_true",
+                    help="skip the timed loop of accepting steps")
     ap.add_argument("--sweep", action="store_true",
                     help="W = G sweep at N fixed (step ms, kernel classes, GEMM MFMA "
                          "throughput); prints one JSON line")
@@ -524,7 +654,10 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profiles(f"gate_up_{cfg.name}"),
                 "kernel": "k_gemm_dma<8, 2, 1, true, 8> (fused gate/up + SwiGLU)",
-                "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_s * 1e6, 2),
+                "bytes_per_launch": gu_bytes,
+                "bytes": "the launch's streamed weights (both FFN input matrices)",
+                "extra_bytes_per_launch": gateup_activation_bytes(cfg, cfg.T),
+                "avg_launch_us": round(gu_s * 1e6, 2),
                 "avg_launch_us_step_events": round(gu_step * 1e3, 2)}
     # the same step with sampled verification (temperature 0.8, top-k 50,
     # top-p 0.95): the difference is the per-row draws
@@ -560,11 +693,13 @@ def main():
         d0.close()
         log(f"plain 1-token decode: {plain:.3f} ms/step")
 
-    cpu = None
+    accepting = None
+    if not args.no_accepting:
+        accepting = accepting_loop(cfg, dev_w, prompt, win, min(args.steps, 32))
+
+    cpu, parity = None, None
     if not args.no_cpu_baseline:
-        del dev_w
-        torch.cuda.empty_cache()
-        cpu = cpu_baseline(cfg, prompt, win)
+        cpu, parity = cpu_baseline(cfg, dev_w, prompt, win)
 
     per_ms = np.array(per) * 1e3
     out = {
@@ -596,8 +731,10 @@ def main():
         "plain_decode_ms_per_step": None if plain is None else round(plain, 4),
         "lookahead_over_plain_step": None if plain is None else round(ms_step / plain, 4),
         "kernel_ms_per_step": {k: round(v, 4) for k, v in step_ms_by_class.items()},
+        "accepting_step": accepting,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "parity": parity,
     }
     print(json.dumps(out), flush=True)
 
