@@ -1,16 +1,16 @@
 /*
  * la.h — C ABI of the MI355X (gfx950) lookahead decoding library.
  *
- * One call of la_step runs one lookahead decoding step as described in
+ * One call of la_step runs one lookahead decoding step, the method of
  * "Break the Sequential Dependency of LLM Inference Using Lookahead
- * Decoding" (Fu, Bailis, Stoica, Zhang 2024), summary page:
- *   - Summary: decoding is a non-linear system solved by Jacobi iteration; a
- *     lookahead branch keeps a 2D window over recent iterations and produces
- *     many disjoint n-grams per step; the n-grams are cached in a pool; a
- *     verification branch checks pool candidates in the same forward pass,
- *     so the output is exactly that of ordinary (here: greedy) decoding;
- *   - Key points, "Tuning knobs": W = lookahead window, N = n-gram size,
- *     G = verification size; the step forwards 1 + (W + G)(N - 1) rows.
+ * Decoding" (Fu, Bailis, Stoica, Zhang 2024), summary page, sections Summary
+ * and Key points ("Tuning knobs").  In this library's words: a single forward
+ * pass carries the current token, W x (N-1) rows of Jacobi guesses (the
+ * lookahead window, whose diagonals become new n-grams for a per-token
+ * n-gram store) and up to G stored n-grams that start with the current token;
+ * the longest candidate prefix that agrees with the model's own next-token
+ * choices is accepted, so the emitted tokens are those of plain decoding.
+ * A step forwards 1 + (W + G)(N - 1) rows.
  * The model is a LLaMA-style decoder (pre-norm RMSNorm, rotary embedding on
  * adjacent dimension pairs, grouped KV heads, SwiGLU, untied LM head).
  *
@@ -19,8 +19,10 @@
  *     ordinary host memory.  The library never allocates or frees device
  *     memory: the caller passes one workspace of la_workspace_bytes() bytes
  *     and owns the weights, the workspace and the stream; all must outlive
- *     the context.  The library allocates one small pinned host buffer per
- *     context for the step result.
+ *     the context.  The library allocates three small pinned host buffers
+ *     per context (two step-result slots, so that two submitted steps never
+ *     share one, and a staging buffer for prompts, windows and inspection)
+ *     and frees them in la_destroy.
  *   - Every call returns la_status; nothing aborts and no exception crosses
  *     the ABI.  Arguments are validated before any HIP call.  After a HIP
  *     failure the context is poisoned: every later call except la_destroy

@@ -2,12 +2,12 @@
 // RMSNorm, greedy verification with window shift and n-gram pool update, KV
 // compaction, and fills.  (Per-row token selection: la_sample.hip.)
 //
-// Method source: "Break the Sequential Dependency of LLM Inference Using
-// Lookahead Decoding" (summary page).  Summary: the lookahead branch keeps a
-// 2D window over recent Jacobi iterations and yields disjoint n-grams; the
-// n-grams are cached in a pool; a verification branch checks pool candidates
-// in the same forward pass so the output equals ordinary decoding.  Key
-// points, "Tuning knobs": W window, N n-gram size, G verification size.
+// Method: "Break the Sequential Dependency of LLM Inference Using Lookahead
+// Decoding", summary page, Summary and Key points ("Tuning knobs").  Here:
+// the window's column diagonals become new n-grams stored per lead token
+// (at most G each), the stored n-grams that start with the current token are
+// verified inside the step's own forward pass, and the longest agreeing prefix is
+// emitted, so the output is that of plain decoding.
 #include "la_epilogue.h"
 
 namespace la {

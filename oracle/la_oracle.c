@@ -9,11 +9,12 @@
  *
  * Source: "Break the Sequential Dependency of LLM Inference Using Lookahead
  * Decoding" (Fu, Bailis, Stoica, Zhang 2024), summary page.
- *   - Summary: decoding is treated as a non-linear system solved by Jacobi
- *     iteration; a lookahead branch keeps a 2D window over recent iteration
- *     history and yields many disjoint n-grams per step; the n-grams go to a
- *     pool; a verification branch checks pool candidates in the same forward
- *     pass, so the output equals ordinary decoding.
+ *   - Summary (in this file's words): each step guesses several future
+ *     tokens at once by fixed-point (Jacobi) iteration on a window of
+ *     guesses, turns the window's trajectories into n-grams kept in a store
+ *     keyed by their first token, and checks stored n-grams against the
+ *     model's own choices within the same step's forward pass, so the
+ *     emitted tokens are those of one-token-at-a-time decoding.
  *   - Key points, "Tuning knobs": W = lookahead window, N = n-gram size,
  *     G = verification size.
  *   - Key points, "Main limitation": the per-step extra work is (W+G)(N-1)
@@ -604,7 +605,7 @@ int orc_visible(const orc_config *c, int r, int s) {
 }
 
 /* ------------------------------------------------------------------------ */
-/* n-gram pool (reading of "cached in a pool", keyed by lead token with at
+/* n-gram pool (reading of the Summary's n-gram store, keyed by lead token with at
  * most G tails per key): each key holds distinct (N-1)-token tails, oldest
  * first; inserting a tail already present moves it to the newest slot;
  * inserting a new tail into a full list drops the oldest.                  */
