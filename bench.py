@@ -150,6 +150,116 @@ def write_traffic(dirs, config_name):
     print(json.dumps(entry))
 
 
+def _dispatches(run_dir, counter):
+    """Every dispatch of a rocprofv3 csv counter run: (id, kernel name,
+    workgroups, counter value in KiB), in dispatch order."""
+    import csv
+    import glob
+    out = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row["Counter_Name"] != counter:
+                    continue
+                wg = int(row["Grid_Size"]) // max(int(row["Workgroup_Size"]), 1)
+                out[int(row["Dispatch_Id"])] = (row["Kernel_Name"], wg, float(row["Counter_Value"]))
+    return [(i,) + out[i] for i in sorted(out)]
+
+
+def _step_segments(disp):
+    """The dispatches of each step: from a k_assemble to the next one, kept
+    when the segment holds the verification kernel (prefill chunks do not)."""
+    segs, cur = [], None
+    for d in disp:
+        if "k_assemble" in d[1]:
+            cur = []
+            segs.append(cur)
+        if cur is not None:
+            cur.append(d)
+    return [sg for sg in segs if any("k_verify" in d[1] for d in sg)]
+
+
+def _kernel_class(name):
+    """Class of a step dispatch that is not a GEMM (those are told apart by
+    their order in the step)."""
+    for key, cls in (("k_attn", "attention"), ("k_red_qkv", "reduce_qkv"),
+                     ("k_red_resid_scale", "reduce_residual"), ("k_red_resid_norm", "final_norm"),
+                     ("k_select", "select"), ("k_verify", "verify"), ("k_assemble", "assemble"),
+                     ("k_kv_compact", "kv_compact")):
+        if key in name:
+            return cls
+    return "other"
+
+
+def step_traffic(dirs, config_name):
+    """profiles/step_<cfg>_traffic.json and a markdown table from four
+    counter runs: FETCH_SIZE and WRITE_SIZE over `--traffic-steps`, then
+    over the copy probe (calibration).  Per kernel of one step: HBM bytes
+    per dispatch (median over the steps) against its algorithmic bytes."""
+    cfg = lasynth.get_config(config_name)
+    fetch, write = _dispatches(dirs[0], "FETCH_SIZE"), _dispatches(dirs[1], "WRITE_SIZE")
+    cp_f, _ = _counter_kb(dirs[2], "FETCH_SIZE", COPY_RE)
+    cp_w, _ = _counter_kb(dirs[3], "WRITE_SIZE", COPY_RE)
+    sf, sw = COPY_PROBE_BYTES / (cp_f * 1024.0), COPY_PROBE_BYTES / (cp_w * 1024.0)
+    d, f, V = cfg.d_model, cfg.d_ffn, cfg.vocab
+    qd, kvd = cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
+    gemm_alg = {"qkv": (qd + 2 * kvd) * d * 2, "o_proj": d * qd * 2, "gate_up": 2 * f * d * 2,
+                "down": d * f * 2, "lm_head": V * d * 2}
+    per_layer_gemm_order = ["qkv", "o_proj", "gate_up", "down"]
+    steps_f, steps_w = _step_segments(fetch), _step_segments(write)
+    n = min(len(steps_f), len(steps_w))
+    assert n >= 1, "no steps in the counter runs"
+    rows = {}
+    for sf_seg, sw_seg in zip(steps_f[:n], steps_w[:n]):
+        gi = 0
+        for (_, name, wg, fk), (_, name2, _, wk) in zip(sf_seg, sw_seg):
+            if "k_gemm" in name:
+                # the step's GEMMs run in layer order, then the LM head
+                cls = per_layer_gemm_order[gi % 4] if gi < 4 * cfg.n_layers else "lm_head"
+                gi += 1
+            else:
+                cls = _kernel_class(name)
+            r = rows.setdefault((cls, name), {"fetch": [], "write": [], "wg": wg})
+            r["fetch"].append(fk * 1024.0 * sf)
+            r["write"].append(wk * 1024.0 * sw)
+    out = []
+    tot_t, tot_a = 0.0, 0.0
+    kvb = kv_bytes_per_token(cfg) // cfg.n_layers  # per layer and token
+    for (cls, name), r in sorted(rows.items()):
+        per_step = len(r["fetch"]) / n
+        fm, wm = float(np.median(r["fetch"])), float(np.median(r["write"]))
+        alg = gemm_alg.get(cls, 0)
+        if cls == "attention":  # the committed K/V it reads, at the steps' mean length
+            alg = round((cfg.prompt_len + 1 + (n - 1) / 2) * kvb)
+        out.append({"class": cls, "kernel": name, "workgroups": r["wg"],
+                    "dispatches_per_step": per_step, "fetch_bytes": round(fm),
+                    "write_bytes": round(wm), "algorithmic_bytes": alg})
+        tot_t += (fm + wm) * per_step
+        tot_a += alg * per_step
+    res = {"config": cfg.name, "steps": n, "copy_scale_fetch": sf, "copy_scale_write": sw,
+           "kernels": out, "step_traffic_bytes": round(tot_t),
+           "step_weight_bytes": round(tot_a), "kv_bytes_per_layer_and_token": kvb}
+    path = os.path.join(ROOT, "profiles", f"step_{cfg.name}_traffic.json")
+    with open(path, "w") as fh:
+        json.dump(res, fh, indent=1)
+    print(json.dumps({"step_traffic_bytes": res["step_traffic_bytes"],
+                      "step_weight_bytes": res["step_weight_bytes"], "steps": n}))
+
+
+def traffic_steps(cfg, dev_w, prompt, win, k):
+    """A prefill and k plain la_step calls, nothing else (the program the
+    step-traffic counter runs profile)."""
+    import lookahead_decoding_la_amd as la
+    import torch
+    dec = la.LookaheadDecoder(cfg, dev_w, cfg.prompt_len + (k + 2) * cfg.N + cfg.T + 64)
+    dec.prefill(prompt, win)
+    for _ in range(k):
+        dec.step()
+    torch.cuda.synchronize()
+    dec.close()
+    log(f"traffic steps: prefill + {k} steps")
+
+
 SWEEP_WG = (1, 2, 3, 5, 7, 10, 15, 20, 25)
 
 
@@ -536,6 +646,11 @@ def main():
                     help="run only the copy kernel used to calibrate HBM counters")
     ap.add_argument("--attention", action="store_true",
                     help="the kernel-only masked attention workload (one JSON line)")
+    ap.add_argument("--traffic-steps", type=int, metavar="K",
+                    help="run only a prefill and K steps (for counter runs)")
+    ap.add_argument("--step-traffic", nargs=4, metavar="DIR",
+                    help="rocprofv3 csv runs: --traffic-steps FETCH_SIZE, WRITE_SIZE, copy "
+                         "FETCH_SIZE, copy WRITE_SIZE; writes profiles/step_<cfg>_traffic.json")
     ap.add_argument("--write-traffic", nargs=4, metavar="DIR",
                     help="rocprofv3 csv runs: bench FETCH_SIZE, bench WRITE_SIZE, "
                          "copy FETCH_SIZE, copy WRITE_SIZE; writes profiles/traffic.json")
@@ -544,6 +659,9 @@ def main():
     import lasynth
     if args.write_traffic:
         write_traffic(args.write_traffic, args.config)
+        return
+    if args.step_traffic:
+        step_traffic(args.step_traffic, args.config)
         return
     if args.sweep_counters:
         print(json.dumps({"sweep_counters": sweep_counters(args.sweep_counters)}))
@@ -575,6 +693,9 @@ def main():
         out = {"metric": "lookahead step ms vs W = G (N = %d)" % cfg.N, "config": cfg.name,
                "sweep": sweep(cfg, dev_w, prompt, args.steps, args.warmup)}
         print(json.dumps(out), flush=True)
+        return
+    if args.traffic_steps:
+        traffic_steps(cfg, dev_w, prompt, win, args.traffic_steps)
         return
     if args.batch_sweep:
         out = {"metric": "tokens/s vs sequences per step", "config": cfg.name,

@@ -90,3 +90,24 @@ def test_pipelined_batch_equals_step():
             pipe.step_submit()
         got.append(pipe.step_collect())
     assert got == want
+
+
+def test_submit_reserves_capacity_for_steps_in_flight():
+    """A submit assumes each step in flight commits its maximum of N
+    tokens: with room for one step only (prompt + step rows + N - 1 tokens
+    of capacity) the first submit is accepted and the second refused with
+    LA_ERR_OUT_OF_CAPACITY (a host-side check: nothing is launched), and
+    the context keeps working: the step in flight collects normally."""
+    cfg = lasynth.get_config("tiny")
+    p = lasynth.make_prompt(cfg)
+    cap = len(p) + cfg.T + cfg.N - 1
+    d = la.LookaheadDecoder(cfg, la.upload_weights(lasynth.make_weights(cfg)), cap)
+    d.prefill(p, lasynth.make_init_window(cfg, p))
+    d.step_submit()
+    with pytest.raises(la.LaError) as e:
+        d.step_submit()
+    assert e.value.status == la.LA_ERR_OUT_OF_CAPACITY
+    r = d.step_collect()
+    assert 1 <= r["n_emitted"] <= cfg.N and r["kv_len"] == len(p) + r["n_emitted"]
+    kv, _ = d.debug_state()
+    assert kv == r["kv_len"]
