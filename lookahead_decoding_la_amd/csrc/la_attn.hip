@@ -554,10 +554,10 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 // grid (heads x tiles, 256 workgroups at 32 heads x 121 rows) fills the
 // CUs by itself.  K and V^T go through LDS in 128-key chunks
 // (global_load_lds, 1 KiB = 4 whole K rows or 4 whole V^T rows per
-// instruction) in a 2-chunk ring; the NW = 4 waves share every chunk, wave
-// w taking its keys 32 w .. 32 w + 31, and each runs its own online softmax
-// over its keys; (m, l, O) of the four are combined through LDS at the
-// end.  K/V of a head is read by all of its tiles' workgroups: grid x
+// instruction) through a ring of K and V^T slots (below); the NW = 4 waves
+// share every chunk, wave w taking its keys 32 w .. 32 w + 31, and each
+// runs its own online softmax over its keys; (m, l, O) of the four are
+// combined through LDS at the end.  K/V of a head is read by all of its tiles' workgroups: grid x
 // enumerates heads KV head first, so that the tiles of a head, and the
 // query heads of one KV head, share an XCD and its L2.
 constexpr int AT_NW = 4;                 // waves per workgroup
@@ -570,8 +570,15 @@ constexpr int AT_LPC = 2 * AT_CK / 4 / AT_NW;  // 1 KiB loads per thread per chu
 // read touches spread over all 64 banks.
 __device__ inline int vswz16(int d) { return d & 15; }
 
+// LDS ring: three K slots and two V^T slots of one chunk each (160 KiB,
+// all of a CU's LDS).  While chunk c is consumed, K of c + 1 and c + 2 and
+// V^T of c + 1 are in flight (96 KiB), half as much again as a ring of two
+// whole chunks would hold.
+constexpr int AT_KSLOTS = 3, AT_VSLOTS = 2;
+
 __global__ __launch_bounds__(AT_NW * 64) void k_attn_tile(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * 2 * AT_KB];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[(AT_KSLOTS + AT_VSLOTS) * AT_KB];
+  unsigned char* const vring = lds + AT_KSLOTS * AT_KB;
   const int M = a.M;
   const int gq = a.H / a.Hkv;  // query heads per KV head
   const int kvh = blockIdx.x % a.Hkv, h = kvh * gq + blockIdx.x / a.Hkv;
@@ -611,10 +618,8 @@ __global__ __launch_bounds__(AT_NW * 64) void k_attn_tile(AttnArgs a) {
     vdim[q] = 4 * j + (l >> 4);
     vkey[q] = 8 * ((l & 15) ^ vswz16(vdim[q]));
   }
-  auto issue = [&](int c, int b) {
-    c = min(c, nch - 1);  // past the end: the last chunk again, never read
-    unsigned char* kb = lds + b * 2 * AT_KB;
-    unsigned char* vb = kb + AT_KB;
+  auto issue_k = [&](int c) {
+    unsigned char* kb = lds + (c % AT_KSLOTS) * AT_KB;
 #pragma unroll
     for (int q = 0; q < AT_LPC / 2; q++) {
       const int j = w + q * AT_NW;
@@ -622,6 +627,13 @@ __global__ __launch_bounds__(AT_NW * 64) void k_attn_tile(AttnArgs a) {
       __builtin_amdgcn_global_load_lds((const void*)(kc + (size_t)key * A_DH + 8 * kpc[q]),
                                        (__attribute__((address_space(3))) void*)(kb + j * 1024),
                                        16, 0, 0);
+    }
+  };
+  auto issue_v = [&](int c) {
+    unsigned char* vb = vring + (c % AT_VSLOTS) * AT_KB;
+#pragma unroll
+    for (int q = 0; q < AT_LPC / 2; q++) {
+      const int j = w + q * AT_NW;
       const int k0 = min(c * AT_CK + vkey[q], a.ctx_stride - 8);
       __builtin_amdgcn_global_load_lds((const void*)(vc + (size_t)vdim[q] * a.ctx_stride + k0),
                                        (__attribute__((address_space(3))) void*)(vb + j * 1024),
@@ -638,20 +650,36 @@ __global__ __launch_bounds__(AT_NW * 64) void k_attn_tile(AttnArgs a) {
   // of score-tile row c16 in tile kt: key 8 (c16 / 4) + 4 kt + c16 % 4 of
   // the slice, so that the 8 keys a lane holds after QK^T are keys
   // 8 g .. 8 g + 7, the lane's P^T operand and one contiguous V^T piece.
+  // Only a slice that reaches into the block needs the mask and, if it is
+  // the last one, the zeroing of V^T entries past the context; both sit in
+  // one wave-uniform branch that every earlier slice (plain committed
+  // cache) skips.  All K and V^T operands of the slice are read from LDS up
+  // front, so their latency overlaps the MFMAs and the softmax instead of
+  // stalling each pair.
   auto compute = [&](const unsigned char* kb, const unsigned char* vb, int c) {
     const int s = c * AT_NW + w;
-    f32x4 sc[2];
+    bf16x8 kf[2][4];
 #pragma unroll
     for (int kt = 0; kt < 2; kt++) {
-      sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int r = 32 * w + 8 * (c16 >> 2) + 4 * kt + (c16 & 3);
       const unsigned char* kr = kb + r * 256;
       const int sw = kswz(r & 63);
 #pragma unroll
-      for (int ks = 0; ks < 4; ks++) {
-        const bf16x8 kf = *(const bf16x8*)(kr + (((4 * ks + g) ^ sw) << 4));
-        sc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sc[kt], 0, 0, 0);
-      }
+      for (int ks = 0; ks < 4; ks++) kf[kt][ks] = *(const bf16x8*)(kr + (((4 * ks + g) ^ sw) << 4));
+    }
+    bf16x8 vf[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) {
+      const int d = dt * 16 + c16;
+      vf[dt] = *(const bf16x8*)(vb + d * 256 + (((4 * w + g) ^ vswz16(d)) << 4));
+    }
+    f32x4 sc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++) {
+      sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ks++)
+        sc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt][ks], qf[ks], sc[kt], 0, 0, 0);
     }
     if (32 * s + 32 > L) {  // the slice reaches into the block (wave-uniform)
       uint64_t rm0 = 0ull, rm1 = 0ull, rm2 = 0ull, rm3 = 0ull;
@@ -662,6 +690,20 @@ __global__ __launch_bounds__(AT_NW * 64) void k_attn_tile(AttnArgs a) {
 #pragma unroll
         for (int v = 0; v < 4; v++)
           if (!((win >> (4 * kt + v)) & 1ull)) sc[kt][v] = -INFINITY;
+      // Keys past the context (last slice only) have zero probability, but
+      // their V^T entries may be stale memory: zero them so that no NaN
+      // reaches the MFMA.
+      const int kv = ctx - 32 * s - 8 * g;  // valid keys among this lane's 8
+      const uint32_t vm0 = kv >= 2 ? ~0u : (kv == 1 ? 0xffffu : 0u);
+      const uint32_t vm1 = kv >= 4 ? ~0u : (kv == 3 ? 0xffffu : 0u);
+      const uint32_t vm2 = kv >= 6 ? ~0u : (kv == 5 ? 0xffffu : 0u);
+      const uint32_t vm3 = kv >= 8 ? ~0u : (kv == 7 ? 0xffffu : 0u);
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++) {
+        uint4 vr = __builtin_bit_cast(uint4, vf[dt]);
+        vr.x &= vm0; vr.y &= vm1; vr.z &= vm2; vr.w &= vm3;
+        vf[dt] = __builtin_bit_cast(bf16x8, vr);
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -687,40 +729,33 @@ __global__ __launch_bounds__(AT_NW * 64) void k_attn_tile(AttnArgs a) {
         l_run += p;
         pf[4 * kt + v] = (__bf16)p;
       }
-    // Keys past the context (last chunk only) have zero probability, but
-    // their V^T entries may be stale memory: zero them so that no NaN
-    // reaches the MFMA.
-    const int nvk = ctx - 32 * s;
-    const int kv = nvk - 8 * g;  // valid keys among this lane's 8
-    const uint32_t vm0 = kv >= 2 ? ~0u : (kv == 1 ? 0xffffu : 0u);
-    const uint32_t vm1 = kv >= 4 ? ~0u : (kv == 3 ? 0xffffu : 0u);
-    const uint32_t vm2 = kv >= 6 ? ~0u : (kv == 5 ? 0xffffu : 0u);
-    const uint32_t vm3 = kv >= 8 ? ~0u : (kv == 7 ? 0xffffu : 0u);
 #pragma unroll
-    for (int dt = 0; dt < 8; dt++) {
-      const int d = dt * 16 + c16;
-      bf16x8 vf = *(const bf16x8*)(vb + d * 256 + (((4 * w + g) ^ vswz16(d)) << 4));
-      if (nvk < 32) {  // uniform
-        uint4 vr = __builtin_bit_cast(uint4, vf);
-        vr.x &= vm0; vr.y &= vm1; vr.z &= vm2; vr.w &= vm3;
-        vf = __builtin_bit_cast(bf16x8, vr);
-      }
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[dt], 0, 0, 0);
-    }
+    for (int dt = 0; dt < 8; dt++)
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf, o[dt], 0, 0, 0);
   };
 
-  // ring of two chunks: chunk c + 1 loads while chunk c computes
-  issue(0, 0);
+  // Issue order: K0 V0 K1, then per chunk c: V(c+1) K(c+2) (while they
+  // exist).  The slots refilled at chunk c held chunk c - 1, finished at the
+  // last barrier.  Chunk c is complete once V(c) has landed; after V(c) this
+  // thread has at most K(c+1), V(c+1), K(c+2) in flight, 8 loads each.
+  constexpr int G8 = AT_LPC / 2;  // loads per thread per K or V^T chunk
+  issue_k(0);
+  issue_v(0);
+  if (nch > 1) issue_k(1);
   for (int c = 0; c < nch; c++) {
-    issue(c + 1, (c + 1) & 1);  // that slot's chunk (c - 1) was finished at the last barrier
-    wait_vm<AT_LPC>();          // this thread's part of chunk c has landed
-    lds_barrier();              // ... and everyone's
-    const unsigned char* kb = lds + (c & 1) * 2 * AT_KB;
-    if (32 * (c * AT_NW + w) < ctx) compute(kb, kb + AT_KB, c);  // keys of this wave exist
-    lds_barrier();  // the slot may be refilled
+    if (c + 1 < nch) issue_v(c + 1);
+    if (c + 2 < nch) issue_k(c + 2);
+    if (c + 2 < nch)
+      wait_vm<3 * G8>();
+    else if (c + 1 < nch)
+      wait_vm<2 * G8>();
+    else
+      wait_vm<0>();
+    lds_barrier();  // every thread's part of chunk c has landed
+    if (32 * (c * AT_NW + w) < ctx)  // keys of this wave exist
+      compute(lds + (c % AT_KSLOTS) * AT_KB, vring + (c % AT_VSLOTS) * AT_KB, c);
+    lds_barrier();  // chunk c's slots may be refilled (and, after the last, the ring reused)
   }
-  wait_vm<0>();   // the redundant last issue has landed ...
-  lds_barrier();  // ... in every wave, before the ring is reused
 
   // combine the waves' (m, l, O) through the idle ring: wave w's O^T at
   // [w][dt][lane], its m and l per row after them
