@@ -88,6 +88,7 @@ struct la_ctx {
   float *x = nullptr, *logits = nullptr, *rope_cos = nullptr, *rope_sin = nullptr;
   float *gpart = nullptr, *attn_po = nullptr, *attn_pml = nullptr;
   float* ssq = nullptr;  // bf16: per-row partial sums of squares (deferred RMSNorm)
+  float* ssq16 = nullptr;  // bf16, passes of <= 16 rows: [16][d / 16], one per 16 columns
   float* rope_rows = nullptr;  // bf16: per block row cos[64], sin[64]
   int ssn = 1;
   void *xn = nullptr, *ffa = nullptr, *qb = nullptr;  // f32 path: row-major
@@ -221,6 +222,7 @@ size_t carve(la_ctx* c, void* base) {
     c->attn_po = cv.take<float>(rows16 * dh);
     c->attn_pml = cv.take<float>(rows16 * 2);
     c->ssq = cv.take<float>((size_t)c->MR * SSQ_STRIDE);
+    c->ssq16 = cv.take<float>((size_t)16 * (d / 16));
     c->rope_rows = cv.take<float>((size_t)c->MR * 128);
     c->ssn = (d + SSQ_CHUNK - 1) / SSQ_CHUNK;
   } else {
@@ -319,6 +321,82 @@ AttnArgs attn_args(la_ctx* c, int l, const Pass& p) {
   return aa;
 }
 
+// Passes of at most 16 rows (one token tile) take the one-tile GEMMs,
+// whose epilogues replace the K-split reduce kernels.
+bool small_pass(const la_ctx* c, int M) {
+  const la_config& g = c->cfg;
+  const int d = g.d_model, F = g.d_ffn;
+  return gemv_bf16_ok(M, c->qkv_rows, d) && gemv_bf16_ok(M, d, c->qdim) &&
+         gemv_bf16_ok(M, 2 * F, d) && gemv_bf16_ok(M, d, F);
+}
+
+// One launch of layer l's kernel class k (QKV, ATTN, O, GATEUP or DOWN) in
+// a pass of at most 16 rows.  The first layer's QKV reads the sums of
+// squares the assembly wrote (per SSQ_CHUNK columns); every later norm
+// input was written by an O or down epilogue (per 16 columns, ssq16).
+void launch_small(la_ctx* c, const Pass& p, int l, int k, const EpiArgs& ea, hipStream_t s) {
+  const la_config& g = c->cfg;
+  const int d = g.d_model, F = g.d_ffn;
+  const Layer& L = c->layers[l];
+  GemvArgs ga;
+  memset(&ga, 0, sizeof(ga));
+  ga.MTT = c->MTT;
+  ga.M = p.M;
+  ga.eps = g.rms_eps;
+  ga.d_in = d;
+  switch (k) {
+    case LA_PROF_QKV:
+      ga.X = c->xnf;
+      ga.Wp = (const uint16_t*)L.wqkv;
+      ga.K = d;
+      ga.N = c->qkv_rows;
+      ga.ssq = l == 0 ? c->ssq : c->ssq16;
+      ga.ssq_n = l == 0 ? c->ssn : d / 16;
+      ga.ssq_stride = l == 0 ? SSQ_STRIDE : d / 16;
+      ga.ea = ea;
+      launch_gemv_bf16(EPI_QKV, ga, s);
+      break;
+    case LA_PROF_ATTN:
+      launch_attn_bf16(attn_args(c, l, p), s);
+      break;
+    case LA_PROF_O:
+      ga.X = c->of;
+      ga.Wp = (const uint16_t*)L.wo;
+      ga.K = c->qdim;
+      ga.N = d;
+      ga.x = c->x;
+      ga.wn = (const uint16_t*)L.fnorm;
+      ga.xnf = c->xnf;
+      ga.ssq_out = c->ssq16;
+      launch_gemv_bf16(EPI_RESID, ga, s);
+      break;
+    case LA_PROF_GATEUP:
+      ga.X = c->xnf;
+      ga.Wp = (const uint16_t*)L.wgu;
+      ga.K = d;
+      ga.N = 2 * F;
+      ga.ssq = c->ssq16;
+      ga.ssq_n = d / 16;
+      ga.ssq_stride = d / 16;
+      ga.act = c->af;
+      launch_gemv_bf16(EPI_SWIGLU, ga, s);
+      break;
+    default: {  // down; the last layer's next norm is the final one, applied whole afterwards
+      const bool last = l + 1 == g.n_layers;
+      ga.X = c->af;
+      ga.Wp = (const uint16_t*)L.wd;
+      ga.K = F;
+      ga.N = d;
+      ga.x = c->x;
+      ga.wn = last ? nullptr : (const uint16_t*)c->layers[l + 1].anorm;
+      ga.xnf = last ? nullptr : c->xnf;
+      ga.ssq_out = c->ssq16;
+      launch_gemv_bf16(EPI_RESID, ga, s);
+      break;
+    }
+  }
+}
+
 // The decoder over the assembled rows.  bf16: x holds their embeddings and
 // xnf the first layer's normalized input; f32: x only.
 void enqueue_layers(la_ctx* c, const Pass& p, hipStream_t s, Prof* pf = nullptr) {
@@ -337,7 +415,20 @@ void enqueue_layers(la_ctx* c, const Pass& p, hipStream_t s, Prof* pf = nullptr)
     ea.ssn = c->ssn;
     ea.dmodel = d;
     ea.eps = g.rms_eps;
-    if (c->bf16) {
+    if (c->bf16 && small_pass(c, M)) {
+      const uint16_t* next_norm =
+          (const uint16_t*)(l + 1 < g.n_layers ? c->layers[l + 1].anorm : c->final_norm);
+      for (int k = LA_PROF_QKV; k <= LA_PROF_DOWN; k++) {
+        P_BEGIN(k);
+        launch_small(c, p, l, k, ea, s);
+        P_END();
+      }
+      if (l + 1 == g.n_layers) {  // the LM head takes fully normalized rows
+        P_BEGIN(LA_PROF_REDUCE);
+        launch_red_resid_norm(nullptr, 0, d, M, c->x, next_norm, g.rms_eps, c->xnf, c->MTT, s);
+        P_END();
+      }
+    } else if (c->bf16) {
       const uint16_t* next_norm =
           (const uint16_t*)(l + 1 < g.n_layers ? c->layers[l + 1].anorm : c->final_norm);
       P_BEGIN(LA_PROF_QKV);
@@ -414,7 +505,21 @@ void enqueue_layers(la_ctx* c, const Pass& p, hipStream_t s, Prof* pf = nullptr)
 void enqueue_head(la_ctx* c, const Pass& p, hipStream_t s, Prof* pf = nullptr) {
   const la_config& g = c->cfg;
   const int M = p.M;
-  if (c->bf16) {
+  if (c->bf16 && small_pass(c, M) && g.vocab % 16 == 0) {
+    // xnf already holds the final-norm'd rows
+    GemvArgs ga;
+    memset(&ga, 0, sizeof(ga));
+    ga.X = c->xnf;
+    ga.MTT = c->MTT;
+    ga.Wp = (const uint16_t*)c->lm;
+    ga.K = g.d_model;
+    ga.N = g.vocab;
+    ga.M = M;
+    ga.logits = c->logits;
+    P_BEGIN(LA_PROF_LMHEAD);
+    launch_gemv_bf16(EPI_LOGITS, ga, s);
+    P_END();
+  } else if (c->bf16) {
     // xnf already holds the final-norm'd rows
     P_BEGIN(LA_PROF_LMHEAD);
     launch_gemm_bf16(c->xnf, c->MTT, (const uint16_t*)c->lm, g.d_model, g.vocab, M, c->p_lm,
@@ -795,8 +900,18 @@ la_status la_profile_kernel(la_ctx* c, int32_t klass, int32_t reps, float* us_pe
   const hipStream_t s = c->stream;
   // launch i runs layer i % n_layers, so the weights streamed differ from
   // one launch to the next (no help from the last-level cache)
+  const bool small = small_pass(c, M);
   auto launch = [&](int l) {
     const Layer& L = c->layers[l];
+    if (small) {
+      EpiArgs ea = base_epi(c, p);
+      ea.out_act = c->qb;
+      ea.k_cache = layer_k(c, l, p.seq0);
+      ea.vt_cache = layer_v(c, l, p.seq0);
+      ea.rope_rows = c->rope_rows;
+      launch_small(c, p, l, klass, ea, s);
+      return;
+    }
     switch (klass) {
       case LA_PROF_QKV:
         launch_gemm_bf16(c->xnf, c->MTT, (const uint16_t*)L.wqkv, d, c->qkv_rows, M, c->p_qkv,

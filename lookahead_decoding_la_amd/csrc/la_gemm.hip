@@ -785,6 +785,175 @@ void launch_red_swiglu(const float* P, int ks, int F, int M, uint16_t* af, int M
 }
 
 // ---------------------------------------------------------------------------
+// One-tile GEMMs: at most 16 rows (one-token decode, small batches, small
+// lookahead blocks).  The activations of a k-step are then one token tile
+// of which only the valid rows' lanes are loaded (M x 64 bytes against the
+// 1 KiB weight tile), so a workgroup can own a single 16-row weight tile
+// over all of K and still stream nearly pure weights: 256 - 2000
+// workgroups per GEMM without splitting K across workgroups.  The 8 waves
+// of a workgroup take consecutive k ranges, each issuing V_U k-steps of
+// loads before their MFMAs; their accumulators are summed through LDS in
+// wave order (deterministic) and wave 0 applies the epilogue, so there are
+// no fp32 partial sums in memory and no reduce kernel.  The deferred
+// RMSNorm's row scale (QKV, gate/up inputs) comes from partial sums of
+// squares that the producing epilogue wrote per 16 columns (or per 1024
+// columns for the first layer's input), added in a fixed order.
+constexpr int V_NW = 8;  // waves per workgroup
+constexpr int V_U = 8;   // k-steps of loads per wave in flight
+
+// sum over the lanes l, l^16, l^32, l^48 (same token column of a tile)
+__device__ inline float sum_groups(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(V_NW * 64) void k_gemv_bf16(GemvArgs a) {
+  constexpr int NT = EPI == EPI_SWIGLU ? 2 : 1;  // weight tiles per workgroup
+  __shared__ f32x4 red[V_NW][NT][64];
+  __shared__ float invs[16];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int wt = blockIdx.x;
+  const int KS = a.K >> 5;
+  const int k0 = KS * w / V_NW, k1 = KS * (w + 1) / V_NW;
+  const int M = a.M;
+  const bool live = (l & 15) < M;  // this lane's token column holds a row
+  // weight tile wt (SWIGLU: gate tile 2 wt and up tile 2 wt + 1)
+  const uint16_t* wb = a.Wp + (size_t)wt * NT * KS * 512 + l * 8;
+  const uint16_t* xb = a.X + l * 8;
+
+  if constexpr (EPI == EPI_QKV || EPI == EPI_SWIGLU) {
+    // the input rows' 1/rms, tokens w and w + 8; its loads go out ahead
+    // of the weight stream
+    for (int t = w; t < M; t += V_NW) {
+      float sq = 0.f;
+      for (int i = l; i < a.ssq_n; i += 64) sq += a.ssq[(size_t)t * a.ssq_stride + i];
+      for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o);
+      if (l == 0) invs[t] = 1.f / sqrtf(sq / (float)a.d_in + a.eps);
+    }
+  }
+
+  f32x4 acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; j++) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int ks = k0;
+  for (; ks + V_U <= k1; ks += V_U) {
+    bf16x8 wv[NT][V_U], xv[V_U];
+#pragma unroll
+    for (int u = 0; u < V_U; u++)
+#pragma unroll
+      for (int j = 0; j < NT; j++)
+        wv[j][u] = __builtin_nontemporal_load((const bf16x8*)(wb + ((size_t)j * KS + ks + u) * 512));
+#pragma unroll
+    for (int u = 0; u < V_U; u++) xv[u] = bf16x8{};
+    if (live) {
+#pragma unroll
+      for (int u = 0; u < V_U; u++) xv[u] = *(const bf16x8*)(xb + (size_t)(ks + u) * a.MTT * 512);
+    }
+#pragma unroll
+    for (int u = 0; u < V_U; u++)
+#pragma unroll
+      for (int j = 0; j < NT; j++)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[j][u], xv[u], acc[j], 0, 0, 0);
+  }
+  for (; ks < k1; ks++) {
+    bf16x8 wv[NT], xv = bf16x8{};
+#pragma unroll
+    for (int j = 0; j < NT; j++)
+      wv[j] = __builtin_nontemporal_load((const bf16x8*)(wb + ((size_t)j * KS + ks) * 512));
+    if (live) xv = *(const bf16x8*)(xb + (size_t)ks * a.MTT * 512);
+#pragma unroll
+    for (int j = 0; j < NT; j++)
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[j], xv, acc[j], 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < NT; j++) red[w][j][l] = acc[j];
+  __syncthreads();
+  if (w != 0) return;
+
+  // lane l: output rows n = 16 wt + 4 g + i (i = 0..3) of token t
+  f32x4 sum[NT];
+#pragma unroll
+  for (int j = 0; j < NT; j++) {
+    sum[j] = red[0][j][l];
+#pragma unroll
+    for (int ww = 1; ww < V_NW; ww++) sum[j] += red[ww][j][l];
+  }
+  const int t = l & 15, g = l >> 4;
+  const int n = wt * 16 + 4 * g;
+
+  if constexpr (EPI == EPI_LOGITS) {
+    if (t < M) *(f32x4*)&a.logits[(size_t)t * a.N + n] = sum[0];
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    if (t < M) {
+      const float inv = invs[t];
+      const f32x4 gt = sum[0] * inv, u = sum[1] * inv;
+      uint2 pk;
+      pk.x = (uint32_t)f2bf(silu(gt[0]) * u[0]) | ((uint32_t)f2bf(silu(gt[1]) * u[1]) << 16);
+      pk.y = (uint32_t)f2bf(silu(gt[2]) * u[2]) | ((uint32_t)f2bf(silu(gt[3]) * u[3]) << 16);
+      *(uint2*)&a.act[frag_index(t, n, a.MTT)] = pk;
+    }
+  } else if constexpr (EPI == EPI_RESID) {
+    float ss = 0.f;
+    if (t < M) {
+      float* xr = a.x + (size_t)t * a.N + n;
+      const f32x4 v = *(const f32x4*)xr + sum[0];
+      *(f32x4*)xr = v;
+      if (a.xnf) {
+        const uint2 wv = *(const uint2*)(a.wn + n);
+        uint2 pk;
+        pk.x = (uint32_t)f2bf(v[0] * bf2f((uint16_t)wv.x)) | ((uint32_t)f2bf(v[1] * bf2f((uint16_t)(wv.x >> 16))) << 16);
+        pk.y = (uint32_t)f2bf(v[2] * bf2f((uint16_t)wv.y)) | ((uint32_t)f2bf(v[3] * bf2f((uint16_t)(wv.y >> 16))) << 16);
+        *(uint2*)&a.xnf[frag_index(t, n, a.MTT)] = pk;
+      }
+      ss = fmaf(v[0], v[0], fmaf(v[1], v[1], fmaf(v[2], v[2], v[3] * v[3])));
+    }
+    ss = sum_groups(ss);
+    if (g == 0 && t < M) a.ssq_out[(size_t)t * (a.N >> 4) + wt] = ss;
+  } else {  // EPI_QKV: 1/rms, RoPE on q and k, q rows and the KV cache
+    if (t < M) {
+      const EpiArgs& ea = a.ea;
+      const f32x4 v = sum[0] * invs[t];
+      const int b = t / ea.rps, tl = t - b * ea.rps;
+      const int L = ea.st[b].L;
+      if (n < ea.qdim + ea.kvdim) {
+        const int di = (n < ea.qdim ? n : n - ea.qdim) & 127;  // dim within the head
+        const float* cs = ea.rope_rows + (size_t)t * 128 + di / 2;
+        const float c0 = cs[0], c1 = cs[1], s0 = cs[64], s1 = cs[65];
+        uint2 pk;
+        pk.x = (uint32_t)f2bf(v[0] * c0 - v[1] * s0) | ((uint32_t)f2bf(v[0] * s0 + v[1] * c0) << 16);
+        pk.y = (uint32_t)f2bf(v[2] * c1 - v[3] * s1) | ((uint32_t)f2bf(v[2] * s1 + v[3] * c1) << 16);
+        uint16_t* dst;
+        if (n < ea.qdim) {
+          dst = (uint16_t*)ea.out_act + (size_t)t * ea.qdim + n;
+        } else {
+          const int hk = (n - ea.qdim) >> 7;
+          dst = (uint16_t*)ea.k_cache + b * ea.kv_seq + ((size_t)hk * ea.max_ctx + L + tl) * 128 + di;
+        }
+        *(uint2*)dst = pk;
+      } else {
+        const int vv = n - ea.qdim - ea.kvdim, hk = vv >> 7, di = vv & 127;
+        uint16_t* dst = (uint16_t*)ea.vt_cache + b * ea.kv_seq + ((size_t)hk * 128 + di) * ea.max_ctx + L + tl;
+#pragma unroll
+        for (int i = 0; i < 4; i++) dst[(size_t)i * ea.max_ctx] = f2bf(v[i]);
+      }
+    }
+  }
+}
+
+bool gemv_bf16_ok(int M, int N, int K) { return M >= 1 && M <= 16 && N % 32 == 0 && K % 32 == 0; }
+
+void launch_gemv_bf16(int epi, const GemvArgs& a, hipStream_t s) {
+  const dim3 block(V_NW * 64);
+  switch (epi) {
+    case EPI_QKV: hipLaunchKernelGGL(k_gemv_bf16<EPI_QKV>, dim3(a.N / 16), block, 0, s, a); break;
+    case EPI_RESID: hipLaunchKernelGGL(k_gemv_bf16<EPI_RESID>, dim3(a.N / 16), block, 0, s, a); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL(k_gemv_bf16<EPI_SWIGLU>, dim3(a.N / 32), block, 0, s, a); break;
+    default: hipLaunchKernelGGL(k_gemv_bf16<EPI_LOGITS>, dim3(a.N / 16), block, 0, s, a); break;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // repack row-major bf16 weights into A-operand tiles
 
 __global__ void k_repack_bf16(const uint16_t* __restrict__ src, int rows, int K,

@@ -208,6 +208,34 @@ void launch_gemm_bf16(const uint16_t* X, int MTT, const uint16_t* Wp, int K, int
 void launch_gemm_bf16_swiglu(const uint16_t* X, int MTT, const uint16_t* Wp, int K, int N, int M,
                              int J, uint16_t* A, const float* ssq, int ssn, float eps,
                              hipStream_t s);
+// One-tile GEMMs (at most 16 rows: one token tile): a workgroup owns one
+// 16-row weight tile (QKV, O, down, LM head) or one gate/up tile pair over
+// all of K, splits K over its waves, sums them through LDS in wave order
+// and applies the epilogue itself (no partial sums in memory).
+struct GemvArgs {
+  const uint16_t* X;  // input in fragment layout (token tile 0 of each k-step)
+  int MTT;            // token tiles per k-step of X (and of xnf / act)
+  const uint16_t* Wp; // packed weight tiles
+  int K, N, M;        // reduction length, output rows, valid tokens (1..16)
+  // QKV, SWIGLU: deferred RMSNorm of the input rows: partial sums of
+  // squares ssq[t * ssq_stride + i], i < ssq_n, over d_in columns
+  const float* ssq;
+  int ssq_n, ssq_stride, d_in;
+  float eps;
+  // RESID (O, down): x [M][N] += Y; bf16(x * wn) into xnf (fragment layout,
+  // skipped when xnf is NULL) and each 16-column tile's sum of squares of
+  // the new x into ssq_out[t * (N / 16) + tile]
+  float* x;
+  const uint16_t* wn;
+  uint16_t* xnf;
+  float* ssq_out;
+  uint16_t* act;   // SWIGLU: FFN activation (N / 2 wide), fragment layout
+  float* logits;   // LOGITS: [M][N]
+  EpiArgs ea;      // QKV: q rows, the caches, rotary factors per row
+};
+bool gemv_bf16_ok(int M, int N, int K);
+void launch_gemv_bf16(int epi, const GemvArgs& a, hipStream_t s);
+
 // reduce kernels (sum K splits in order + epilogue)
 void launch_red_qkv(const float* P, int ks, int N, int M, const EpiArgs& ea, hipStream_t s);
 // residual add; next GEMM input bf16(x * w) in fragment layout and the
