@@ -321,12 +321,18 @@ AttnArgs attn_args(la_ctx* c, int l, const Pass& p) {
   return aa;
 }
 
-// Passes of at most 16 rows (one token tile) take the one-tile GEMMs,
-// whose epilogues replace the K-split reduce kernels.
+// Passes of at most SMALL_PASS_ROWS rows take the one-tile GEMMs, whose
+// epilogues replace the K-split reduce kernels.  Their activation loads
+// grow with the rows (M x 64 bytes beside each 1 KiB weight tile), so
+// the gain shrinks as the rows grow.  Measured on the 7B shape
+// (same-process A/B, plain batched decode, ms per step, K-split path /
+// one-tile path): 1 row 3.28 / 2.91, 4 rows 3.44 / 3.08, 8 rows 3.49 /
+// 3.30, 12 rows 3.55 / 3.48, 16 rows 3.63 / 3.71.
+constexpr int SMALL_PASS_ROWS = 12;
 bool small_pass(const la_ctx* c, int M) {
   const la_config& g = c->cfg;
   const int d = g.d_model, F = g.d_ffn;
-  return gemv_bf16_ok(M, c->qkv_rows, d) && gemv_bf16_ok(M, d, c->qdim) &&
+  return M <= SMALL_PASS_ROWS && gemv_bf16_ok(M, c->qkv_rows, d) && gemv_bf16_ok(M, d, c->qdim) &&
          gemv_bf16_ok(M, 2 * F, d) && gemv_bf16_ok(M, d, F);
 }
 

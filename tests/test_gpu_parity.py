@@ -75,15 +75,15 @@ BF16 = [
     lasynth.get_config("7b", name="bf16_plain", n_layers=2, d_model=512, n_heads=4,
                        n_kv_heads=4, d_ffn=1408, vocab=2048, prompt_len=64,
                        span_len=8, n_spans=2, W=0, G=0),
-    # a 13-row block (W3 N3 G3): one token tile, so the one-tile GEMMs with
-    # their fused epilogues carry the lookahead step
-    lasynth.get_config("7b", name="bf16_t13", n_layers=2, d_model=512, n_heads=4,
+    # an 11-row block (W2 N3 G3): at most 12 rows, so the one-tile GEMMs
+    # with their fused epilogues carry the lookahead step
+    lasynth.get_config("7b", name="bf16_t11", n_layers=2, d_model=512, n_heads=4,
                        n_kv_heads=4, d_ffn=1408, vocab=2048, prompt_len=64,
-                       span_len=8, n_spans=2, W=3, N=3, G=3),
+                       span_len=8, n_spans=2, W=2, N=3, G=3),
     # a 12-token prompt: the prefill itself is a one-tile pass (causal rows)
-    lasynth.get_config("7b", name="bf16_t13_short_prompt", n_layers=2, d_model=512, n_heads=4,
+    lasynth.get_config("7b", name="bf16_t11_short_prompt", n_layers=2, d_model=512, n_heads=4,
                        n_kv_heads=2, d_ffn=1408, vocab=2048, prompt_len=12,
-                       span_len=4, n_spans=1, W=3, N=3, G=3),
+                       span_len=4, n_spans=1, W=2, N=3, G=3),
     # a wide FFN (1056 gate/up tile pairs, as the 34B shape's 1376: dealt
     # over 256 twelve-wave workgroups) and a 16-way split of the down GEMM;
     # 57-row steps and plain decode
