@@ -321,18 +321,23 @@ AttnArgs attn_args(la_ctx* c, int l, const Pass& p) {
   return aa;
 }
 
-// Passes of at most SMALL_PASS_ROWS rows take the one-tile GEMMs, whose
-// epilogues replace the K-split reduce kernels.  Their activation loads
-// grow with the rows (M x 64 bytes beside each 1 KiB weight tile), so
-// the gain shrinks as the rows grow.  Measured on the 7B shape
-// (same-process A/B, plain batched decode, ms per step, K-split path /
-// one-tile path): 1 row 3.28 / 2.91, 4 rows 3.44 / 3.08, 8 rows 3.49 /
-// 3.30, 12 rows 3.55 / 3.48, 16 rows 3.63 / 3.71.
+// Passes of at most SMALL_PASS_ROWS rows of models up to SMALL_PASS_DMODEL
+// wide take the one-tile GEMMs, whose epilogues replace the K-split reduce
+// kernels.  Their activation loads grow with the rows (M x 64 bytes beside
+// each 1 KiB weight tile), so the gain shrinks as the rows grow.  Measured
+// (same-process A/Bs, ms per step, K-split path / one-tile path): 7B shape,
+// plain batched decode, 1 row 3.28 / 2.91, 4 rows 3.44 / 3.08, 8 rows 3.49
+// / 3.30, 12 rows 3.55 / 3.48, 16 rows 3.63 / 3.71.  On wider models the
+// K-split GEMMs fill the CUs (7B leaves a third of them idle in QKV and
+// gate/up) and stream faster than the one-tile kernel, more than the reduce
+// kernels cost: plain decode 13B shape 5.51 / 5.85, 34B shape 12.0 / 12.6.
 constexpr int SMALL_PASS_ROWS = 12;
+constexpr int SMALL_PASS_DMODEL = 4096;
 bool small_pass(const la_ctx* c, int M) {
   const la_config& g = c->cfg;
   const int d = g.d_model, F = g.d_ffn;
-  return M <= SMALL_PASS_ROWS && gemv_bf16_ok(M, c->qkv_rows, d) && gemv_bf16_ok(M, d, c->qdim) &&
+  return M <= SMALL_PASS_ROWS && d <= SMALL_PASS_DMODEL && gemv_bf16_ok(M, c->qkv_rows, d) &&
+         gemv_bf16_ok(M, d, c->qdim) &&
          gemv_bf16_ok(M, 2 * F, d) && gemv_bf16_ok(M, d, F);
 }
 
