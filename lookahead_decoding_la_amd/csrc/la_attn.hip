@@ -836,14 +836,20 @@ static void launch_attn_inst(const AttnArgs& a, hipStream_t s) {
 }
 
 // Blocks above 32 rows take k_attn_tile (no split, no merge) while the
-// cache rows are at most 1280 keys: there each CU reading the head's whole
+// cache rows are at most 2048 keys: there each CU reading the head's whole
 // K/V from L2 costs less than the split kernel's extra launch and merge
-// traffic.  Measured, HBM-cold, us per call (split + merge / k_attn_tile):
-// 32 heads x 121 rows at 550 committed keys 17.4 / 12.4, at 1024 19.8 /
-// 17.1; 40 heads x 81 rows at 1100: 19.5 / 19.0; 64 heads (8 KV heads) x
-// 57 rows at 2100: 20.7 / 25.4.  ctx_stride bounds every length the launch
-// (or a captured step graph) can see.
-bool attn_bf16_tiled(int M, int ctx_stride) { return M > 32 && ctx_stride <= 1280; }
+// traffic, or little more at the longest contexts the capacity allows
+// (the choice is fixed per launch shape, and a captured step graph serves
+// every length up to ctx_stride).  Measured, HBM-cold / L2-hot, us per call
+// (split + merge against k_attn_tile): 32 heads x 121 rows at 550
+// committed keys 17.4 / 11.1 cold, 1024 keys 15.3 / 15.4 cold and 11.9 /
+// 12.1 hot, 1536 keys 21.0 / 19.9 and 19.2 / 15.7, 2048 keys 22.4 / 24.8
+// and 20.4 / 20.7, 3072 keys 27.1 / 33.8; 40 heads x 81 rows at 1100 16.7
+// / 16.7, 1600 21.1 / 21.5 and 19.5 / 17.5 hot, 2400 24.5 / 28.6; 64 heads
+// (8 KV heads) x 57 rows at 2100 20.6 / 21.3 and 20.6 / 18.8 hot, 4000
+// 30.6 / 38.8.  The 13B-shape step (capacity 1,472 positions) takes 7.44
+// ms with the split kernel and 7.32 ms with this one.
+bool attn_bf16_tiled(int M, int ctx_stride) { return M > 32 && ctx_stride <= 2048; }
 
 void launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   if (attn_bf16_tiled(a.M, a.ctx_stride)) {

@@ -58,6 +58,7 @@ CASES = [
     dict(prefix=300, n_heads=8, n_kv_heads=2, W=3, N=5, G=8),  # 45 rows, grouped KV heads
     dict(prefix=64, n_heads=4, W=4, N=5, G=4),         # 33 rows: a wave's second tile empty
     dict(prefix=700, n_heads=4, W=12, N=5, G=12),      # 97 rows: last group has one tile
+    dict(prefix=1900, n_heads=8, W=10, N=5, G=10),     # 81 rows, cache rows of 1984 keys (per-tile kernel, 16 chunks)
 ]
 
 
