@@ -45,6 +45,12 @@ CASES = [
                         n_kv_heads=4, d_ffn=1408, vocab=2048, span_len=8, n_spans=2,
                         W=0, G=0),
      16, [40, 64, 51], 8),
+    # 40 plain one-token decodes of 8 heads (320 sequence heads): the most
+    # sequences one context takes at one row each below the row cap
+    (lasynth.get_config("7b", name="bf16_plain_b40", n_layers=2, d_model=1024, n_heads=8,
+                        n_kv_heads=8, d_ffn=2816, vocab=4096, span_len=8, n_spans=2,
+                        W=0, G=0),
+     40, [40, 64, 51], 6),
 ]
 
 

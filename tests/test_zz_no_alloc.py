@@ -26,9 +26,9 @@ def _inputs(H, Hkv, prefix, W, N, G, seed):
 
 
 # (heads, KV heads, committed prefix, W, N, G): both use split-KV partials
-# (the first: cache rows above the per-tile kernel's 1280; the second: 13
-# rows); the second is the smaller problem
-CASES = [(32, 32, 1500, 15, 5, 15), (8, 2, 300, 3, 3, 3)]
+# (cache rows above the per-tile kernel's 2048 keys); the second (13 rows,
+# 8 heads) is the smaller problem
+CASES = [(32, 32, 2100, 15, 5, 15), (8, 2, 2100, 3, 3, 3)]
 
 
 def test_noalloc_attention_equals_workspace_attention():
