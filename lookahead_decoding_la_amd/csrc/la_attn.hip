@@ -823,10 +823,6 @@ int attn_bf16_splits(int H, int M, int max_ctx) {
   return eff_splits((max_ctx + M + AKC - 1) / AKC, std::min(A_MAX_SPLITS, cap), M);
 }
 
-size_t attn_bf16_partial_floats(int H, int M, int splits, int dh) {
-  const int rows16 = (M + 15) & ~15;
-  return (size_t)H * splits * rows16 * (dh + 2);
-}
 
 template <int NRP, int KSPL, int NBUF>
 static void launch_attn_inst(const AttnArgs& a, hipStream_t s) {

@@ -33,18 +33,15 @@ constexpr int G_NW = 8;                 // waves per workgroup
 constexpr int G_ROWS = G_NW * 16;       // output rows per workgroup
 constexpr int G_D = 3;                  // weight stages in the ring
 
-// OUT = 0: fp32 partial sums P[kz][t][n]; OUT = 1 (no K split, gate/up
-// packed as alternating 16-row tiles): SwiGLU written to the fragment-layout
-// activation buffer A (FFN width N/2).
-template <int MT, int J, int OUT>
+// Writes fp32 partial sums P[kz][t][n] of K split kz.
+template <int MT, int J>
 __global__ __launch_bounds__(G_NW * 64) void k_gemm_bf16(
     const uint16_t* __restrict__ X, int MTT, const uint16_t* __restrict__ Wp, int K,
-    int ksplit, float* __restrict__ P, int N, int M, uint16_t* __restrict__ A) {
+    int ksplit, float* __restrict__ P, int N, int M) {
   constexpr int NF = J * MT;                       // B fragments per stage
   constexpr int FPW = (NF + G_NW - 1) / G_NW;      // of them loaded per wave
   constexpr int D = G_D;
-  constexpr int NFX = (OUT == 1 && NF < 2 * MT) ? 2 * MT : NF;  // room for the exchange
-  __shared__ bf16x8 xs[2][NFX][64];
+  __shared__ bf16x8 xs[2][NF][64];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int wt = blockIdx.x, kz = blockIdx.y;
   const int KS = K >> 5;
@@ -123,39 +120,12 @@ __global__ __launch_bounds__(G_NW * 64) void k_gemm_bf16(
 #undef LA_MMAS
 
   // lane holds rows n = 16*tile + 4*(l/16) + v of token 16*m + l%16
-  if (OUT == 0) {
-    float* out = P + (size_t)kz * M * N;
-    const int n = (wt * G_NW + w) * 16 + (l >> 4) * 4;
+  float* out = P + (size_t)kz * M * N;
+  const int n = (wt * G_NW + w) * 16 + (l >> 4) * 4;
 #pragma unroll
-    for (int m = 0; m < MT; m++) {
-      const int t = m * 16 + (l & 15);
-      if (t < M) *(f32x4*)&out[(size_t)t * N + n] = acc[m];
-    }
-  } else {
-    // wave 2i holds gate rows, wave 2i+1 the matching up rows (FFN tile
-    // 4*wt + i); the up values pass through LDS
-    static_assert(OUT == 0 || sizeof(xs) >= (G_NW / 2) * MT * 64 * sizeof(f32x4), "LDS exchange");
-    f32x4* ex = (f32x4*)&xs[0][0][0];
-    __syncthreads();
-    if (w & 1) {
-#pragma unroll
-      for (int m = 0; m < MT; m++) ex[((w >> 1) * MT + m) * 64 + l] = acc[m];
-    }
-    __syncthreads();
-    if (!(w & 1)) {
-      const int j = (wt * (G_NW / 2) + (w >> 1)) * 16 + (l >> 4) * 4;
-#pragma unroll
-      for (int m = 0; m < MT; m++) {
-        const int t = m * 16 + (l & 15);
-        if (t >= M) continue;
-        const f32x4 u = ex[((w >> 1) * MT + m) * 64 + l];
-        const size_t o = frag_index(t, j, MTT);
-        uint2 pk;
-        pk.x = (uint32_t)f2bf(silu(acc[m][0]) * u[0]) | ((uint32_t)f2bf(silu(acc[m][1]) * u[1]) << 16);
-        pk.y = (uint32_t)f2bf(silu(acc[m][2]) * u[2]) | ((uint32_t)f2bf(silu(acc[m][3]) * u[3]) << 16);
-        *(uint2*)&A[o] = pk;
-      }
-    }
+  for (int m = 0; m < MT; m++) {
+    const int t = m * 16 + (l & 15);
+    if (t < M) *(f32x4*)&out[(size_t)t * N + n] = acc[m];
   }
 }
 
@@ -336,8 +306,6 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_dma(
   }
 }
 
-bool gemm_bf16_shape_ok(int N, int K) { return N % G_ROWS == 0 && K % 32 == 0; }
-
 // K split of a plain GEMM for a step of `rows` rows, with at least 6
 // k-steps per split.
 //  - From 4 token tiles on (the LDS-direct kernel, every workgroup loading
@@ -369,13 +337,13 @@ GemmPlan gemm_bf16_plan(int N, int K, int rows) {
   return p;
 }
 
-template <int J, int OUT>
+template <int J>
 static void launch_j(int MT, dim3 grid, const uint16_t* X, int MTT, const uint16_t* Wp, int K,
-                     int ks, float* P, int N, int M, uint16_t* A, hipStream_t s) {
-#define LA_GEMM_CASE(mt)                                                                        \
-  case mt:                                                                                      \
-    hipLaunchKernelGGL((k_gemm_bf16<mt, J, OUT>), grid, dim3(G_NW * 64), 0, s, X, MTT, Wp, K, ks, \
-                       P, N, M, A);                                                             \
+                     int ks, float* P, int N, int M, hipStream_t s) {
+#define LA_GEMM_CASE(mt)                                                                     \
+  case mt:                                                                                   \
+    hipLaunchKernelGGL((k_gemm_bf16<mt, J>), grid, dim3(G_NW * 64), 0, s, X, MTT, Wp, K, ks, \
+                       P, N, M);                                                             \
     break;
   switch (MT) {
     LA_GEMM_CASE(1) LA_GEMM_CASE(2) LA_GEMM_CASE(3) LA_GEMM_CASE(4)
@@ -420,8 +388,8 @@ void launch_gemm_bf16(const uint16_t* X, int MTT, const uint16_t* Wp, int K, int
     else launch_dma_part<1>(MT, grid, X, MTT, Wp, K, plan.ksplit, P, N, M, s);
     return;
   }
-  if (plan.J == 2) launch_j<2, 0>(MT, grid, X, MTT, Wp, K, plan.ksplit, P, N, M, nullptr, s);
-  else launch_j<1, 0>(MT, grid, X, MTT, Wp, K, plan.ksplit, P, N, M, nullptr, s);
+  if (plan.J == 2) launch_j<2>(MT, grid, X, MTT, Wp, K, plan.ksplit, P, N, M, s);
+  else launch_j<1>(MT, grid, X, MTT, Wp, K, plan.ksplit, P, N, M, s);
 }
 
 template <int J, int NW>
@@ -726,30 +694,6 @@ __global__ __launch_bounds__(512) void k_red_resid_norm(const float* __restrict_
   }
 }
 
-// SwiGLU of the fused gate/up output (16-row tiles alternate gate, up)
-__global__ __launch_bounds__(256) void k_red_swiglu(const float* __restrict__ P, int ks, int F,
-                                                    int M, uint16_t* __restrict__ af, int MTT) {
-  const int t = blockIdx.y, N = 2 * F;
-  const int j = (blockIdx.x * 256 + threadIdx.x) * 8;
-  if (j >= F) return;
-  const int cg = (j >> 4) * 32 + (j & 15);
-  float g[8], u[8], p[8];
-  load8(P + (size_t)t * N + cg, g);
-  load8(P + (size_t)t * N + cg + 16, u);
-  for (int z = 1; z < ks; z++) {
-    const float* pr = P + ((size_t)z * M + t) * N;
-    load8(pr + cg, p);
-#pragma unroll
-    for (int e = 0; e < 8; e++) g[e] += p[e];
-    load8(pr + cg + 16, p);
-#pragma unroll
-    for (int e = 0; e < 8; e++) u[e] += p[e];
-  }
-#pragma unroll
-  for (int e = 0; e < 8; e++) g[e] = silu(g[e]) * u[e];
-  *(uint4*)&af[frag_index(t, j, MTT)] = pack8(g);
-}
-
 void launch_red_qkv(const float* P, int ks, int N, int M, const EpiArgs& ea, hipStream_t s) {
   const dim3 grid(N / 128, (M + RQ_TOK - 1) / RQ_TOK);
   if (ks == 1) hipLaunchKernelGGL(k_red_qkv<1>, grid, dim3(256), 0, s, P, ks, N, M, ea);
@@ -777,11 +721,6 @@ void launch_red_resid_scale(const float* P, int ks, int d, int M, float* x, cons
 void launch_red_resid_norm(const float* P, int ks, int d, int M, float* x, const uint16_t* w,
                            float eps, uint16_t* xnf, int MTT, hipStream_t s) {
   hipLaunchKernelGGL(k_red_resid_norm, dim3(M), dim3(512), 0, s, P, ks, d, M, x, w, eps, xnf, MTT);
-}
-void launch_red_swiglu(const float* P, int ks, int F, int M, uint16_t* af, int MTT,
-                       hipStream_t s) {
-  hipLaunchKernelGGL(k_red_swiglu, dim3((F / 8 + 255) / 256, M), dim3(256), 0, s, P, ks, F, M, af,
-                     MTT);
 }
 
 // ---------------------------------------------------------------------------

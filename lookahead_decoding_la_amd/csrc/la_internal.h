@@ -199,7 +199,6 @@ struct GemmPlan {
   int ksplit;  // K splits (workgroups per 128-row tile)
   int J;       // k-steps per pipeline stage
 };
-bool gemm_bf16_shape_ok(int N, int K);
 GemmPlan gemm_bf16_plan(int N, int K, int rows);
 void launch_gemm_bf16(const uint16_t* X, int MTT, const uint16_t* Wp, int K, int N, int M,
                       const GemmPlan& plan, float* P, hipStream_t s);
@@ -245,8 +244,6 @@ void launch_red_resid_scale(const float* P, int ks, int d, int M, float* x, cons
                             uint16_t* xnf, int MTT, float* ssq, hipStream_t s);
 void launch_red_resid_norm(const float* P, int ks, int d, int M, float* x, const uint16_t* w,
                            float eps, uint16_t* xnf, int MTT, hipStream_t s);
-void launch_red_swiglu(const float* P, int ks, int F, int M, uint16_t* af, int MTT,
-                       hipStream_t s);
 
 // fp32 path (small models): Y = X W^T with W row-major [N][K] (two
 // matrices for SWIGLU: W2 is the up projection).
@@ -277,7 +274,6 @@ void launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 // whether launch_attn_bf16 takes the unsplit per-tile kernel (no partials)
 bool attn_bf16_tiled(int M, int ctx_stride);
 int attn_bf16_splits(int H, int M, int max_ctx);
-size_t attn_bf16_partial_floats(int H, int M, int splits, int dh);
 void launch_attn_f32(const AttnArgs& a, hipStream_t s);
 
 // small kernels
