@@ -1,6 +1,6 @@
-// Output-side helpers shared by the fp32 GEMM (direct epilogues) and the
-// bf16 reduce kernels: RoPE + q / KV-cache stores, residual add, SwiGLU,
-// and the MFMA fragment layout of bf16 activations.
+// Output-side helpers of the GEMMs and their epilogues: the MFMA fragment
+// layout of bf16 activations, SiLU, and the fp32 GEMM's fused-QKV epilogue
+// (RoPE + q / KV-cache stores).
 #pragma once
 
 #include "la_internal.h"

@@ -6,23 +6,26 @@
 // weight byte feeds ~121 multiply-adds: still under the MI355X bf16 ridge,
 // so the kernel is built to stream weights while MFMA works on the side.
 //
-// bf16 kernel (gfx950, wave64, v_mfma_f32_16x16x32_bf16):
+// bf16 kernels (gfx950, wave64, v_mfma_f32_16x16x32_bf16), chosen by the
+// pass's rows:
 //   - A operand = weights, pre-packed in 16-row x 32-k tiles so one wave
-//     load is 1 KiB contiguous;
-//   - B operand = activations, stored by their producers in the fragment
-//     layout (la_epilogue.h) so one fragment is 1 KiB contiguous;
-//   - a workgroup of 8 waves owns 128 output rows (one 16-row tile per
-//     wave); all waves walk the same k-steps, so each activation fragment
-//     is fetched once per workgroup and shared through an LDS ring (the
-//     per-wave alternative makes L1->L2 traffic several times the weight
-//     traffic);
-//   - a ring of weight stages in VGPRs keeps several stages in flight; the
-//     order of loads and MFMAs is pinned so loads of later stages stay
-//     outstanding while a stage computes;
+//     load is 1 KiB contiguous; B operand = activations, stored by their
+//     producers in the fragment layout (la_epilogue.h) so one fragment is
+//     1 KiB contiguous;
+//   - k_gemm_dma (4 or more token tiles): a workgroup of 8 (12) waves owns
+//     128 (192) output rows, one 16-row tile per wave; all waves walk the
+//     same k-steps, so each activation fragment is fetched once per
+//     workgroup; weights and fragments go straight into an LDS ring
+//     (global_load_lds), several stages deep;
+//   - k_gemm_bf16 (2-3 token tiles): the same workgroup shape with a ring of
+//     weight stages in VGPRs and the fragments shared through LDS;
 //   - when the row tiles alone cannot fill 256 CUs, K is split across
 //     workgroups; each split writes fp32 partial sums and a reduce kernel
 //     (which also applies the epilogue) adds them in split order, so
-//     results are deterministic and no workgroup waits on another.
+//     results are deterministic and no workgroup waits on another;
+//   - k_gemv_bf16 (at most 12 rows, one token tile): one workgroup per
+//     16-row weight tile over all of K, its waves summed through LDS, the
+//     epilogue fused: no partial sums and no reduce kernel.
 #include <algorithm>
 
 #include "la_epilogue.h"
