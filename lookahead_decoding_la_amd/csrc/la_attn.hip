@@ -618,8 +618,27 @@ __global__ __launch_bounds__(AT_NW * 64) void k_attn_tile(AttnArgs a) {
     vdim[q] = 4 * j + (l >> 4);
     vkey[q] = 8 * ((l & 15) ^ vswz16(vdim[q]));
   }
+  // A chunk that lies wholly inside the cache row (every one but possibly
+  // the last) is loaded from a scalar chunk base plus fixed 32-bit lane
+  // offsets (the cache rows of this kernel hold at most 2048 keys, so the
+  // offsets fit), which leaves no per-load address arithmetic on the VALU.
+  uint32_t koff[AT_LPC / 2], voff[AT_LPC / 2];
+#pragma unroll
+  for (int q = 0; q < AT_LPC / 2; q++) {
+    koff[q] = (uint32_t)(krow[q] * A_DH + 8 * kpc[q]) * 2u;
+    voff[q] = (uint32_t)(vdim[q] * a.ctx_stride + vkey[q]) * 2u;
+  }
   auto issue_k = [&](int c) {
     unsigned char* kb = lds + (c % AT_KSLOTS) * AT_KB;
+    if ((c + 1) * AT_CK <= a.ctx_stride) {  // wave-uniform
+      const char* base = (const char*)kc + (size_t)c * (AT_CK * A_DH * 2);
+#pragma unroll
+      for (int q = 0; q < AT_LPC / 2; q++)
+        __builtin_amdgcn_global_load_lds((const void*)(base + koff[q]),
+                                         (__attribute__((address_space(3))) void*)(kb + (w + q * AT_NW) * 1024),
+                                         16, 0, 0);
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < AT_LPC / 2; q++) {
       const int j = w + q * AT_NW;
@@ -631,6 +650,15 @@ __global__ __launch_bounds__(AT_NW * 64) void k_attn_tile(AttnArgs a) {
   };
   auto issue_v = [&](int c) {
     unsigned char* vb = vring + (c % AT_VSLOTS) * AT_KB;
+    if ((c + 1) * AT_CK <= a.ctx_stride) {  // wave-uniform
+      const char* base = (const char*)vc + (size_t)c * (AT_CK * 2);
+#pragma unroll
+      for (int q = 0; q < AT_LPC / 2; q++)
+        __builtin_amdgcn_global_load_lds((const void*)(base + voff[q]),
+                                         (__attribute__((address_space(3))) void*)(vb + (w + q * AT_NW) * 1024),
+                                         16, 0, 0);
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < AT_LPC / 2; q++) {
       const int j = w + q * AT_NW;
