@@ -45,6 +45,17 @@ CASES = [
                         n_kv_heads=4, d_ffn=1408, vocab=2048, span_len=8, n_spans=2,
                         W=0, G=0),
      16, [40, 64, 51], 8),
+    # passes of at most 12 rows take the one-tile GEMMs, whose QKV epilogue
+    # places each row's K/V in its own sequence's cache: 8 one-row
+    # sequences, and 2 sequences of 5-row lookahead blocks (W1 N3 G1)
+    (lasynth.get_config("7b", name="bf16_plain_b8_one_tile", n_layers=2, d_model=512, n_heads=4,
+                        n_kv_heads=2, d_ffn=1408, vocab=2048, span_len=8, n_spans=2,
+                        W=0, G=0),
+     8, [40, 64, 51], 8),
+    (lasynth.get_config("7b", name="bf16_t5_b2_one_tile", n_layers=2, d_model=512, n_heads=4,
+                        n_kv_heads=4, d_ffn=1408, vocab=2048, span_len=8, n_spans=2,
+                        W=1, N=3, G=1),
+     2, [64, 45], 10),
     # 40 plain one-token decodes of 8 heads (320 sequence heads): the most
     # sequences one context takes at one row each below the row cap
     (lasynth.get_config("7b", name="bf16_plain_b40", n_layers=2, d_model=1024, n_heads=8,
