@@ -60,6 +60,8 @@ CASES = [
     dict(prefix=700, n_heads=4, W=12, N=5, G=12),      # 97 rows: last group has one tile
     dict(prefix=1900, n_heads=8, W=10, N=5, G=10),     # 81 rows, cache rows of 1984 keys (per-tile kernel, 16 chunks)
     dict(prefix=2100, W=3, N=4, G=2),                  # 16 rows at 2100 committed keys: split kernel + merge
+    dict(prefix=2100, n_heads=4, W=12, N=5, G=12),     # 97 rows above 2048 keys: split, 32-row groups
+    dict(prefix=2100, n_heads=2, W=25, N=5, G=25),     # 201 rows above 2048 keys: split, one 128-row group per head
 ]
 
 

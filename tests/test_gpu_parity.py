@@ -93,7 +93,14 @@ BF16 = [
     lasynth.get_config("34b", name="bf16_wide_ffn_plain", n_layers=1, d_model=256, n_heads=2,
                        n_kv_heads=2, d_ffn=16896, vocab=1024, prompt_len=96,
                        span_len=8, n_spans=2, W=0, G=0),
+    # cache rows above 2048 keys (capacity LONG_CTX): the split attention for
+    # the 128- and 44-row causal prefill chunks of a 300-token prompt and for
+    # the 57-row steps
+    lasynth.get_config("34b", name="bf16_long_ctx_w7", n_layers=1, d_model=256, n_heads=2,
+                       n_kv_heads=2, d_ffn=704, vocab=1024, prompt_len=300,
+                       span_len=16, n_spans=4),
 ]
+LONG_CTX = {"bf16_long_ctx_w7": 2304}
 
 
 @pytest.mark.parametrize("cfg", BF16, ids=lambda c: c.name)
@@ -102,7 +109,7 @@ def test_bf16_lockstep(cfg):
     p = lasynth.make_prompt(cfg)
     win = lasynth.make_init_window(cfg, p) if cfg.W else None
     log(f"[bf16 lockstep] {cfg.name} T={cfg.T}")
-    ls = Lockstep(cfg, w, 1024, logit_tol=2e-2)
+    ls = Lockstep(cfg, w, LONG_CTX.get(cfg.name, 1024), logit_tol=2e-2)
     ls.run(p, win, n_steps=10)
     ls.compare_kv(3e-2)
     log(f"  steps={len(ls.steps)} max|dlogit|={ls.max_diff:.2e} ties={ls.ties}")
