@@ -5,10 +5,11 @@ rows per step) and the 34B shape with grouped KV heads (48 layers, d 8192,
 64 query / 8 KV heads, FFN 22016, W7 N5 G7: 57 rows; about 68 GB of bf16
 weights).
 
-- Lockstep with the exact oracle: a 32-token prompt, the pool seeded with
-  the oracle's own greedy continuation, two lookahead steps (the first
-  accepts it), every valid row's logits and decisions, the result, the
-  window and the pool.
+- Lockstep with the exact oracle, in the launch shapes bench.py times (its
+  default capacity): a 32-token prompt, the pool seeded with the oracle's
+  own greedy continuation, two lookahead steps (the first accepts it),
+  every valid row's logits and decisions, the result, the window and the
+  pool.
 - The lookahead output equals plain one-token greedy decoding (both on the
   GPU; 128 generated tokens after a 128-token prompt for 13B, 64 after 64
   for 34B, so that the oracle can check the first divergence): where the
@@ -32,6 +33,11 @@ from lockstep import Lockstep, log, margin
 pytestmark = pytest.mark.gpu
 
 PLAIN_RUN = {"13b": (128, 128), "34b": (64, 64)}  # prompt tokens, generated tokens
+
+# The capacity bench.py gives these shapes by default (prompt + 105 N + T + 64
+# positions): the lockstep runs the launch shapes the benchmark times (at
+# 34B, cache rows above 2048 keys, so the split attention kernel).
+BENCH_CAPACITY = {"13b": 1024 + 105 * 5 + 81 + 64, "34b": 2048 + 105 * 5 + 57 + 64}
 
 
 @pytest.fixture(scope="module", params=["13b", "34b"])
@@ -62,7 +68,7 @@ def test_full_size_lockstep_with_oracle(big):
     c32 = cfg.with_(prompt_len=32, n_spans=1, span_len=8, span_repeats=2)
     prompt = [int(x) for x in lasynth.make_prompt(c32)]
     win = lasynth.make_init_window(cfg, np.array(prompt))
-    ls = Lockstep(cfg, _host(big), 128 + 3 * cfg.T, logit_tol=max_tol, tie_margin=dmargin,
+    ls = Lockstep(cfg, _host(big), BENCH_CAPACITY[cfg.name], logit_tol=max_tol, tie_margin=dmargin,
                   dev_weights=dev_w)
     first = ls.prefill(prompt, win)
     cont = [ls.orc.greedy_next() for _ in range(cfg.N - 1)]
