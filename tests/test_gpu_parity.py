@@ -93,6 +93,15 @@ BF16 = [
     lasynth.get_config("34b", name="bf16_wide_ffn_plain", n_layers=1, d_model=256, n_heads=2,
                        n_kv_heads=2, d_ffn=16896, vocab=1024, prompt_len=96,
                        span_len=8, n_spans=2, W=0, G=0),
+    # N = 2 (a window of one level, one-token candidates), 17 rows: the
+    # register-ring GEMMs (two token tiles)
+    lasynth.get_config("7b", name="bf16_n2_w8", n_layers=2, d_model=512, n_heads=4,
+                       n_kv_heads=4, d_ffn=1408, vocab=2048, prompt_len=64,
+                       span_len=8, n_spans=2, W=8, N=2, G=8),
+    # a one-token prompt (a one-row causal prefill), then 9-row steps
+    lasynth.get_config("7b", name="bf16_prompt1_n2", n_layers=2, d_model=512, n_heads=4,
+                       n_kv_heads=4, d_ffn=1408, vocab=2048, prompt_len=1,
+                       span_len=1, n_spans=0, W=4, N=2, G=4),
     # cache rows above 2048 keys (capacity LONG_CTX): the split attention for
     # the 128- and 44-row causal prefill chunks of a 300-token prompt and for
     # the 57-row steps
