@@ -882,7 +882,182 @@ static void launch_attn_inst(const AttnArgs& a, hipStream_t s) {
 // 1024-token prompt, 1 row: attention 0.60 / 0.74 ms per step.
 bool attn_bf16_tiled(int M, int ctx_stride) { return M > 32 && ctx_stride <= 2048; }
 
+// ---------------------------------------------------------------------------
+// One-row blocks (plain decode, batches of one-row sequences): the row sees
+// every committed key and itself (keys 0 .. L).  A workgroup takes one
+// (head, key split, sequence); its NW waves take 32-key blocks of the
+// split's range in turn, loading K and V^T straight into registers (the
+// next block's loads go out before the current block computes), so the
+// workgroup needs LDS only for its final combine and several fit on a CU.
+//
+// Scores: S^T = K Q^T on 16x16x32 MFMAs, the query in every column (all 16
+// columns equal), two 16-key tiles per block.  Tile u's MFMA row r holds key
+// 8 (r / 4) + 4 u + r % 4, so the lane with rows 4g .. 4g+3 ends up with
+// the block's keys 8g .. 8g+7 over its two tiles: exactly the key (k) range
+// that lane supplies to a 16x16x32 MFMA.  Values: O^T += V^T P^T on those
+// MFMAs, each lane reading 16 contiguous bytes of a V^T row (keys 8g ..
+// 8g+7) and feeding its own eight probabilities as P^T.  Lazy online
+// softmax per wave; the waves' (m, l, O) combine in LDS in wave order, and
+// a split's result goes either to the output (one split) or to the partial
+// buffers that k_attn_merge combines (the split kernel's format and split
+// count, so the merge is shared).
+//
+// Bounds: a block starts at a multiple of 32 below the context, and the
+// cache row (ctx_stride, a multiple of 32) holds the whole block.
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void k_attn_row(AttnArgs a) {
+  __shared__ float xo[NW][A_DH];
+  __shared__ float xm[NW], xl[NW];
+  const int gq = a.H / a.Hkv;  // query heads per KV head
+  // the gq heads of a KV head sit Hkv apart in the grid: with Hkv a
+  // multiple of 8 their workgroups share an XCD (and its L2)
+  const int kvh = blockIdx.x % a.Hkv, h = kvh * gq + blockIdx.x / a.Hkv;
+  const int sp = blockIdx.y, sq = blockIdx.z;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+  const int g = l >> 4, c16 = l & 15;
+  const int r = sq * a.rps;  // the sequence's row in q and out
+  const int L = a.st ? *(const __attribute__((address_space(4))) int32_t*)&a.st[sq].L : a.L_host;
+  const int ctx = L + 1;
+  const int S = eff_splits((ctx + AKC - 1) / AKC, a.splits, 1);
+  if (sp >= S) return;  // a split this length does not use (uniform)
+  const float sl2 = LOG2E / sqrtf((float)A_DH);
+
+  bf16x8 qf[4];  // Q^T (B operand): the row's query in every column
+  {
+    const uint16_t* qp = (const uint16_t*)a.q + (size_t)r * (a.H * A_DH) + h * A_DH + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) qf[ks] = *(const bf16x8*)(qp + 32 * ks);
+  }
+  const uint16_t* kc = (const uint16_t*)a.k_cache + sq * a.kv_seq + (size_t)kvh * a.ctx_stride * A_DH;
+  const uint16_t* vc = (const uint16_t*)a.vt_cache + sq * a.kv_seq + (size_t)kvh * A_DH * a.ctx_stride;
+  const int nblk = (ctx + 31) / 32;  // S <= nblk: every split holds a block
+  const int bs0 = nblk * sp / S, bs1 = nblk * (sp + 1) / S;
+
+  // this lane's K row of tile u and its V^T rows, relative to the block
+  const int krow = 8 * (c16 >> 2) + (c16 & 3);
+  auto load = [&](bf16x8 (&kf)[2][4], bf16x8 (&vf)[8], int b) {
+    const uint16_t* kb = kc + (size_t)(32 * b + krow) * A_DH + 8 * g;
+#pragma unroll
+    for (int u = 0; u < 2; u++)
+#pragma unroll
+      for (int ks = 0; ks < 4; ks++) kf[u][ks] = *(const bf16x8*)(kb + 4 * u * A_DH + 32 * ks);
+    const uint16_t* vb = vc + (size_t)c16 * a.ctx_stride + 32 * b + 8 * g;
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) vf[dt] = *(const bf16x8*)(vb + (size_t)(16 * dt) * a.ctx_stride);
+  };
+  f32x4 o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; dt++) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  auto compute = [&](const bf16x8 (&kf)[2][4], bf16x8 (&vf)[8], int b) {
+    f32x4 sc[2];
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      sc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ks++)
+        sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u][ks], qf[ks], sc[u], 0, 0, 0);
+    }
+    // sc[u][i]: key 32 b + 8 g + 4 u + i
+    if (32 * b + 32 > ctx) {  // the last block (wave-uniform)
+      const int kv = ctx - 32 * b - 8 * g;  // valid keys among this lane's 8
+#pragma unroll
+      for (int j = 0; j < 8; j++)
+        if (j >= kv) sc[j >> 2][j & 3] = -INFINITY;
+      // zero the values of keys past the context (stale cache contents
+      // could be NaN, and 0 x NaN is NaN)
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++) {
+        uint4 vr = __builtin_bit_cast(uint4, vf[dt]);
+        vr.x = kv >= 2 ? vr.x : (kv == 1 ? vr.x & 0xffffu : 0u);
+        vr.y = kv >= 4 ? vr.y : (kv == 3 ? vr.y & 0xffffu : 0u);
+        vr.z = kv >= 6 ? vr.z : (kv == 5 ? vr.z & 0xffffu : 0u);
+        vr.w = kv >= 8 ? vr.w : (kv == 7 ? vr.w & 0xffffu : 0u);
+        vf[dt] = __builtin_bit_cast(bf16x8, vr);
+      }
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mx = wave_max_groups(mx) * sl2;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + RESCALE_LOG2)) {  // wave-uniform
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++) o[dt] *= alpha;
+      m_run = m_new;
+    }
+    const float nm = m_run == -INFINITY ? 0.f : -m_run;
+    bf16x8 pf;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sc[j >> 2][j & 3], sl2, nm));
+      l_run += p;
+      pf[j] = (__bf16)p;
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf, o[dt], 0, 0, 0);
+  };
+  // blocks bs0 + w, bs0 + w + NW, ...; two register sets: the next block
+  // loads while the current one computes
+  bf16x8 kA[2][4], kB[2][4], vA[8], vB[8];
+  int b = bs0 + w;
+  if (b < bs1) load(kA, vA, b);
+  for (; b + NW < bs1; b += 2 * NW) {
+    load(kB, vB, b + NW);
+    compute(kA, vA, b);
+    if (b + 2 * NW < bs1) load(kA, vA, b + 2 * NW);
+    compute(kB, vB, b + NW);
+  }
+  if (b < bs1) compute(kA, vA, b);
+
+  // every column holds the row; column 0 (lanes c16 = 0) is combined
+  const float lsum = wave_sum_groups(l_run);
+  if (c16 == 0) {
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) xo[w][dt * 16 + 4 * g + i] = o[dt][i];
+  }
+  if (l == 0) {
+    xm[w] = m_run;
+    xl[w] = lsum;
+  }
+  __syncthreads();
+  if (tid >= A_DH) return;
+  float mstar = -INFINITY;
+#pragma unroll
+  for (int ww = 0; ww < NW; ww++) mstar = fmaxf(mstar, xm[ww]);
+  float num = 0.f, den = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < NW; ww++) {
+    const float wgt = xm[ww] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(xm[ww] - mstar);
+    num += wgt * xo[ww][tid];
+    den += wgt * xl[ww];
+  }
+  if (S == 1) {
+    const int k = h * A_DH + tid;
+    const size_t oi = a.out_mtt ? frag_index(r, k, a.out_mtt) : (size_t)r * (a.H * A_DH) + k;
+    ((uint16_t*)a.out)[oi] = f2bf(num / den);
+  } else {
+    // the split kernel's partial layout with 16 row slots, row 0
+    const size_t pb = (((size_t)sq * a.H + h) * a.splits + sp) * 16;
+    a.part_o[pb * A_DH + tid] = num;
+    if (tid == 0) {
+      a.part_ml[pb * 2] = mstar;
+      a.part_ml[pb * 2 + 1] = den;
+    }
+  }
+}
+
 void launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
+  if (a.M == 1) {
+    // the row kernel, then (more than one split) the merge; ctx_stride is
+    // a multiple of 64 (the engine aligns it, la_attention checks it)
+    hipLaunchKernelGGL(k_attn_row<4>, dim3(a.H, a.splits, a.nseq), dim3(4 * 64), 0, s, a);
+    if (a.splits > 1) hipLaunchKernelGGL(k_attn_merge, dim3(1, a.H, a.nseq), dim3(256), 0, s, a);
+    return;
+  }
   if (attn_bf16_tiled(a.M, a.ctx_stride)) {
     hipLaunchKernelGGL(k_attn_tile, dim3(a.H, (a.M + 15) / 16, a.nseq), dim3(AT_NW * 64), 0, s, a);
     return;
