@@ -56,6 +56,12 @@ CASES = [
                         n_kv_heads=4, d_ffn=1408, vocab=2048, span_len=8, n_spans=2,
                         W=1, N=3, G=1),
      2, [64, 45], 10),
+    # one-token decodes over long prompts: up to 8 key splits per head and
+    # their merge
+    (lasynth.get_config("7b", name="bf16_plain_b2_long", n_layers=2, d_model=512, n_heads=4,
+                        n_kv_heads=4, d_ffn=1408, vocab=2048, span_len=8, n_spans=2,
+                        W=0, G=0),
+     2, [600, 350], 8),
     # 40 plain one-token decodes of 8 heads (320 sequence heads): the most
     # sequences one context takes at one row each below the row cap
     (lasynth.get_config("7b", name="bf16_plain_b40", n_layers=2, d_model=1024, n_heads=8,
