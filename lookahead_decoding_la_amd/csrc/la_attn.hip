@@ -501,29 +501,33 @@ __global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
 
 // Combine the splits of each (row, head) with log-sum-exp weights
 // 2^(m_s - m*).  A workgroup covers 8 rows of one head of one sequence
-// (grid z); a thread, 4 dims.  All splits' (m, l, O) are loaded up front
-// (one round trip; splits <= 16).
+// (grid z); a thread, 4 dims.  The (m, l, O) of every split the launch
+// provides are loaded up front, together with the committed length that
+// says how many of them this length used: one round trip.  The loads are
+// unconditional (slots past the launch's split count repeat its last one),
+// so none waits on another (a load under a per-split branch made the
+// compiler wait for each before the next); slots this length did not use
+// hold stale values and are not read past the load.
 constexpr int A_MAX_SPLITS = 16;
 
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const int h = blockIdx.y, t = blockIdx.x * 8 + (threadIdx.x >> 5), i = (threadIdx.x & 31) * 4;
   const int sq = blockIdx.z;
-  const int L = a.st ? *(const __attribute__((address_space(4))) int32_t*)&a.st[sq].L : a.L_host;
-  const int S = eff_splits((L + a.M + AKC - 1) / AKC, a.splits, a.M);
-  if (t >= a.M || S == 1) return;  // one split wrote the output itself
+  if (t >= a.M) return;
   const int rows16 = (a.M + 15) & ~15;
   float m[A_MAX_SPLITS], l[A_MAX_SPLITS];
   f32x4 o[A_MAX_SPLITS];
 #pragma unroll
   for (int s = 0; s < A_MAX_SPLITS; s++) {
-    if (s < S) {
-      const size_t b = (((size_t)sq * a.H + h) * a.splits + s) * rows16 + t;
-      const float2 ml = *(const float2*)&a.part_ml[b * 2];
-      m[s] = ml.x;
-      l[s] = ml.y;
-      o[s] = *(const f32x4*)&a.part_o[b * A_DH + i];
-    }
+    const size_t b = (((size_t)sq * a.H + h) * a.splits + min(s, a.splits - 1)) * rows16 + t;
+    const float2 ml = *(const float2*)&a.part_ml[b * 2];
+    m[s] = ml.x;
+    l[s] = ml.y;
+    o[s] = *(const f32x4*)&a.part_o[b * A_DH + i];
   }
+  const int L = a.st ? *(const __attribute__((address_space(4))) int32_t*)&a.st[sq].L : a.L_host;
+  const int S = eff_splits((L + a.M + AKC - 1) / AKC, a.splits, a.M);
+  if (S == 1) return;  // one split wrote the output itself
   float mstar = -INFINITY;
 #pragma unroll
   for (int s = 0; s < A_MAX_SPLITS; s++)
@@ -904,7 +908,7 @@ bool attn_bf16_tiled(int M, int ctx_stride) { return M > 32 && ctx_stride <= 204
 //
 // Bounds: a block starts at a multiple of 32 below the context, and the
 // cache row (ctx_stride, a multiple of 32) holds the whole block.
-template <int NW>
+template <int NW, bool DEEP>
 __global__ __launch_bounds__(NW * 64) void k_attn_row(AttnArgs a) {
   __shared__ float xo[NW][A_DH];
   __shared__ float xm[NW], xl[NW];
@@ -998,18 +1002,47 @@ __global__ __launch_bounds__(NW * 64) void k_attn_row(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < 8; dt++) o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf, o[dt], 0, 0, 0);
   };
-  // blocks bs0 + w, bs0 + w + NW, ...; two register sets: the next block
-  // loads while the current one computes
+  // This wave's blocks: bs0 + w, bs0 + w + NW, ... (nb of them), through
+  // two register sets.  DEEP: the loop body's loads are unconditional and
+  // the last one or two blocks run after it, so the next block's loads stay
+  // in flight through both products of the current one.  Otherwise the
+  // block after next loads under a branch, and the compiler, counting for
+  // the worst path, waits for it before the current block's value
+  // products: fewer bytes in flight per wave, which measured faster once
+  // the grid holds 1024 or more (head, sequence) pairs and HBM is the
+  // limit (plain decode, 32 heads, 1024-token prompts, ms per step, DEEP /
+  // not: batch 1 2.962 / 3.008, 16 4.742 / 4.779, 64 10.39 / 10.24, 128
+  // 17.44 / 17.13).
   bf16x8 kA[2][4], kB[2][4], vA[8], vB[8];
-  int b = bs0 + w;
-  if (b < bs1) load(kA, vA, b);
-  for (; b + NW < bs1; b += 2 * NW) {
-    load(kB, vB, b + NW);
-    compute(kA, vA, b);
-    if (b + 2 * NW < bs1) load(kA, vA, b + 2 * NW);
-    compute(kB, vB, b + NW);
+  const int nb = bs1 - bs0 > w ? (bs1 - bs0 - w + NW - 1) / NW : 0;
+  auto blk = [&](int i) { return bs0 + w + i * NW; };
+  if (nb > 0) {  // wave-uniform
+    load(kA, vA, blk(0));
+    int i = 0;
+    if constexpr (DEEP) {
+      for (; i + 2 < nb; i += 2) {
+        load(kB, vB, blk(i + 1));
+        compute(kA, vA, blk(i));
+        load(kA, vA, blk(i + 2));
+        compute(kB, vB, blk(i + 1));
+      }
+      if (i + 1 < nb) {
+        load(kB, vB, blk(i + 1));
+        compute(kA, vA, blk(i));
+        compute(kB, vB, blk(i + 1));
+      } else {
+        compute(kA, vA, blk(i));
+      }
+    } else {
+      for (; i + 1 < nb; i += 2) {
+        load(kB, vB, blk(i + 1));
+        compute(kA, vA, blk(i));
+        if (i + 2 < nb) load(kA, vA, blk(i + 2));
+        compute(kB, vB, blk(i + 1));
+      }
+      if (i < nb) compute(kA, vA, blk(i));
+    }
   }
-  if (b < bs1) compute(kA, vA, b);
 
   // every column holds the row; column 0 (lanes c16 = 0) is combined
   const float lsum = wave_sum_groups(l_run);
@@ -1054,7 +1087,10 @@ void launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.M == 1) {
     // the row kernel, then (more than one split) the merge; ctx_stride is
     // a multiple of 64 (the engine aligns it, la_attention checks it)
-    hipLaunchKernelGGL(k_attn_row<4>, dim3(a.H, a.splits, a.nseq), dim3(4 * 64), 0, s, a);
+    if (a.H * a.nseq < 1024)
+      hipLaunchKernelGGL((k_attn_row<4, true>), dim3(a.H, a.splits, a.nseq), dim3(4 * 64), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_attn_row<4, false>), dim3(a.H, a.splits, a.nseq), dim3(4 * 64), 0, s, a);
     if (a.splits > 1) hipLaunchKernelGGL(k_attn_merge, dim3(1, a.H, a.nseq), dim3(256), 0, s, a);
     return;
   }

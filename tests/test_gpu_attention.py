@@ -67,6 +67,7 @@ CASES = [
     dict(prefix=127, W=0, N=2, G=0),                   # one row, 128 keys: whole 32-key blocks, 2 key splits
     dict(prefix=2100, W=0, N=2, G=0),                  # one row, 2101 keys, 32 heads: 8 key splits + merge
     dict(prefix=1000, n_heads=256, n_kv_heads=32, W=0, N=2, G=0),  # one row, 256 heads: 2 key splits
+    dict(prefix=300, n_heads=1024, n_kv_heads=128, W=0, N=2, G=0),  # one row, 1024 heads: the shallow-prefetch loop
 ]
 
 
