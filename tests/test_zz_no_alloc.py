@@ -1,7 +1,8 @@
 """la_attention_noalloc (the kernel-level attention for callers that cannot
 allocate) against la_attention with a caller workspace, through the C ABI:
-two calls in a row, the second smaller, both on the split path whose
-partials live in the library's scratch array; the results must be
+calls in a row, each smaller than the one before, all with split-KV
+partials in the library's scratch array (the split kernel, and the
+one-row kernel with its merge); the results must be
 bit-identical (the same kernels in the same order).  A call needing more
 than the array holds is refused before any launch."""
 import ctypes as C
@@ -25,10 +26,10 @@ def _inputs(H, Hkv, prefix, W, N, G, seed):
     return T, ctx, q, k, vt
 
 
-# (heads, KV heads, committed prefix, W, N, G): both use split-KV partials
-# (cache rows above the per-tile kernel's 2048 keys); the second (13 rows,
-# 8 heads) is the smaller problem
-CASES = [(32, 32, 2100, 15, 5, 15), (8, 2, 2100, 3, 3, 3)]
+# (heads, KV heads, committed prefix, W, N, G): all use split-KV partials
+# (cache rows above the per-tile kernel's 2048 keys; one row: 8 key
+# splits), each call a smaller problem than the one before
+CASES = [(32, 32, 2100, 15, 5, 15), (32, 32, 2100, 0, 2, 0), (8, 2, 2100, 3, 3, 3)]
 
 
 def test_noalloc_attention_equals_workspace_attention():
