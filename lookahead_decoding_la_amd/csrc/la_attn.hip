@@ -883,8 +883,15 @@ static void launch_attn_inst(const AttnArgs& a, hipStream_t s) {
 // per step (split + merge / per-tile): 128-token prompts, 1 row 2.90 /
 // 2.84, an 11-row block 3.23 / 3.12, a 21-row block 3.63 / 3.39, 16 one-row
 // sequences 3.62 / 3.69; 512-token prompt, 1 row 2.986 / 3.014; 13B shape,
-// 1024-token prompt, 1 row: attention 0.60 / 0.74 ms per step.
-bool attn_bf16_tiled(int M, int ctx_stride) { return M > 32 && ctx_stride <= 2048; }
+// 1024-token prompt, 1 row: attention 0.60 / 0.74 ms per step.  Once the
+// per-tile grid (heads x tiles x sequences) alone fills the 256 CUs, small
+// blocks take it too: 4 sequences of 21-row blocks, 512 / 1024-token
+// prompts, 4.62 / 4.46 and 4.80 / 4.68 ms per step, where one sequence
+// (64 workgroups) measured 3.64 / 3.57 and 3.65 / 3.72.
+bool attn_bf16_tiled(int M, int ctx_stride, int H, int nseq) {
+  if (ctx_stride > 2048) return false;
+  return M > 32 || (M > 1 && H * ((M + 15) / 16) * nseq >= 256);
+}
 
 // ---------------------------------------------------------------------------
 // One-row blocks (plain decode, batches of one-row sequences): the row sees
@@ -1094,7 +1101,7 @@ void launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
     if (a.splits > 1) hipLaunchKernelGGL(k_attn_merge, dim3(1, a.H, a.nseq), dim3(256), 0, s, a);
     return;
   }
-  if (attn_bf16_tiled(a.M, a.ctx_stride)) {
+  if (attn_bf16_tiled(a.M, a.ctx_stride, a.H, a.nseq)) {
     hipLaunchKernelGGL(k_attn_tile, dim3(a.H, (a.M + 15) / 16, a.nseq), dim3(AT_NW * 64), 0, s, a);
     return;
   }

@@ -272,7 +272,7 @@ struct AttnArgs {
 };
 void launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 // whether launch_attn_bf16 takes the unsplit per-tile kernel (no partials)
-bool attn_bf16_tiled(int M, int ctx_stride);
+bool attn_bf16_tiled(int M, int ctx_stride, int H, int nseq);
 int attn_bf16_splits(int H, int M, int max_ctx);
 void launch_attn_f32(const AttnArgs& a, hipStream_t s);
 

@@ -62,6 +62,7 @@ CASES = [
     dict(prefix=2100, W=3, N=4, G=2),                  # 16 rows at 2100 committed keys: split kernel + merge
     dict(prefix=2100, n_heads=4, W=12, N=5, G=12),     # 97 rows above 2048 keys: split, 32-row groups
     dict(prefix=2100, n_heads=2, W=25, N=5, G=25),     # 201 rows above 2048 keys: split, one 128-row group per head
+    dict(prefix=700, n_heads=256, n_kv_heads=32, W=3, N=3, G=3),  # 13 rows, 256 heads: per-tile kernel for a small block
     dict(prefix=0, W=0, N=2, G=0),                     # one row (plain decode), one key
     dict(prefix=13, n_heads=8, n_kv_heads=2, W=0, N=2, G=0),  # one row, 14 keys: one 32-key block, grouped KV heads
     dict(prefix=127, W=0, N=2, G=0),                   # one row, 128 keys: whole 32-key blocks, 2 key splits

@@ -62,6 +62,12 @@ CASES = [
                         n_kv_heads=4, d_ffn=1408, vocab=2048, span_len=8, n_spans=2,
                         W=0, G=0),
      2, [600, 350], 8),
+    # 8 sequences of 21-row blocks (W5 N3 G5), 16 heads: heads x tiles x
+    # sequences fill 256 CUs, so the small blocks take the per-tile kernel
+    (lasynth.get_config("7b", name="bf16_w5n3g5_b8", n_layers=2, d_model=1024, n_heads=16,
+                        n_kv_heads=16, d_ffn=2816, vocab=4096, span_len=8, n_spans=2,
+                        W=5, N=3, G=5),
+     8, [40, 64, 51], 6),
     # 40 plain one-token decodes of 8 heads (320 sequence heads): the most
     # sequences one context takes at one row each below the row cap
     (lasynth.get_config("7b", name="bf16_plain_b40", n_layers=2, d_model=1024, n_heads=8,
