@@ -884,16 +884,20 @@ static void launch_attn_inst(const AttnArgs& a, hipStream_t s) {
 // 2.84, an 11-row block 3.23 / 3.12, a 21-row block 3.63 / 3.39, 16 one-row
 // sequences 3.62 / 3.69; 512-token prompt, 1 row 2.986 / 3.014; 13B shape,
 // 1024-token prompt, 1 row: attention 0.60 / 0.74 ms per step.  Small
-// blocks (one-row blocks have their own kernel) take it too when the
-// per-tile grid (heads x tiles x sequences) alone fills the 256 CUs (4
-// sequences of 21-row blocks, 512 / 1024-token prompts: 4.60 / 4.43 and
-// 5.13 / 4.62 ms per step), or when the cache rows are short enough that
-// each CU reading its head's whole cache costs little (at most 768 keys:
-// one 17-25-row block, 512-token prompt, 2% faster; at 1024-token prompts,
-// 1216-1280-key rows, 2-4% slower).
+// blocks (one-row blocks have their own kernel) take it too while its grid
+// (heads x tiles x sequences) is one or two rounds on the 256 CUs and
+// either fills the first round (4 sequences of 21-row blocks, 512 /
+// 1024-token prompts: 4.60 / 4.43 and 5.13 / 4.62 ms per step) or the
+// cache rows are short enough that each CU reading its head's whole cache
+// costs little (at most 768 keys: one 17-25-row block, 512-token prompt,
+// 2% faster; at 1024-token prompts, 1216-1280-key rows, 2-4% slower).  At
+// three rounds the split kernel is faster (12 sequences of 21-row blocks,
+// 128 / 512-token prompts: 8.21 / 8.37 and 8.71 / 8.92).
 bool attn_bf16_tiled(int M, int ctx_stride, int H, int nseq) {
   if (ctx_stride > 2048) return false;
-  return M > 32 || (M > 1 && (ctx_stride <= 768 || H * ((M + 15) / 16) * nseq >= 256));
+  if (M > 32) return true;
+  const int wgs = H * ((M + 15) / 16) * nseq;
+  return M > 1 && wgs <= 512 && (ctx_stride <= 768 || wgs >= 256);
 }
 
 // ---------------------------------------------------------------------------
