@@ -68,6 +68,12 @@ CASES = [
                         n_kv_heads=16, d_ffn=2816, vocab=4096, span_len=8, n_spans=2,
                         W=5, N=3, G=5),
      8, [40, 64, 51], 6),
+    # 64 plain one-token decodes of 16 heads: 1024 (head, sequence) pairs
+    # take the one-row attention kernel's shallow-prefetch form
+    (lasynth.get_config("7b", name="bf16_plain_b64_h16", n_layers=2, d_model=1024, n_heads=16,
+                        n_kv_heads=16, d_ffn=2816, vocab=4096, span_len=8, n_spans=2,
+                        W=0, G=0),
+     64, [40, 64, 51, 100], 4),
     # 40 plain one-token decodes of 8 heads (320 sequence heads): the most
     # sequences one context takes at one row each below the row cap
     (lasynth.get_config("7b", name="bf16_plain_b40", n_layers=2, d_model=1024, n_heads=8,
