@@ -318,6 +318,9 @@ AttnArgs attn_args(la_ctx* c, int l, const Pass& p) {
   aa.part_o = c->attn_po;
   aa.part_ml = c->attn_pml;
   aa.splits = c->attn_splits;
+  // the caches are zero-filled at creation and the steps write only
+  // projections into them: every V^T entry, also past the context, is finite
+  aa.vt_finite = 1;
   return aa;
 }
 

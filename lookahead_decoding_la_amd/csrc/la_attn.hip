@@ -388,7 +388,7 @@ __global__ __launch_bounds__(NRP * KSPL * 64) void k_attn_bf16(AttnArgs a) {
         const int d = dt * 16 + c16;
         bf16x8 vf = *(const bf16x8*)(vb + d * 128 + (((4 * s2 + g) ^ ((d >> 1) & 7)) << 4));
         if constexpr (MASKED) {
-          if (nvk < AKC) {  // uniform
+          if (!a.vt_finite && nvk < AKC) {  // uniform
             uint4 vr = __builtin_bit_cast(uint4, vf);
             vr.x &= vm0; vr.y &= vm1; vr.z &= vm2; vr.w &= vm3;
             vf = __builtin_bit_cast(bf16x8, vr);
@@ -723,18 +723,21 @@ __global__ __launch_bounds__(AT_NW * 64) void k_attn_tile(AttnArgs a) {
         for (int v = 0; v < 4; v++)
           if (!((win >> (4 * kt + v)) & 1ull)) sc[kt][v] = -INFINITY;
       // Keys past the context (last slice only) have zero probability, but
-      // their V^T entries may be stale memory: zero them so that no NaN
-      // reaches the MFMA.
-      const int kv = ctx - 32 * s - 8 * g;  // valid keys among this lane's 8
-      const uint32_t vm0 = kv >= 2 ? ~0u : (kv == 1 ? 0xffffu : 0u);
-      const uint32_t vm1 = kv >= 4 ? ~0u : (kv == 3 ? 0xffffu : 0u);
-      const uint32_t vm2 = kv >= 6 ? ~0u : (kv == 5 ? 0xffffu : 0u);
-      const uint32_t vm3 = kv >= 8 ? ~0u : (kv == 7 ? 0xffffu : 0u);
+      // their V^T entries may be stale memory: unless the cache is known to
+      // hold finite values there, zero them so that no NaN reaches the MFMA
+      // (measured: the zeroing costs 0.35 us a call at 550 committed keys).
+      if (!a.vt_finite && 32 * s + 32 > ctx) {  // wave-uniform
+        const int kv = ctx - 32 * s - 8 * g;  // valid keys among this lane's 8
+        const uint32_t vm0 = kv >= 2 ? ~0u : (kv == 1 ? 0xffffu : 0u);
+        const uint32_t vm1 = kv >= 4 ? ~0u : (kv == 3 ? 0xffffu : 0u);
+        const uint32_t vm2 = kv >= 6 ? ~0u : (kv == 5 ? 0xffffu : 0u);
+        const uint32_t vm3 = kv >= 8 ? ~0u : (kv == 7 ? 0xffffu : 0u);
 #pragma unroll
-      for (int dt = 0; dt < 8; dt++) {
-        uint4 vr = __builtin_bit_cast(uint4, vf[dt]);
-        vr.x &= vm0; vr.y &= vm1; vr.z &= vm2; vr.w &= vm3;
-        vf[dt] = __builtin_bit_cast(bf16x8, vr);
+        for (int dt = 0; dt < 8; dt++) {
+          uint4 vr = __builtin_bit_cast(uint4, vf[dt]);
+          vr.x &= vm0; vr.y &= vm1; vr.z &= vm2; vr.w &= vm3;
+          vf[dt] = __builtin_bit_cast(bf16x8, vr);
+        }
       }
     }
     float mx = -INFINITY;
@@ -983,9 +986,10 @@ __global__ __launch_bounds__(NW * 64) void k_attn_row(AttnArgs a) {
       for (int j = 0; j < 8; j++)
         if (j >= kv) sc[j >> 2][j & 3] = -INFINITY;
       // zero the values of keys past the context (stale cache contents
-      // could be NaN, and 0 x NaN is NaN)
+      // could be NaN, and 0 x NaN is NaN) unless the cache is known to hold
+      // finite values there
 #pragma unroll
-      for (int dt = 0; dt < 8; dt++) {
+      for (int dt = 0; dt < 8 && !a.vt_finite; dt++) {
         uint4 vr = __builtin_bit_cast(uint4, vf[dt]);
         vr.x = kv >= 2 ? vr.x : (kv == 1 ? vr.x & 0xffffu : 0u);
         vr.y = kv >= 4 ? vr.y : (kv == 3 ? vr.y & 0xffffu : 0u);

@@ -269,6 +269,9 @@ struct AttnArgs {
   float* part_o;       // split-KV partials [seq][H][splits][rows16][dh]
   float* part_ml;      // [seq][H][splits][rows16][2]
   int splits;
+  int vt_finite;       // 1: every V^T entry of the cache rows holds a finite value (the
+                       // engine's caches), so the entries past the context in the last
+                       // chunk need no zeroing; 0: they may hold anything
 };
 void launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 // whether launch_attn_bf16 takes the unsplit per-tile kernel (no partials)

@@ -25,14 +25,20 @@ from lockstep import log
 pytestmark = pytest.mark.gpu
 
 
-def _run(a):
+BF16_NAN = 0x7FC0
+
+
+def _run(a, past=0):
+    """la_attention on the inputs of `a`, the cache rows padded to a multiple
+    of 64 positions; the positions past the context hold the bf16 pattern
+    `past` (0, or a NaN: the kernel must not let them reach the output)."""
     T, H, Hkv, dh, L = a["T"], a["n_heads"], a["n_kv_heads"], a["head_dim"], a["prefix"]
     ctx = ((L + T + 63) // 64) * 64
     dev = torch.device("cuda")
     q = torch.from_numpy(a["q"].view(np.int16)).to(dev)
-    k = torch.zeros((Hkv, ctx, dh), dtype=torch.int16, device=dev)
+    k = torch.full((Hkv, ctx, dh), past, dtype=torch.int16, device=dev)
     k[:, :L + T] = torch.from_numpy(a["k"].view(np.int16)).to(dev)
-    vt = torch.zeros((Hkv, dh, ctx), dtype=torch.int16, device=dev)
+    vt = torch.full((Hkv, dh, ctx), past, dtype=torch.int16, device=dev)
     vt[:, :, :L + T] = torch.from_numpy(a["v"].view(np.int16)).to(dev).transpose(1, 2)
     out = torch.zeros((T, H, dh), dtype=torch.int16, device=dev)
     la.attention(q, k, vt.contiguous(), out, H, Hkv, L, a["W"], a["N"], a["G"])
@@ -72,11 +78,31 @@ CASES = [
 ]
 
 
+# Cache rows whose positions past the context hold NaN (la_attention makes no
+# assumption about them): the per-tile kernel, the split kernel and the row
+# kernel, each with a last chunk or block that reaches past the context.
+NAN_CASES = [
+    dict(),                                            # per-tile kernel, 1145 keys in 1152
+    dict(prefix=2100, W=3, N=4, G=2),                  # split kernel + merge
+    dict(prefix=13, n_heads=8, n_kv_heads=2, W=0, N=2, G=0),  # row kernel, 14 keys
+]
+
+
 @pytest.mark.parametrize("kw", CASES, ids=lambda kw: ",".join(f"{k}={v}" for k, v in kw.items()) or "attn")
 def test_attention_matches_oracle(kw):
+    _check(kw, 0)
+
+
+@pytest.mark.parametrize("kw", NAN_CASES, ids=lambda kw: ",".join(f"{k}={v}" for k, v in kw.items()) or "attn")
+def test_attention_ignores_nan_past_the_context(kw):
+    _check(kw, BF16_NAN)
+
+
+def _check(kw, past):
     a = lasynth.make_attn_inputs(seed=7, **kw)
-    log(f"[attention] {kw} T={a['T']}")
-    got, ref, vmax = _run(a)
+    log(f"[attention] {kw} T={a['T']} past-context fill {past:#06x}")
+    got, ref, vmax = _run(a, past)
+    assert np.all(np.isfinite(got))
     err = np.abs(got - ref)
     bound = 2.0**-8 * (vmax[None, :, None] + np.abs(ref)) + 1e-4
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
