@@ -414,11 +414,20 @@ def cpu_baseline(cfg, dev_w, prompt, win, n_steps=3):
     import lookahead_decoding_la_amd as la
     P = min(len(prompt), 512)
     P_PLAIN = 16
+    log("cpu oracle: copying the weights to the host")
     w = lasynth.host_bits(dev_w)
     max_ctx = P + (n_steps + 1) * cfg.T + 8
     o = oracle.Oracle(cfg, w, max_ctx)
     dev = la.LookaheadDecoder(cfg, dev_w, max_ctx)
-    fo, lgp = o.prefill(prompt[:P], win, logits=True)
+    # the oracle's prefill (not timed) in chunks, with a progress line each:
+    # a chunk is appended causally like the rest of the prompt, and the
+    # current token is the decision after the last one
+    CH = 64
+    fo, lgp = o.prefill(prompt[:min(P, CH)], win, logits=True)
+    for a in range(CH, P, CH):
+        log(f"cpu oracle: prefill {a} of {P} prompt tokens")
+        fo, lgp = o.extend(prompt[a:min(a + CH, P)], logits=True)
+    o.set_current(fo)
     fg = dev.prefill(prompt[:P], win)
     adopted = []
     if fg != fo:  # a near-tie decided the prefill's token differently
