@@ -432,3 +432,33 @@ def test_rewind_then_decode_again_is_identical(tiny):
     assert ra == rb and np.array_equal(la_, lb, equal_nan=True)
     with pytest.raises(ValueError):
         a.rewind(a.kv_len + 1, 0)
+
+
+def test_prefill_in_chunks_equals_one_prefill(tiny):
+    """A prompt prefilled as a first chunk (with the window), the rest appended
+    causally with extend, and the current token set to the decision after the
+    last prompt token, leaves the same state as one prefill: the same current
+    token and KV cache, and the next lookahead step's block and logits are
+    identical (bench.py's CPU baseline prefills long prompts this way)."""
+    cfg, w, p, win = tiny
+    p = [int(x) for x in p]
+    a = oracle.Oracle(cfg, w, 256)
+    b = oracle.Oracle(cfg, w, 256)
+    ta = a.prefill(p, win)
+    tb = b.prefill(p[:5], win)
+    for s in range(5, len(p), 7):
+        tb = b.extend(p[s:s + 7])
+    b.set_current(tb)
+    assert ta == tb
+    for layer in range(cfg.n_layers):
+        for kh in range(cfg.n_kv_heads):
+            ka, va = a.kv(layer, kh, len(p))
+            kb, vb = b.kv(layer, kh, len(p))
+            assert np.array_equal(ka, kb) and np.array_equal(va, vb)
+    tok_a, val_a, nc_a = a.block_tokens()
+    tok_b, val_b, nc_b = b.block_tokens()
+    assert nc_a == nc_b and np.array_equal(tok_a, tok_b) and np.array_equal(val_a, val_b)
+    v = val_a.astype(bool)
+    la_ = a.forward_block(tok_a, val_a, keep=False)
+    lb_ = b.forward_block(tok_b, val_b, keep=False)
+    assert np.array_equal(la_[v], lb_[v])
