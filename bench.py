@@ -508,8 +508,8 @@ def cpu_baseline(cfg, dev_w, prompt, win, n_steps=3):
                    f"{n_steps} steps of {cfg.T} rows after a {P}-token prompt)",
         "max_abs_dlogit": round(dmax, 5),
         "rms_dlogit": round(float(np.sqrt(sq / ncmp)), 5),
-        "north_star_logit_tol": 0.02,
-        "within_north_star_tol": dmax <= 0.02,
+        "target_logit_tol": 0.02,
+        "within_target_logit_tol": dmax <= 0.02,
         "bf16_storage_rounding_only": None if rb is None else
         {"max_abs_dlogit": round(rb["max_abs_dlogit"], 5), "rms_dlogit": round(rb["rms_dlogit"], 5)},
         "decisions": ndec + 1,
