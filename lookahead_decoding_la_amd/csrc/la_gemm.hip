@@ -180,15 +180,18 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_dma(
   // nontemporal (aux bit 1, "nt"), which measured a few percent faster; the
   // activation fragments, re-read by every workgroup, keep the default
   // policy so they stay in L2.
-  // The fused gate/up GEMM and the 8-split GEMMs (no fragment prefetch)
-  // walk each workgroup's K range from a different starting stage (rotated
-  // by its share of the range, wrapping around), so that the workgroups of
-  // a launch do not all read the same offset of their weight tiles at the
-  // same moment.  Measured (same-box A/B, 7B step shapes, us per launch):
-  // gate/up 49.2 -> 48.8, down 23.4 -> 22.9; QKV (2 splits, prefetched
-  // fragments) 27.3 -> 27.6, so it keeps the plain order.  The order is
-  // fixed per workgroup, so the sums do not depend on timing.
-  constexpr bool ROT = OUT == 1 || !XP;
+  // The fused gate/up GEMM and, up to 8 token tiles, the 8-split GEMMs (no
+  // fragment prefetch) walk each workgroup's K range from a different
+  // starting stage (rotated by its share of the range, wrapping around), so
+  // that the workgroups of a launch do not all read the same offset of their
+  // weight tiles at the same moment.  Measured (same-box A/Bs, 7B shapes, us
+  // per launch): 121 rows, gate/up 49.2 -> 48.8, down 23.4 -> 22.9; 201
+  // rows, gate/up 84.5 -> 81.2 but down 35.3 -> 44.5 (161 rows: 30.7 ->
+  // 37.2), so the 8-split GEMMs rotate only up to 8 token tiles; QKV (2
+  // splits, prefetched fragments) 27.3 -> 27.6 at 121 rows keeps the plain
+  // order.  The order is fixed per workgroup, so the sums do not depend on
+  // timing.
+  constexpr bool ROT = OUT == 1 || (!XP && MT <= 8);
   const int rot = ROT ? (int)(((uint32_t)wt * (uint32_t)nst) / gridDim.x) : 0;
   auto issue = [&](int st, int b) {
     st = min(st, nst - 1) + rot;
