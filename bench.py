@@ -362,6 +362,26 @@ def batch_sweep(cfg, dev_w, steps, warmup, prompt_len=128):
     return out
 
 
+def counter_summary(run_dirs):
+    """Mean value per dispatch of every counter in rocprofv3 csv counter
+    runs, by kernel (name up to its argument list), with the dispatch count;
+    runs of different counter sets over the same program merge by kernel."""
+    import csv
+    import glob
+    acc = {}
+    for run_dir in run_dirs:
+        for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for row in csv.DictReader(fh):
+                    name = row["Kernel_Name"].split("(")[0]
+                    k = acc.setdefault(name, {})
+                    v = k.setdefault(row["Counter_Name"], [0.0, 0])
+                    v[0] += float(row["Counter_Value"])
+                    v[1] += 1
+    return {name: {c: {"mean": v[0] / v[1], "dispatches": v[1]} for c, v in cs.items()}
+            for name, cs in acc.items()}
+
+
 def sweep_counters(run_dir):
     """MFMA busy fraction of the GEMM dispatches of each sweep setting, from
     a rocprofv3 run of `--sweep` with SQ_VALU_MFMA_BUSY_CYCLES and
@@ -653,6 +673,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="W = G sweep at N fixed (step ms, kernel classes, GEMM MFMA "
                          "throughput); prints one JSON line")
+    ap.add_argument("--counter-summary", nargs="+", metavar="DIR",
+                    help="mean per dispatch of every counter of rocprofv3 csv counter runs, "
+                         "by kernel; prints one JSON line")
     ap.add_argument("--sweep-counters", metavar="DIR",
                     help="MFMA busy fraction per sweep setting from a rocprofv3 counter run "
                          "of --sweep; prints one JSON line")
@@ -678,6 +701,9 @@ def main():
         return
     if args.step_traffic:
         step_traffic(args.step_traffic, args.config)
+        return
+    if args.counter_summary:
+        print(json.dumps(counter_summary(args.counter_summary)))
         return
     if args.sweep_counters:
         print(json.dumps({"sweep_counters": sweep_counters(args.sweep_counters)}))
